@@ -1,0 +1,256 @@
+"""Pins for the oracle's expert FFN, combine and whole layer.
+
+Special cases that reduce to textbook routines (k=1 is one expert's dense SwiGLU FFN,
+checked with numpy float64 matmuls on independently decoded weights; a zero router
+makes every logit tie; x = 0 gives y = 0), exact metamorphic relations, and negative
+controls: planted mistakes (in copies of the oracle's steps, on the CPU) that the
+parity tolerance must catch by a wide margin.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from indep import expert_weights, silu
+
+TINY = synth.WORKLOADS["tiny"]
+TOL_F32 = 1e-4   # parity tolerance for fp32 output (rel-L2)
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def _inputs(wl, seed=0, T=None):
+    lay = synth.make_layer(wl, 0, seed, "cpu")
+    x = synth.make_x(wl, seed, "cpu", tokens=T)
+    blobs = [lay["blob"][e].numpy() for e in range(wl.n_experts)]
+    bias = None if lay["bias"] is None else lay["bias"].numpy()
+    return oracle.to_f64(x), lay["router"].numpy(), bias, blobs
+
+
+def _layer(wl, x64, wr, bias, blobs, scaling=1.0, residual=None):
+    return oracle.layer(x64, wr, bias, blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat, scaling, residual)
+
+
+def _dense_ffn(blob, x, wl):
+    Wg, Wu, Wd = expert_weights(blob, wl.d_model, wl.d_ff, wl.wformat)
+    g = Wg @ x
+    u = Wu @ x
+    return Wd @ (silu(g) * u)
+
+
+@pytest.mark.parametrize("wformat", [synth.MXFP4, synth.NVFP4])
+def test_k1_is_dense_ffn(wformat):
+    wl = dataclasses.replace(TINY, top_k=1, n_experts=4, wformat=wformat, tokens=5)
+    x64, wr, bias, blobs = _inputs(wl)
+    y, idx, w, _ = _layer(wl, x64, wr, bias, blobs)
+    assert np.all(w == 1.0)
+    for t in range(wl.tokens):
+        want = _dense_ffn(blobs[idx[t, 0]], x64[t], wl)
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-14 * np.abs(want).max())
+
+
+def test_zero_router_ties_and_mean_of_all_experts():
+    wl = dataclasses.replace(TINY, top_k=TINY.n_experts, tokens=2)
+    x64, wr, bias, blobs = _inputs(wl)
+    y, idx, w, logits = _layer(wl, x64, np.zeros_like(wr), None, blobs)
+    assert np.all(logits == 0)
+    assert idx.tolist() == [list(range(wl.n_experts))] * 2
+    np.testing.assert_allclose(w, 1.0 / wl.n_experts, rtol=1e-15)
+    for t in range(2):
+        want = np.mean([_dense_ffn(b, x64[t], wl) for b in blobs], axis=0)
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-14 * np.abs(want).max())
+
+
+def test_zero_router_k2_picks_first_two():
+    x64, wr, bias, blobs = _inputs(TINY)
+    _, idx, w, _ = _layer(TINY, x64, np.zeros_like(wr), None, blobs)
+    assert idx.tolist() == [[0, 1]] * TINY.tokens
+    assert np.all(w == 0.5)
+
+
+def test_zero_input_gives_zero_output():
+    x64, wr, bias, blobs = _inputs(TINY)
+    y, _, _, _ = _layer(TINY, np.zeros_like(x64), wr, bias, blobs)
+    assert np.all(y == 0.0)
+
+
+def test_residual_is_added():
+    x64, wr, bias, blobs = _inputs(TINY)
+    y0, _, _, _ = _layer(TINY, x64, wr, bias, blobs)
+    y1, _, _, _ = _layer(TINY, x64, wr, bias, blobs, residual=x64)
+    np.testing.assert_array_equal(y1, y0 + x64)
+
+
+def test_steps_compose_to_layer():
+    x64, wr, bias, blobs = _inputs(TINY)
+    y, idx, w, logits = _layer(TINY, x64, wr, bias, blobs)
+    l2, idx2, w2 = oracle.route(x64, wr, bias, TINY.top_k)
+    off, sp, pp = oracle.permute(idx2, TINY.n_experts)
+    o = oracle.expert_ffn(blobs, TINY.d_model, TINY.d_ff, TINY.wformat, x64, TINY.top_k, off, sp)
+    y2 = oracle.combine(o, w2, pp)
+    np.testing.assert_array_equal(idx, idx2)
+    np.testing.assert_array_equal(y, y2)
+    # each o row is that pick's dense FFN
+    for i, p in enumerate(sp):
+        t, j = divmod(int(p), TINY.top_k)
+        np.testing.assert_allclose(o[i], _dense_ffn(blobs[idx[t, j]], x64[t], TINY), rtol=1e-12,
+                                   atol=1e-14 * np.abs(o[i]).max())
+
+
+# -------------------------------------------------------------------------------------------
+# exact metamorphic relations
+# -------------------------------------------------------------------------------------------
+
+def _bump_scales(blobs, wl, part, delta=1):
+    off = synth.blob_offsets(wl.d_model, wl.d_ff, wl.wformat)
+    so, sn = off[part + "_s"]
+    out = []
+    for b in blobs:
+        b = b.copy()
+        b[so:so + sn] = b[so:so + sn] + delta
+        out.append(b)
+    return out
+
+
+def test_down_scale_plus_one_doubles_output_exactly():
+    x64, wr, bias, blobs = _inputs(TINY)
+    y, _, _, _ = _layer(TINY, x64, wr, bias, blobs)
+    y2, _, _, _ = _layer(TINY, x64, wr, bias, _bump_scales(blobs, TINY, "down"))
+    np.testing.assert_array_equal(y2, 2 * y)
+
+
+def test_up_scale_plus_one_doubles_output_exactly():
+    x64, wr, bias, blobs = _inputs(TINY)
+    y, _, _, _ = _layer(TINY, x64, wr, bias, blobs)
+    y2, _, _, _ = _layer(TINY, x64, wr, bias, _bump_scales(blobs, TINY, "up"))
+    np.testing.assert_array_equal(y2, 2 * y)
+
+
+def test_scaling_two_doubles_exactly():
+    x64, wr, bias, blobs = _inputs(TINY)
+    y, _, _, _ = _layer(TINY, x64, wr, bias, blobs)
+    y2, _, _, _ = _layer(TINY, x64, wr, bias, blobs, scaling=2.0)
+    np.testing.assert_array_equal(y2, 2 * y)
+
+
+def test_token_permutation_permutes_output():
+    wl = dataclasses.replace(TINY, tokens=9)
+    x64, wr, bias, blobs = _inputs(wl)
+    y, idx, _, _ = _layer(wl, x64, wr, bias, blobs)
+    perm = np.random.default_rng(0).permutation(9)
+    y2, idx2, _, _ = _layer(wl, np.ascontiguousarray(x64[perm]), wr, bias, blobs)
+    np.testing.assert_array_equal(y2, y[perm])
+    np.testing.assert_array_equal(idx2, idx[perm])
+
+
+def test_expert_relabelling_leaves_output_unchanged():
+    x64, wr, bias, blobs = _inputs(TINY)
+    y, idx, _, _ = _layer(TINY, x64, wr, bias, blobs)
+    perm = np.random.default_rng(3).permutation(TINY.n_experts)   # new id of old expert e
+    inv = np.argsort(perm)
+    wr2 = np.ascontiguousarray(wr[inv])
+    blobs2 = [blobs[inv[e]] for e in range(TINY.n_experts)]
+    y2, idx2, _, _ = _layer(TINY, x64, wr2, bias, blobs2)
+    np.testing.assert_array_equal(idx2, perm[idx])
+    np.testing.assert_array_equal(y2, y)
+
+
+# -------------------------------------------------------------------------------------------
+# negative controls: each planted mistake must exceed the fp32 parity tolerance >= 100x
+# -------------------------------------------------------------------------------------------
+
+def _baseline():
+    x64, wr, bias, blobs = _inputs(TINY)
+    y, idx, w, logits = _layer(TINY, x64, wr, bias, blobs)
+    return x64, wr, bias, blobs, y, idx, w, logits
+
+
+def _assert_caught(y_bad, y, name):
+    err = rel_l2(y_bad, y)
+    assert err > 100 * TOL_F32, f"negative control '{name}' not separated: rel-L2 {err:.3g}"
+
+
+def test_negative_flipped_nibble_order():
+    x64, wr, bias, blobs, y, *_ = _baseline()
+    flipped = [((b >> 4) | (b << 4)).astype(np.uint8) for b in blobs]
+    off = synth.blob_offsets(TINY.d_model, TINY.d_ff, TINY.wformat)
+    for fb, b in zip(flipped, blobs):     # flip only the packed codes, keep the scales
+        fb[off["gate_s"][0]:] = b[off["gate_s"][0]:]
+    y_bad, *_ = _layer(TINY, x64, wr, bias, flipped)
+    _assert_caught(y_bad, y, "flipped nibble order")
+
+
+def test_negative_routed_scaling():
+    x64, wr, bias, blobs, y, *_ = _baseline()
+    y_bad, *_ = _layer(TINY, x64, wr, bias, blobs, scaling=2.5)
+    _assert_caught(y_bad, y, "routed_scaling 2.5 vs 1.0")
+
+
+def test_negative_e8m0_bias_off_by_one():
+    x64, wr, bias, blobs, y, *_ = _baseline()
+    bad = _bump_scales(_bump_scales(_bump_scales(blobs, TINY, "gate"), TINY, "up"), TINY, "down")
+    y_bad, *_ = _layer(TINY, x64, wr, bias, bad)
+    _assert_caught(y_bad, y, "E8M0 bias off by one")
+
+
+def _combine_with(w_bad, x64, wr, bias, blobs, idx):
+    off, sp, pp = oracle.permute(idx, TINY.n_experts)
+    o = oracle.expert_ffn(blobs, TINY.d_model, TINY.d_ff, TINY.wformat, x64, TINY.top_k, off, sp)
+    return oracle.combine(o, np.ascontiguousarray(w_bad), pp)
+
+
+def test_negative_softmax_instead_of_sigmoid():
+    x64, wr, bias, blobs, y, idx, w, logits = _baseline()
+    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=1)
+    soft = np.exp(sel) / np.exp(sel).sum(axis=1, keepdims=True)
+    _assert_caught(_combine_with(soft, x64, wr, bias, blobs, idx), y, "softmax scoring")
+
+
+def test_negative_no_renormalisation():
+    x64, wr, bias, blobs, y, idx, w, logits = _baseline()
+    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=1)
+    raw = 1.0 / (1.0 + np.exp(-sel))
+    _assert_caught(_combine_with(raw, x64, wr, bias, blobs, idx), y, "no renormalisation")
+
+
+def test_negative_higher_index_tie_break():
+    x64, wr, bias, blobs, *_ = _baseline()
+    wr0 = np.zeros_like(wr)
+    b = np.zeros(TINY.n_experts, dtype=np.float32)
+    b[3], b[5], b[11] = 1.0, 0.5, 0.5             # second place is a tie between 5 and 11
+    y, idx, w, _ = _layer(TINY, x64, wr0, b, blobs)
+    assert idx[0].tolist() == [3, 5]
+    idx_bad = np.tile(np.array([[3, 11]], dtype=np.int32), (TINY.tokens, 1))
+    _assert_caught(_combine_with(w, x64, wr0, b, blobs, idx_bad), y, "higher-index tie-break")
+
+
+def test_negative_wrong_block_axis():
+    """Scales applied down the columns instead of along each row's reduction dim."""
+    x64, wr, bias, blobs, y, idx, w, _ = _baseline()
+    d, f = TINY.d_model, TINY.d_ff
+
+    def ffn_wrong_axis(blob, x):
+        import indep
+        nq, ns = f * d // 2, f * d // 32
+        mats = []
+        for i, (rows, K) in enumerate(((f, d), (f, d), (d, f))):
+            q = blob[i * nq:(i + 1) * nq].reshape(rows, K // 2)
+            s = blob[3 * nq + i * ns: 3 * nq + (i + 1) * ns].reshape(-1)
+            c = indep.codes(q, K)
+            sc = torch.from_numpy(s.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+            r, k = np.meshgrid(np.arange(rows), np.arange(K), indexing="ij")
+            mats.append(indep._table()[c] * sc[(k * rows + r) // 32])
+        Wg, Wu, Wd = mats
+        return Wd @ (silu(Wg @ x) * (Wu @ x))
+
+    y_bad = np.zeros_like(y)
+    for t in range(TINY.tokens):
+        for j in range(TINY.top_k):
+            y_bad[t] += w[t, j] * ffn_wrong_axis(blobs[idx[t, j]], x64[t])
+    _assert_caught(y_bad, y, "wrong block axis")
