@@ -1,0 +1,248 @@
+// Host side of the C ABI: argument validation (before any launch), workspace layout and the
+// launch sequence of each entry point.
+#include <math.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int act_terms(const moe_shape* s) { return s->act_dtype == MOE_DT_BF16 ? 2 : 4; }
+
+WsLayout ws_layout(const moe_shape* s, int32_t T) {
+    WsLayout L;
+    memset(&L, 0, sizeof L);
+    const size_t E = s->n_experts, k = s->top_k, d = s->d_model, f = s->d_ff;
+    const size_t P = (size_t)T * k;
+    L.nt = act_terms(s);
+    const int variant = gemm_variant(s, T);
+    const size_t tt = (size_t)gemm_tile_tokens(variant, L.nt);
+    L.max_tiles = (int)((E < P ? E : P) + P / tt + 1);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
+    L.logits = take(8 * (size_t)T * E);
+    L.idx = take(4 * P);
+    L.w = take(4 * P);
+    L.offsets = take(4 * (E + 1));
+    L.sorted_pick = take(4 * P);
+    L.pick_pos = take(4 * P);
+    L.tiles = take(8 * (size_t)L.max_tiles);
+    L.ntiles = take(4);
+    L.xq = take((size_t)T * L.nt * d);
+    L.xs = take((size_t)T * L.nt * d / 32);
+    L.hq = take(P * L.nt * f);
+    L.hs = take(P * L.nt * f / 32);
+    L.o = take(4 * P * d);
+    L.total = o;
+    return L;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+static moe_status check_shape(const moe_shape* s) {
+    if (!s) return MOE_ERR_INVALID;
+    if (s->d_model <= 0 || s->d_ff <= 0 || s->n_experts <= 0 || s->top_k <= 0) return MOE_ERR_INVALID;
+    if (s->top_k > s->n_experts) return MOE_ERR_INVALID;
+    if (s->wformat != MOE_WF_MXFP4 && s->wformat != MOE_WF_NVFP4) return MOE_ERR_INVALID;
+    if (s->act_dtype != MOE_DT_F32 && s->act_dtype != MOE_DT_BF16) return MOE_ERR_INVALID;
+    if (!isfinite(s->routed_scaling)) return MOE_ERR_INVALID;
+    if (s->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
+    if (s->d_model % 128 != 0 || s->d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if ((long long)s->d_model * s->d_ff > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+static moe_status check_T(const moe_shape* s, int32_t T) {
+    if (T < 0) return MOE_ERR_INVALID;
+    if (T > 65536) return MOE_ERR_UNSUPPORTED;
+    (void)s;
+    return MOE_OK;
+}
+
+static moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                              \
+    do {                                           \
+        moe_status st_ = (expr);                   \
+        if (st_ != MOE_OK) return st_;             \
+    } while (0)
+#define MOE_HIP(expr)                              \
+    do {                                           \
+        if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+// sequence shared by moe_expert_ffn and moe_layer
+static moe_status run_ffn(const moe_shape* s, const moe_expert* table, const void* x, int32_t T,
+                          const int32_t* offsets, const int32_t* sorted_pick, float* o, uint8_t* ws,
+                          const WsLayout& L, hipStream_t st) {
+    const int variant = gemm_variant(s, T);
+    const int NT = L.nt;
+    const int tt = gemm_tile_tokens(variant, NT);
+    int32_t* tiles = (int32_t*)(ws + L.tiles);
+    int32_t* ntiles = (int32_t*)(ws + L.ntiles);
+    MOE_HIP(launch_plan(s, offsets, tt, tiles, ntiles, st));
+    const int ks1 = (variant == 0 && (s->d_model / 4) % 128 == 0) ? 4 : 1;
+    const int SS1 = super_step(s->d_model, ks1);
+    MOE_HIP(launch_act_split(s, x, T, s->d_model, SS1, NT, ws + L.xq, ws + L.xs, st));
+    GemmArgs a;
+    a.table = table;
+    a.d = s->d_model;
+    a.f = s->d_ff;
+    a.E = s->n_experts;
+    a.k = s->top_k;
+    a.P = T * s->top_k;
+    a.sorted_pick = sorted_pick;
+    a.tiles = tiles;
+    a.ntiles = ntiles;
+    a.offsets = offsets;
+    a.aq = ws + L.xq;
+    a.as = ws + L.xs;
+    a.hq = ws + L.hq;
+    a.hs = ws + L.hs;
+    a.o = o;
+    MOE_HIP(launch_gemm_gateup(a, NT, variant, L.max_tiles, st));
+    a.aq = ws + L.hq;
+    a.as = ws + L.hs;
+    MOE_HIP(launch_gemm_down(a, NT, variant, L.max_tiles, st));
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or size";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t moe_blob_stride(const moe_shape* s) {
+    if (check_shape(s) != MOE_OK) return 0;
+    const size_t B = s->wformat == MOE_WF_MXFP4 ? 32 : 16;
+    const size_t fd = (size_t)s->d_model * s->d_ff;
+    size_t n = 3 * (fd / 2) + 3 * (fd / B);
+    if (s->wformat == MOE_WF_NVFP4) n = (n + 12 + 255) / 256 * 256;
+    return n;
+}
+
+size_t moe_workspace_bytes(const moe_shape* s, int32_t T) {
+    if (check_shape(s) != MOE_OK || check_T(s, T) != MOE_OK) return 0;
+    return ws_layout(s, T).total;
+}
+
+moe_status moe_fill_table(const moe_shape* s, const void* base, size_t stride, moe_expert* table,
+                          hipStream_t stream) {
+    MOE_TRY(check_shape(s));
+    if (!base || !table) return MOE_ERR_INVALID;
+    if (!aligned(base, 16) || stride % 16 != 0 || stride < moe_blob_stride(s)) return MOE_ERR_INVALID;
+    return hip_status(launch_fill_table(s, (const uint8_t*)base, stride, table, stream));
+}
+
+moe_status moe_route(const moe_shape* s, const void* x, int32_t T, const float* w_router,
+                     const float* logit_bias, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+    MOE_TRY(check_shape(s));
+    MOE_TRY(check_T(s, T));
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !topk_idx || !topk_w || !ws) return MOE_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(ws, 256)) return MOE_ERR_INVALID;
+    const WsLayout L = ws_layout(s, T);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    uint8_t* w8 = (uint8_t*)ws;
+    double* logits = (double*)(w8 + L.logits);
+    MOE_HIP(launch_router_logits(s, x, T, w_router, logit_bias, logits, stream));
+    MOE_HIP(launch_topk(s, logits, T, topk_idx, topk_w, stream));
+    return MOE_OK;
+}
+
+moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t T, int32_t* expert_offsets,
+                       int32_t* sorted_pick, int32_t* pick_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_shape(s));
+    MOE_TRY(check_T(s, T));
+    (void)ws;
+    (void)ws_bytes;
+    if (!topk_idx || !expert_offsets || !sorted_pick || !pick_pos) return MOE_ERR_INVALID;
+    if (T == 0) return MOE_OK;
+    return hip_status(launch_permute(s, topk_idx, T, expert_offsets, sorted_pick, pick_pos, stream));
+}
+
+moe_status moe_gather_experts(const moe_shape* s, const moe_expert* d_table, const int32_t* d_list, int32_t n,
+                              void* staging, moe_expert* d_staged_table, hipStream_t stream) {
+    MOE_TRY(check_shape(s));
+    if (n < 0) return MOE_ERR_INVALID;
+    if (n == 0) return MOE_OK;
+    if (!d_table || !d_list || !staging || !d_staged_table) return MOE_ERR_INVALID;
+    if (!aligned(staging, 256)) return MOE_ERR_INVALID;
+    const size_t stride = (moe_blob_stride(s) + 255) / 256 * 256;
+    return hip_status(launch_gather(s, d_table, d_list, n, (uint8_t*)staging, stride, d_staged_table, stream));
+}
+
+moe_status moe_expert_ffn(const moe_shape* s, const moe_expert* d_table, const void* x, int32_t T,
+                          const int32_t* expert_offsets, const int32_t* sorted_pick, float* o, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_shape(s));
+    MOE_TRY(check_T(s, T));
+    if (T == 0) return MOE_OK;
+    if (!d_table || !x || !expert_offsets || !sorted_pick || !o || !ws) return MOE_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(o, 16) || !aligned(ws, 256)) return MOE_ERR_INVALID;
+    if (s->wformat != MOE_WF_MXFP4) return MOE_ERR_UNSUPPORTED;
+    const WsLayout L = ws_layout(s, T);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    return run_ffn(s, d_table, x, T, expert_offsets, sorted_pick, o, (uint8_t*)ws, L, stream);
+}
+
+moe_status moe_combine(const moe_shape* s, const float* o, const float* topk_w, const int32_t* pick_pos,
+                       int32_t T, const void* residual, void* y, hipStream_t stream) {
+    MOE_TRY(check_shape(s));
+    MOE_TRY(check_T(s, T));
+    if (T == 0) return MOE_OK;
+    if (!o || !topk_w || !pick_pos || !y) return MOE_ERR_INVALID;
+    if (!aligned(o, 16) || !aligned(y, 16) || (residual && !aligned(residual, 16))) return MOE_ERR_INVALID;
+    return hip_status(launch_combine(s, o, topk_w, pick_pos, T, residual, y, stream));
+}
+
+moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* w_router,
+                     const float* logit_bias, const moe_expert* d_table, void* staging, const void* residual,
+                     void* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+    MOE_TRY(check_shape(s));
+    MOE_TRY(check_T(s, T));
+    (void)staging;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !d_table || !y || !ws) return MOE_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w_router, 16) || !aligned(ws, 256) ||
+        (residual && !aligned(residual, 16)))
+        return MOE_ERR_INVALID;
+    if (x == y) return MOE_ERR_INVALID;
+    if (s->wformat != MOE_WF_MXFP4) return MOE_ERR_UNSUPPORTED;
+    const WsLayout L = ws_layout(s, T);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    uint8_t* w8 = (uint8_t*)ws;
+    int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)(w8 + L.idx);
+    float* w = topk_w_out ? topk_w_out : (float*)(w8 + L.w);
+    double* logits = (double*)(w8 + L.logits);
+    int32_t* offsets = (int32_t*)(w8 + L.offsets);
+    int32_t* sorted_pick = (int32_t*)(w8 + L.sorted_pick);
+    int32_t* pick_pos = (int32_t*)(w8 + L.pick_pos);
+    float* o = (float*)(w8 + L.o);
+    MOE_HIP(launch_router_logits(s, x, T, w_router, logit_bias, logits, stream));
+    MOE_HIP(launch_topk(s, logits, T, idx, w, stream));
+    MOE_HIP(launch_permute(s, idx, T, offsets, sorted_pick, pick_pos, stream));
+    MOE_TRY(run_ffn(s, d_table, x, T, offsets, sorted_pick, o, w8, L, stream));
+    MOE_HIP(launch_combine(s, o, w, pick_pos, T, residual, y, stream));
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+// Route-weighted combine, expert-table fill and the device-list expert gather.
+#include "moe_internal.h"
+
+namespace moe {
+
+// y[t] = s * sum_j w[t,j] * o[pick_pos[t*k+j]] (+ residual[t]); one thread per 4 columns,
+// the k terms summed in rank order in fp32, rounded once to the output dtype.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, const float* __restrict__ w,
+                                                 const int32_t* __restrict__ pick_pos, int T, int k, int d,
+                                                 float scaling, const XT* __restrict__ residual,
+                                                 XT* __restrict__ y) {
+    const int t = blockIdx.y;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= d) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const float wj = w[(size_t)t * k + j];
+        const float4 v = *(const float4*)(o + (size_t)pick_pos[(size_t)t * k + j] * d + c);
+        acc.x = fmaf(wj, v.x, acc.x);
+        acc.y = fmaf(wj, v.y, acc.y);
+        acc.z = fmaf(wj, v.z, acc.z);
+        acc.w = fmaf(wj, v.w, acc.w);
+    }
+    float r[4] = {acc.x * scaling, acc.y * scaling, acc.z * scaling, acc.w * scaling};
+    const size_t b = (size_t)t * d + c;
+    if (residual) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] += load_act(residual, b + i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_act(y, b + i, r[i]);
+}
+
+hipError_t launch_combine(const moe_shape* s, const float* o, const float* w, const int32_t* pick_pos,
+                          int T, const void* residual, void* y, hipStream_t st) {
+    const int d = s->d_model;
+    dim3 grid((d / 4 + 255) / 256, T);
+    if (s->act_dtype == MOE_DT_BF16)
+        hipLaunchKernelGGL(k_combine<uint16_t>, grid, dim3(256), 0, st, o, w, pick_pos, T, s->top_k, d,
+                           s->routed_scaling, (const uint16_t*)residual, (uint16_t*)y);
+    else
+        hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, st, o, w, pick_pos, T, s->top_k, d,
+                           s->routed_scaling, (const float*)residual, (float*)y);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// expert table from fixed-stride blobs [gate_q | up_q | down_q | gate_s | up_s | down_s | ts]
+// ---------------------------------------------------------------------------------------------
+struct BlobSizes {
+    size_t nq, ns;
+};
+
+static BlobSizes blob_sizes(const moe_shape* s) {
+    const size_t B = s->wformat == MOE_WF_MXFP4 ? 32 : 16;
+    const size_t fd = (size_t)s->d_model * s->d_ff;
+    return {fd / 2, fd / B};
+}
+
+__global__ void k_fill_table(const uint8_t* __restrict__ base, size_t stride, int E, size_t nq, size_t ns,
+                             int nv, moe_expert* __restrict__ table) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= E) return;
+    const uint8_t* b = base + (size_t)e * stride;
+    moe_expert m;
+    m.gate_q = b;
+    m.up_q = b + nq;
+    m.down_q = b + 2 * nq;
+    m.gate_s = b + 3 * nq;
+    m.up_s = b + 3 * nq + ns;
+    m.down_s = b + 3 * nq + 2 * ns;
+    m.gate_ts = m.up_ts = m.down_ts = 1.0f;
+    m.reserved = 0.0f;
+    if (nv) {
+        const float* ts = (const float*)(b + 3 * nq + 3 * ns);
+        m.gate_ts = ts[0];
+        m.up_ts = ts[1];
+        m.down_ts = ts[2];
+    }
+    table[e] = m;
+}
+
+hipError_t launch_fill_table(const moe_shape* s, const uint8_t* base, size_t stride, moe_expert* table,
+                             hipStream_t st) {
+    const BlobSizes z = blob_sizes(s);
+    hipLaunchKernelGGL(k_fill_table, dim3((s->n_experts + 255) / 256), dim3(256), 0, st, base, stride,
+                       s->n_experts, z.nq, z.ns, (int)(s->wformat == MOE_WF_NVFP4), table);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// gather: copy the listed experts into contiguous staging with 16-byte loads ("A hot expert
+// cache ...", section "A gather kernel that reads wide": wide reads from a device-resident list)
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gather(const moe_expert* __restrict__ table,
+                                                const int32_t* __restrict__ list, int n, size_t nq,
+                                                size_t ns, size_t stride, uint8_t* __restrict__ staging,
+                                                moe_expert* __restrict__ staged) {
+    const int i = blockIdx.y;
+    const moe_expert src = table[list[i]];
+    uint8_t* dst = staging + (size_t)i * stride;
+    const size_t n16 = (3 * nq + 3 * ns) / 16;
+    for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n16; u += (size_t)gridDim.x * 256) {
+        const size_t off = u * 16;
+        const uint8_t* sp;
+        if (off < nq) sp = src.gate_q + off;
+        else if (off < 2 * nq) sp = src.up_q + (off - nq);
+        else if (off < 3 * nq) sp = src.down_q + (off - 2 * nq);
+        else if (off < 3 * nq + ns) sp = src.gate_s + (off - 3 * nq);
+        else if (off < 3 * nq + 2 * ns) sp = src.up_s + (off - 3 * nq - ns);
+        else sp = src.down_s + (off - 3 * nq - 2 * ns);
+        *(uint4*)(dst + off) = *(const uint4*)sp;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        moe_expert m;
+        m.gate_q = dst;
+        m.up_q = dst + nq;
+        m.down_q = dst + 2 * nq;
+        m.gate_s = dst + 3 * nq;
+        m.up_s = dst + 3 * nq + ns;
+        m.down_s = dst + 3 * nq + 2 * ns;
+        m.gate_ts = src.gate_ts;
+        m.up_ts = src.up_ts;
+        m.down_ts = src.down_ts;
+        m.reserved = 0.0f;
+        float* ts = (float*)(dst + 3 * nq + 3 * ns);
+        if (stride >= 3 * nq + 3 * ns + 12) {
+            ts[0] = src.gate_ts;
+            ts[1] = src.up_ts;
+            ts[2] = src.down_ts;
+        }
+        staged[i] = m;
+    }
+}
+
+hipError_t launch_gather(const moe_shape* s, const moe_expert* table, const int32_t* list, int n,
+                         uint8_t* staging, size_t stride, moe_expert* staged, hipStream_t st) {
+    const BlobSizes z = blob_sizes(s);
+    dim3 grid(64, n);
+    hipLaunchKernelGGL(k_gather, grid, dim3(256), 0, st, table, list, n, z.nq, z.ns, stride, staging, staged);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,129 @@
+// Permute: group the picks by expert on the device (a counting sort, stable in pick order), and
+// plan the grouped-GEMM tiles from the per-expert offsets.  The expert list never leaves the
+// GPU ("A hot expert cache made a 181 GiB model faster ...", section "A gather kernel that reads
+// wide": a device-resident list lets the CPU stay out of the step).
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / 64;
+
+// Block-wide exclusive scan of one int per thread (1024 threads).  Returns the exclusive
+// prefix; *total receives the sum.  Uses `scratch` (kPermWaves ints) in LDS.
+__device__ int block_excl_scan(int v, int* scratch, int* total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) scratch[wv] = incl;
+    __syncthreads();
+    int wbase = 0, tot = 0;
+    for (int w = 0; w < kPermWaves; ++w) {
+        int s = scratch[w];
+        if (w < wv) wbase += s;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return wbase + incl - v;
+}
+
+// One workgroup of 1024 threads.  LDS: counts and running cursors per expert, and per-wave
+// counts of the current chunk (for the stable rank across waves).
+__global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restrict__ idx, int P, int E,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_pick,
+                                                          int32_t* __restrict__ pick_pos) {
+    __shared__ int cnt[1024];
+    __shared__ int run[1024];
+    __shared__ int wcnt[kPermWaves][1024];
+    __shared__ int scratch[kPermWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int e = tid; e < 1024; e += kPermThreads) cnt[e] = 0;
+    for (int i = tid; i < kPermWaves * 1024; i += kPermThreads) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += kPermThreads) {
+        int e = idx[p];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    int total;
+    int excl = block_excl_scan(tid < E ? cnt[tid] : 0, scratch, &total);
+    if (tid < E) {
+        offsets[tid] = excl;
+        run[tid] = excl;
+    }
+    if (tid == 0) offsets[E] = total;
+    __syncthreads();
+    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < P; base += kPermThreads) {
+        const int p = base + tid;
+        int e = (p < P) ? idx[p] : -1;
+        if (e >= E) e = -1;
+        // lanes of this wave holding the same expert id
+        unsigned long long peers = __ballot(e >= 0);
+#pragma unroll
+        for (int b = 0; b < 10; ++b) {
+            unsigned long long m = __ballot((e >> b) & 1);
+            peers &= ((e >> b) & 1) ? m : ~m;
+        }
+        const int rank = __popcll(peers & lt_mask);
+        const int n = __popcll(peers);
+        if (e >= 0 && rank == 0) wcnt[wv][e] = n;
+        __syncthreads();
+        if (e >= 0) {
+            int pos = run[e] + rank;
+            for (int w = 0; w < wv; ++w) pos += wcnt[w][e];
+            sorted_pick[pos] = p;
+            pick_pos[p] = pos;
+        }
+        __syncthreads();
+        if (e >= 0 && rank == 0) {
+            atomicAdd(&run[e], n);
+            wcnt[wv][e] = 0;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_permute(const moe_shape* s, const int32_t* idx, int T, int32_t* offsets,
+                          int32_t* sorted_pick, int32_t* pick_pos, hipStream_t st) {
+    const int P = T * s->top_k;
+    hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), 0, st, idx, P, s->n_experts, offsets,
+                       sorted_pick, pick_pos);
+    return hipGetLastError();
+}
+
+// Tiles of at most `tt` consecutive sorted positions of one expert: tiles[i] = (expert, first).
+__global__ __launch_bounds__(kPermThreads) void k_plan(const int32_t* __restrict__ offsets, int E, int tt,
+                                                       int32_t* __restrict__ tiles,
+                                                       int32_t* __restrict__ ntiles) {
+    __shared__ int scratch[kPermWaves];
+    const int e = threadIdx.x;
+    int n = 0, o0 = 0;
+    if (e < E) {
+        o0 = offsets[e];
+        n = offsets[e + 1] - o0;
+    }
+    const int nt = (n + tt - 1) / tt;
+    int total;
+    const int first = block_excl_scan(nt, scratch, &total);
+    for (int j = 0; j < nt; ++j) {
+        tiles[2 * (first + j)] = e;
+        tiles[2 * (first + j) + 1] = o0 + j * tt;
+    }
+    if (e == 0) *ntiles = total;
+}
+
+hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int tile_tokens, int32_t* tiles,
+                       int32_t* ntiles, hipStream_t st) {
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPermThreads), 0, st, offsets, s->n_experts, tile_tokens,
+                       tiles, ntiles);
+    return hipGetLastError();
+}
+
+}  // namespace moe

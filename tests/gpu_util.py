@@ -1,0 +1,79 @@
+"""Helpers shared by the GPU parity tests: build device inputs from ``synth``, run the HIP
+path through the C ABI binding, and gather what the oracle needs back on the host."""
+import dataclasses
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def tol(wl) -> float:
+    """Parity tolerance on rel-L2 of the layer output: 1e-4 for fp32, 8e-3 for bf16 output."""
+    return 1e-4 if wl.act_dtype == synth.F32 else 8e-3
+
+
+def shape_of(m, wl):
+    return m.make_shape(wl.d_model, wl.d_ff, wl.n_experts, wl.top_k, wl.wformat, wl.act_dtype,
+                        wl.routed_scaling)
+
+
+class DeviceLayer:
+    """One layer's inputs in HBM plus its expert table."""
+
+    def __init__(self, m, wl, layer=0, seed=0, host_gen=None):
+        if host_gen is None:
+            host_gen = wl.d_model * wl.d_ff * wl.n_experts <= 64 * 1024 * 1024
+        gen_dev = "cpu" if host_gen else "cuda"
+        lay = synth.make_layer(wl, layer, seed, gen_dev)
+        self.wl = wl
+        self.shape = shape_of(m, wl)
+        self.router = lay["router"].to("cuda").contiguous()
+        self.bias = None if lay["bias"] is None else lay["bias"].to("cuda").contiguous()
+        self.blob = lay["blob"].to("cuda").contiguous()
+        self.stride = self.blob.shape[1]
+        self.table = torch.empty(wl.n_experts * m.EXPERT_BYTES, dtype=torch.uint8, device="cuda")
+        m.moe_fill_table(self.shape, self.blob, self.stride, self.table)
+
+    def host_blobs(self, experts):
+        """Host copies of the given experts' blobs (None for the others), for the oracle."""
+        out = [None] * self.wl.n_experts
+        for e in sorted(set(int(v) for v in experts)):
+            out[e] = self.blob[e].cpu().numpy()
+        return out
+
+
+def run_layer(m, dl, x, residual=None):
+    wl = dl.wl
+    T = x.shape[0]
+    y = torch.empty_like(x)
+    idx = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, wl.top_k, dtype=torch.float32, device="cuda")
+    ws = m.workspace(dl.shape, T)
+    m.moe_layer(dl.shape, x, T, dl.router, dl.bias, dl.table, None, residual, y, idx, w, ws)
+    torch.cuda.synchronize()
+    return y, idx, w
+
+
+def oracle_layer(dl, x, idx_hint=None, residual=None, scaling=None):
+    wl = dl.wl
+    x64 = oracle.to_f64(x)
+    if idx_hint is None:
+        _, idx_hint, _ = oracle.route(x64, dl.router.cpu().numpy(),
+                                      None if dl.bias is None else dl.bias.cpu().numpy(), wl.top_k)
+    blobs = dl.host_blobs(np.asarray(idx_hint).reshape(-1))
+    res = None if residual is None else oracle.to_f64(residual)
+    return oracle.layer(x64, dl.router.cpu().numpy(), None if dl.bias is None else dl.bias.cpu().numpy(),
+                        blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat,
+                        wl.routed_scaling if scaling is None else scaling, res)
+
+
+def small(name="tiny", **kw):
+    return dataclasses.replace(synth.WORKLOADS[name], **kw)
