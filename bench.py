@@ -1,0 +1,434 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed mixture-of-experts FFN layer on one MI355X.
+
+Headline (one JSON line): MoE-layer tokens/s of the 42-layer GLM-5.3-Flash-class decode stack
+(d_model 4096, d_ff 2048, 288 MXFP4 experts, top-8, T=1, bf16 activations, flat routing), one
+step = one token through all 42 layers (x_{l+1} = x_l + y_l), replayed as one HIP graph, inputs
+resident in HBM.  The same line carries the dominant kernel's roofline (HIP events around that
+kernel inside the graph), the oracle timed on the host cores, and secondary measurements of
+the 4096-token prefill chunk and the 64-token batched decode with skewed routing.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only decode|prefill|batched]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP4_PEAK_TFLOPS = 10100.0      # dense MX-FP4 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0       # dense FP8 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s (decode T=1, prefill T=4096) + % of HBM/MFMA peak"
+
+
+# ---------------------------------------------------------------------------------------------
+# HIP runtime plumbing (events, graphs) through ctypes
+# ---------------------------------------------------------------------------------------------
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        P = ctypes.c_void_p
+        L = self.lib
+        L.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+        L.hipEventRecord.argtypes = [P, P]
+        L.hipEventSynchronize.argtypes = [P]
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+        L.hipStreamBeginCapture.argtypes = [P, ctypes.c_int]
+        L.hipStreamEndCapture.argtypes = [P, ctypes.POINTER(P)]
+        L.hipGraphInstantiate.argtypes = [ctypes.POINTER(P), P, P, P, ctypes.c_size_t]
+        L.hipGraphLaunch.argtypes = [P, P]
+        L.hipStreamSynchronize.argtypes = [P]
+        L.hipGraphExecDestroy.argtypes = [P]
+        L.hipGraphDestroy.argtypes = [P]
+        L.hipGetErrorString.restype = ctypes.c_char_p
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {self.lib.hipGetErrorString(rc).decode()}")
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        self._ok(self.lib.hipEventCreate(ctypes.byref(ev)), "hipEventCreate")
+        return ev.value
+
+    def record(self, ev, stream):
+        self._ok(self.lib.hipEventRecord(ev, stream), "hipEventRecord")
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        self._ok(self.lib.hipEventSynchronize(b), "hipEventSynchronize")
+        self._ok(self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b), "hipEventElapsedTime")
+        return ms.value
+
+    def capture(self, stream, fn):
+        """Capture fn() enqueued on `stream` into an instantiated graph."""
+        self._ok(self.lib.hipStreamBeginCapture(stream, 2), "hipStreamBeginCapture")   # relaxed mode
+        try:
+            fn()
+        finally:
+            g = ctypes.c_void_p()
+            self._ok(self.lib.hipStreamEndCapture(stream, ctypes.byref(g)), "hipStreamEndCapture")
+        ex = ctypes.c_void_p()
+        self._ok(self.lib.hipGraphInstantiate(ctypes.byref(ex), g, None, None, 0), "hipGraphInstantiate")
+        return ex.value, g.value
+
+    def launch(self, graph_exec, stream):
+        self._ok(self.lib.hipGraphLaunch(graph_exec, stream), "hipGraphLaunch")
+
+    def sync(self, stream):
+        self._ok(self.lib.hipStreamSynchronize(stream), "hipStreamSynchronize")
+
+
+class KernelTimer:
+    """Trace hook that records a HIP event pair around every kernel the library enqueues."""
+
+    def __init__(self, hip, names=None):
+        self.hip = hip
+        self.names = names
+        self.pairs = []          # (kernel, ev_begin, ev_end)
+        self.pool = []
+        self._open = {}
+
+    def _ev(self):
+        if self.pool:
+            return self.pool.pop()
+        return self.hip.event()
+
+    def __call__(self, kernel, phase, stream):
+        if self.names is not None and kernel not in self.names:
+            return
+        if phase == 0:
+            ev = self._ev()
+            self.hip.record(ev, stream)
+            self._open[kernel] = ev
+        else:
+            ev = self._ev()
+            self.hip.record(ev, stream)
+            self.pairs.append((kernel, self._open.pop(kernel), ev))
+
+    def durations_us(self):
+        """Durations of the recorded pairs; recycles their events."""
+        out = {}
+        for k, a, b in self.pairs:
+            out.setdefault(k, []).append(1000.0 * self.hip.elapsed_ms(a, b))
+            self.pool += [a, b]
+        self.pairs = []
+        return out
+
+
+def timed_kernels(hip, m, torch, stream, step, reps=3, log=print):
+    """Per-kernel durations (us) of step(), each kernel bracketed by HIP events on its stream.
+
+    The step is enqueued eagerly behind a GPU sleep that outlasts the host-side enqueue, so the
+    kernels then run back to back and no host latency falls between an event pair."""
+    timer = KernelTimer(hip)
+    per = {}
+    cycles = 200_000_000
+    m.moe_set_trace_hook(timer)
+    try:
+        for _ in range(reps):
+            s0, s1 = hip.event(), hip.event()
+            hip.record(s0, stream.cuda_stream)
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(cycles)
+            hip.record(s1, stream.cuda_stream)
+            t0 = time.perf_counter()
+            step()
+            host_ms = 1000.0 * (time.perf_counter() - t0)
+            hip.sync(stream.cuda_stream)
+            sleep_ms = hip.elapsed_ms(s0, s1)
+            if host_ms > sleep_ms:
+                log(f"# warning: host enqueue {host_ms:.1f} ms outlasted the {sleep_ms:.1f} ms GPU sleep")
+                cycles *= 2
+            for k, v in timer.durations_us().items():
+                per.setdefault(k, []).extend(v)
+    finally:
+        m.moe_set_trace_hook(None)
+    return per
+
+
+# ---------------------------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------------------------
+class Stack:
+    """n_layers MoE layers of one workload, all experts resident in HBM."""
+
+    def __init__(self, m, synth, torch, wl, n_layers, seed=0, log=print):
+        self.wl = wl
+        self.n = n_layers
+        d, E = wl.d_model, wl.n_experts
+        self.shape = m.make_shape(wl.d_model, wl.d_ff, E, wl.top_k, wl.wformat, wl.act_dtype, wl.routed_scaling)
+        stride = m.moe_blob_stride(self.shape)
+        t0 = time.time()
+        self.blob = torch.empty(n_layers, E, stride, dtype=torch.uint8, device="cuda")
+        self.router = torch.empty(n_layers, E, d, dtype=torch.float32, device="cuda")
+        self.bias = [None] * n_layers
+        self.table = torch.empty(n_layers, E * m.EXPERT_BYTES, dtype=torch.uint8, device="cuda")
+        for l in range(n_layers):
+            synth.fill_experts(self.blob[l], wl, l, seed)
+            self.router[l] = synth.make_router(wl, l, seed, "cuda")
+            b = synth.make_bias(wl, l, seed, "cuda")
+            self.bias[l] = None if b is None else b.contiguous()
+            m.moe_fill_table(self.shape, self.blob[l], stride, self.table[l])
+            if (l + 1) % 7 == 0 or l + 1 == n_layers:
+                torch.cuda.synchronize()
+                log(f"# generated {l + 1}/{n_layers} layers ({self.blob[:l + 1].numel() / 1e9:.1f} GB) "
+                    f"in {time.time() - t0:.1f} s")
+        torch.cuda.synchronize()
+
+
+def algorithmic_layer_bytes(wl, experts_touched, T):
+    """Bytes a layer must move at least: touched experts' blobs, the router, x and y."""
+    B = 32 if wl.wformat == 0 else 16
+    fd = wl.d_model * wl.d_ff
+    stride = 3 * fd // 2 + 3 * fd // B
+    act = 2 if wl.act_dtype == 1 else 4
+    return experts_touched * stride + wl.n_experts * wl.d_model * 4 + 2 * T * wl.d_model * act
+
+
+def gate_up_bytes(wl, experts):
+    B = 32 if wl.wformat == 0 else 16
+    fd = wl.d_model * wl.d_ff
+    return experts * (2 * fd // 2 + 2 * fd // B)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=42)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--only", choices=["decode", "prefill", "batched"], default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import routed_expert_ffn_router_amd as m
+    import synth
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    torch.cuda.set_device(0)
+    hip = Hip()
+    stream = torch.cuda.Stream()
+    S = stream.cuda_stream
+    out = {}
+    want = (lambda w: args.only is None or args.only == w)
+
+    # ---------------- decode stack (headline) ----------------
+    wl_dec = synth.WORKLOADS["decode"]
+    nl = args.layers
+    log(f"# building the {nl}-layer decode stack in HBM")
+    stack = Stack(m, synth, torch, wl_dec, nl, args.seed, log)
+
+    def run_stack(T, biases, x0, bufs, ws, keep=None):
+        """One step: T tokens through every layer, x_{l+1} = x_l + y_l (residual fused)."""
+        def fn():
+            cur = x0
+            for l in range(nl):
+                nxt = bufs[l % 2]
+                m.moe_layer(stack.shape, cur, T, stack.router[l], biases[l], stack.table[l], None, cur, nxt,
+                            None if keep is None else keep[0][l], None if keep is None else keep[1][l],
+                            ws, stream=S)
+                cur = nxt
+        return fn
+
+    result_kernels = {}
+    if want("decode") or want("batched"):
+        for name, T in (("decode", 1), ("batched", 64)):
+            if not want(name):
+                continue
+            wl = synth.WORKLOADS[name]
+            biases = [synth.make_bias(wl, l, args.seed, "cuda") for l in range(nl)]
+            x0 = synth.make_x(wl, args.seed, "cuda", tokens=T, tag=f"x_{name}")
+            bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+            ws = m.workspace(stack.shape, T)
+            idx_keep = torch.empty(nl, T, wl.top_k, dtype=torch.int32, device="cuda")
+            w_keep = torch.empty(nl, T, wl.top_k, dtype=torch.float32, device="cuda")
+            # eager reference step (keeps every layer's routing), then the graph
+            with torch.cuda.stream(stream):
+                run_stack(T, biases, x0, bufs, ws, keep=(idx_keep, w_keep))()
+            hip.sync(S)
+            y_eager = bufs[(nl - 1) % 2].clone()
+            gexec, _ = hip.capture(S, run_stack(T, biases, x0, bufs, ws, keep=(idx_keep, w_keep)))
+            for _ in range(3):      # replays reproduce the eager step bit for bit
+                hip.launch(gexec, S)
+                hip.sync(S)
+                assert torch.equal(bufs[(nl - 1) % 2].view(torch.int16), y_eager.view(torch.int16)), \
+                    "graph replay differs from the eager step"
+            for _ in range(args.warmup):
+                hip.launch(gexec, S)
+            hip.sync(S)
+            e0, e1 = hip.event(), hip.event()
+            torch.cuda.synchronize()
+            hip.record(e0, S)
+            for _ in range(args.steps):
+                hip.launch(gexec, S)
+            hip.record(e1, S)
+            ms = hip.elapsed_ms(e0, e1) / args.steps
+            torch.cuda.synchronize()
+            # per-kernel durations, HIP events around every kernel of an eager step
+            per = timed_kernels(hip, m, torch, stream, run_stack(T, biases, x0, bufs, ws), log=log)
+            kern = {k: float(np.mean(v)) for k, v in per.items()}
+            touched = [len(np.unique(idx_keep[l].cpu().numpy())) for l in range(nl)]
+            layer_bytes = float(np.mean([algorithmic_layer_bytes(wl, u, T) for u in touched]))
+            us_layer = 1000.0 * ms / nl
+            rec = {
+                "ms_per_step": ms, "us_per_layer": us_layer, "tokens": T, "layers": nl,
+                "layer_tokens_per_s": nl * T / (ms / 1000.0), "stack_tokens_per_s": T / (ms / 1000.0),
+                "algorithmic_bytes_per_layer": layer_bytes, "mean_experts_per_layer": float(np.mean(touched)),
+                "hbm_frac_layer": layer_bytes / (us_layer * 1e-6) / (HBM_PEAK_GBS * 1e9),
+                "kernels_us": kern,
+            }
+            gu_bytes = float(np.mean([gate_up_bytes(wl, u) for u in touched]))
+            rec["gate_up_roofline"] = {"bound": "hbm", "achieved": gu_bytes / (kern["gemm_gate_up"] * 1e-6) / 1e9,
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "bytes_per_launch": gu_bytes}
+            rec["gate_up_roofline"]["frac"] = rec["gate_up_roofline"]["achieved"] / HBM_PEAK_GBS
+            out[name] = rec
+            out[name + "_state"] = (idx_keep, w_keep, x0, bufs, ws)
+            log(f"# {name}: {ms:.3f} ms/step, {us_layer:.2f} us/layer, "
+                f"{rec['layer_tokens_per_s']:.0f} layer-tokens/s, {100 * rec['hbm_frac_layer']:.1f}% of HBM peak")
+            log(f"#   kernels (us): " + ", ".join(f"{k} {v:.2f}" for k, v in kern.items()))
+
+    # ---------------- prefill chunk (layer 0 of the stack, T=4096) ----------------
+    if want("prefill"):
+        wl = synth.WORKLOADS["prefill"]
+        T = wl.tokens
+        x = synth.make_x(wl, args.seed, "cuda", tokens=T, tag="x_prefill")
+        y = torch.empty_like(x)
+        idx = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
+        wts = torch.empty(T, wl.top_k, dtype=torch.float32, device="cuda")
+        ws = m.workspace(stack.shape, T)
+        call = lambda: m.moe_layer(stack.shape, x, T, stack.router[0], None, stack.table[0], None, None, y, idx,
+                                   wts, ws, stream=S)
+        for _ in range(max(2, args.warmup)):
+            call()
+        hip.sync(S)
+        e0, e1 = hip.event(), hip.event()
+        steps = max(3, args.steps // 5)
+        hip.record(e0, S)
+        for _ in range(steps):
+            call()
+        hip.record(e1, S)
+        ms = hip.elapsed_ms(e0, e1) / steps
+        per = timed_kernels(hip, m, torch, stream, call, log=log)
+        kern = {k: float(np.mean(v)) for k, v in per.items()}
+        flops = 2.0 * 3 * wl.d_model * wl.d_ff * T * wl.top_k
+        touched = len(np.unique(idx.cpu().numpy()))
+        bytes_ = algorithmic_layer_bytes(wl, touched, T)
+        floor_ms = max(bytes_ / (HBM_PEAK_GBS * 1e9), flops / (FP4_PEAK_TFLOPS * 1e12)) * 1e3
+        out["prefill"] = {
+            "ms_per_layer": ms, "tokens": T, "tokens_per_s": T / (ms / 1000.0),
+            "experts_active": touched, "algorithmic_bytes": bytes_, "algorithmic_tflop": flops / 1e12,
+            "hbm_frac": bytes_ / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "fp4_mfma_frac": flops / (ms * 1e-3) / (FP4_PEAK_TFLOPS * 1e12),
+            "roofline_frac": floor_ms / ms, "kernels_us": kern,
+        }
+        log(f"# prefill T={T}: {ms:.3f} ms/layer, {T / ms * 1e3:.0f} tokens/s, "
+            f"{100 * out['prefill']['roofline_frac']:.1f}% of the roofline bound")
+        log(f"#   kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern.items()))
+
+    # ---------------- oracle on the host cores (bounded sample of the decode stack) ------------
+    cpu = None
+    parity = None
+    if want("decode") and not args.no_cpu_baseline:
+        import oracle
+        idx_keep, w_keep, x0, bufs, ws = out["decode_state"]
+        # every layer's input x_l of the eager step, and its output y_l without the residual
+        xs = [x0]
+        ys = []
+        cur = x0
+        with torch.cuda.stream(stream):
+            for l in range(nl):
+                y_l = torch.empty_like(x0)
+                m.moe_layer(stack.shape, cur, 1, stack.router[l], None, stack.table[l], None, None, y_l, None, None,
+                            ws, stream=S)
+                nxt = torch.empty_like(x0)
+                m.moe_layer(stack.shape, cur, 1, stack.router[l], None, stack.table[l], None, cur, nxt, None, None,
+                            ws, stream=S)
+                xs.append(nxt)
+                ys.append(y_l)
+                cur = nxt
+        hip.sync(S)
+        t_cpu = 0.0
+        n_done = 0
+        worst = 0.0
+        exact = True
+        for l in range(nl):
+            sel = idx_keep[l].cpu().numpy().reshape(-1)
+            blobs = [None] * wl_dec.n_experts
+            for e in sel:
+                blobs[int(e)] = stack.blob[l, int(e)].cpu().numpy()
+            x64 = oracle.to_f64(xs[l])
+            wr = stack.router[l].cpu().numpy()
+            t0 = time.perf_counter()
+            oy, oidx, ow, _ = oracle.layer(x64, wr, None, blobs, wl_dec.d_model, wl_dec.d_ff, wl_dec.top_k,
+                                           wl_dec.wformat, 1.0, None)
+            t_cpu += time.perf_counter() - t0
+            n_done += 1
+            exact = exact and bool(np.array_equal(oidx, idx_keep[l].cpu().numpy()))
+            gy = oracle.to_f64(ys[l])
+            worst = max(worst, float(np.linalg.norm(gy - oy) / np.linalg.norm(oy)))
+            if t_cpu > args.cpu_seconds:
+                break
+        cpu = {"value": n_done / t_cpu, "unit": "layer-tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"decode stack, T=1, first {n_done} of {nl} layers on the GPU's own layer inputs "
+                         f"({t_cpu:.1f} s of fp64 oracle time)"}
+        parity = {"layers_checked": n_done, "router_indices_exact": exact, "worst_rel_l2_y": worst,
+                  "tolerance": 8e-3, "pass": bool(exact and worst <= 8e-3)}
+        log(f"# oracle: {cpu['value']:.3f} layer-tokens/s on {cpu['cores']} threads; parity {parity}")
+
+    # ---------------- the one JSON line ----------------
+    dec = out.get("decode")
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "mxfp4 x fp8-terms, fp32 accumulate", "data": "synthetic"}
+    if dec is not None:
+        line.update({
+            "value": dec["layer_tokens_per_s"], "unit": "layer-tokens/s", "ms_per_step": dec["ms_per_step"],
+            "config": {"workload": "decode: 42 stacked MoE layers, d_model 4096, d_ff 2048, 288 MXFP4 experts "
+                                   "(E2M1 + E8M0/32), top-8 sigmoid router, T=1, bf16 activations, flat routing",
+                       "layers": nl, "tokens_per_step": 1, "parallelism": "single GPU"},
+            "stack_tokens_per_s": dec["stack_tokens_per_s"], "us_per_layer": dec["us_per_layer"],
+            "hbm_frac_layer": dec["hbm_frac_layer"],
+            "roofline": {"bound": "hbm", "kernel": "gemm_gate_up (k_mx_gemm gate/up, 8 experts x 8.9 MB)",
+                         "achieved": dec["gate_up_roofline"]["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dec["gate_up_roofline"]["frac"], "traffic": None,
+                         "bytes_per_launch": dec["gate_up_roofline"]["bytes_per_launch"],
+                         "avg_launch_us": dec["kernels_us"]["gemm_gate_up"]},
+            "kernels_us": dec["kernels_us"],
+        })
+    else:
+        first = next(k for k in ("prefill", "batched") if k in out)
+        r = out[first]
+        line.update({"value": r.get("tokens_per_s", r.get("layer_tokens_per_s")), "unit": "tokens/s",
+                     "ms_per_step": r.get("ms_per_layer", r.get("ms_per_step")),
+                     "config": {"workload": first}})
+    line["cpu_baseline"] = cpu
+    line["parity"] = parity
+    for k in ("prefill", "batched"):
+        if k in out:
+            line[k] = {kk: vv for kk, vv in out[k].items()}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -164,6 +164,18 @@ moe_status moe_combine(const moe_shape *shape, const float *o, const float *topk
                        const int32_t *pick_pos, int32_t T, const void *residual, void *y,
                        hipStream_t stream);
 
+/* Tracing hook.  When set (non-NULL), every entry point calls hook(user, kernel, 0, stream)
+ * right before it enqueues each of its kernels and hook(user, kernel, 1, stream) right after,
+ * on the calling host thread; `kernel` is a static name ("router_logits", "topk",
+ * "act_split", "permute", "plan", "gemm_gate_up", "gemm_down", "combine", "fill_table",
+ * "gather").  A hook may record HIP events on `stream` to time one kernel in place (inside
+ * stream capture those become graph nodes).  This is the only process-wide state in the
+ * library; setting it while other threads are inside the library is a race.  Measuring each
+ * step where it runs follows the pages' practice of writing the measurement next to each design
+ * rule ("Project Maya ...", section "Three tiers and the rules between them"). */
+typedef void (*moe_trace_hook)(void *user, const char *kernel, int phase, hipStream_t stream);
+void moe_set_trace_hook(moe_trace_hook hook, void *user);
+
 /* The whole layer: moe_route, moe_permute, moe_expert_ffn and moe_combine on the stream,
  * with the intermediates in the workspace.  topk_idx_out / topk_w_out ([T][top_k], device)
  * are optional copies of the routing.  staging: unused for now (pass NULL).  y may not

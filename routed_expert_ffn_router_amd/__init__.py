@@ -66,11 +66,29 @@ _SIGS = {
     "moe_expert_ffn": (ctypes.c_int, [_SP, _P, _P, _i32, _P, _P, _P, _P, _sz, _P]),
     "moe_combine": (ctypes.c_int, [_SP, _P, _P, _P, _i32, _P, _P, _P]),
     "moe_layer": (ctypes.c_int, [_SP, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
+    "moe_set_trace_hook": (None, [_P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
     _fn.restype = _res
     _fn.argtypes = _args
+
+
+TRACE_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int, ctypes.c_void_p)
+_hook_ref = None
+
+
+def moe_set_trace_hook(hook):
+    """Install a Python callable hook(kernel: str, phase: int, stream: int), or None to clear.
+
+    The library calls it right before (phase 0) and after (phase 1) enqueuing each kernel."""
+    global _hook_ref
+    if hook is None:
+        _hook_ref = None
+        _lib.moe_set_trace_hook(None, None)
+        return
+    _hook_ref = TRACE_HOOK(lambda user, name, phase, stream: hook(name.decode(), phase, stream or 0))
+    _lib.moe_set_trace_hook(ctypes.cast(_hook_ref, ctypes.c_void_p), None)
 
 
 def header_functions() -> list:

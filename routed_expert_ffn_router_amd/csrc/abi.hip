@@ -7,6 +7,13 @@
 
 namespace moe {
 
+static moe_trace_hook g_hook = nullptr;
+static void* g_hook_user = nullptr;
+
+void trace(const char* kernel, int phase, hipStream_t st) {
+    if (g_hook) g_hook(g_hook_user, kernel, phase, st);
+}
+
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int act_terms(const moe_shape* s) { return s->act_dtype == MOE_DT_BF16 ? 2 : 4; }
@@ -116,6 +123,11 @@ using namespace moe;
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+void moe_set_trace_hook(moe_trace_hook hook, void* user) {
+    g_hook = hook;
+    g_hook_user = user;
+}
 
 const char* moe_status_string(moe_status status) {
     switch (status) {

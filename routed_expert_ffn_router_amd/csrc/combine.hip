@@ -34,6 +34,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, co
 
 hipError_t launch_combine(const moe_shape* s, const float* o, const float* w, const int32_t* pick_pos,
                           int T, const void* residual, void* y, hipStream_t st) {
+    trace("combine", 0, st);
     const int d = s->d_model;
     dim3 grid((d / 4 + 255) / 256, T);
     if (s->act_dtype == MOE_DT_BF16)
@@ -42,6 +43,7 @@ hipError_t launch_combine(const moe_shape* s, const float* o, const float* w, co
     else
         hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, st, o, w, pick_pos, T, s->top_k, d,
                            s->routed_scaling, (const float*)residual, (float*)y);
+    trace("combine", 1, st);
     return hipGetLastError();
 }
 
@@ -83,9 +85,11 @@ __global__ void k_fill_table(const uint8_t* __restrict__ base, size_t stride, in
 
 hipError_t launch_fill_table(const moe_shape* s, const uint8_t* base, size_t stride, moe_expert* table,
                              hipStream_t st) {
+    trace("fill_table", 0, st);
     const BlobSizes z = blob_sizes(s);
     hipLaunchKernelGGL(k_fill_table, dim3((s->n_experts + 255) / 256), dim3(256), 0, st, base, stride,
                        s->n_experts, z.nq, z.ns, (int)(s->wformat == MOE_WF_NVFP4), table);
+    trace("fill_table", 1, st);
     return hipGetLastError();
 }
 
@@ -136,9 +140,11 @@ __global__ __launch_bounds__(256) void k_gather(const moe_expert* __restrict__ t
 
 hipError_t launch_gather(const moe_shape* s, const moe_expert* table, const int32_t* list, int n,
                          uint8_t* staging, size_t stride, moe_expert* staged, hipStream_t st) {
+    trace("gather", 0, st);
     const BlobSizes z = blob_sizes(s);
     dim3 grid(64, n);
     hipLaunchKernelGGL(k_gather, grid, dim3(256), 0, st, table, list, n, z.nq, z.ns, stride, staging, staged);
+    trace("gather", 1, st);
     return hipGetLastError();
 }
 

@@ -263,11 +263,17 @@ static hipError_t launch_gemm(const GemmArgs& a, int NT, int variant, int max_ti
 }
 
 hipError_t launch_gemm_gateup(const GemmArgs& a, int NT, int variant, int max_tiles, hipStream_t st) {
-    return launch_gemm<true>(a, NT, variant, max_tiles, st);
+    trace("gemm_gate_up", 0, st);
+    hipError_t e = launch_gemm<true>(a, NT, variant, max_tiles, st);
+    trace("gemm_gate_up", 1, st);
+    return e;
 }
 
 hipError_t launch_gemm_down(const GemmArgs& a, int NT, int variant, int max_tiles, hipStream_t st) {
-    return launch_gemm<false>(a, NT, variant, max_tiles, st);
+    trace("gemm_down", 0, st);
+    hipError_t e = launch_gemm<false>(a, NT, variant, max_tiles, st);
+    trace("gemm_down", 1, st);
+    return e;
 }
 
 }  // namespace moe

@@ -125,6 +125,9 @@ __device__ __forceinline__ void split_terms(float (&v)[N], uint32_t (&codes)[NT]
 // launchers (one per kernel family); all return hipGetLastError() of their launch
 // ---------------------------------------------------------------------------------------------
 
+// tracing hook (set through moe_set_trace_hook); every launcher brackets its launch with these
+void trace(const char* kernel, int phase, hipStream_t st);
+
 struct WsLayout {
     size_t logits, idx, w, offsets, sorted_pick, pick_pos, tiles, ntiles, xq, xs, hq, hs, o, total;
     int nt;        // activation terms

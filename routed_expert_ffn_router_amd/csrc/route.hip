@@ -109,6 +109,7 @@ __global__ __launch_bounds__(256) void k_logits_tiled(const XT* __restrict__ x, 
 
 hipError_t launch_router_logits(const moe_shape* s, const void* x, int T, const float* wr,
                                 const float* bias, double* logits, hipStream_t st) {
+    trace("router_logits", 0, st);
     const int d = s->d_model, E = s->n_experts;
     const bool bf = s->act_dtype == MOE_DT_BF16;
     if (T <= 8) {
@@ -128,6 +129,7 @@ hipError_t launch_router_logits(const moe_shape* s, const void* x, int T, const 
             hipLaunchKernelGGL((k_logits_tiled<float>), grid, dim3(256), 0, st,
                                (const float*)x, T, d, wr, bias, E, logits);
     }
+    trace("router_logits", 1, st);
     return hipGetLastError();
 }
 
@@ -191,8 +193,10 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
 
 hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t* idx, float* w,
                        hipStream_t st) {
+    trace("topk", 0, st);
     dim3 grid((T + 3) / 4);
     hipLaunchKernelGGL(k_topk, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, idx, w);
+    trace("topk", 1, st);
     return hipGetLastError();
 }
 
@@ -224,6 +228,7 @@ __global__ __launch_bounds__(256) void k_act_split(const XT* __restrict__ x, int
 
 hipError_t launch_act_split(const moe_shape* s, const void* x, int rows, int K, int SS, int NT,
                             uint8_t* q, uint8_t* sc, hipStream_t st) {
+    trace("act_split", 0, st);
     const size_t n = (size_t)rows * (K / 32);
     dim3 grid((unsigned)((n + 255) / 256));
     const bool bf = s->act_dtype == MOE_DT_BF16;
@@ -234,6 +239,7 @@ hipError_t launch_act_split(const moe_shape* s, const void* x, int rows, int K, 
     else if (!bf && NT == 2) MOE_SPLIT(float, 2);
     else MOE_SPLIT(float, 4);
 #undef MOE_SPLIT
+    trace("act_split", 1, st);
     return hipGetLastError();
 }
 
