@@ -103,7 +103,10 @@ const char *moe_status_string(moe_status status);
 size_t moe_blob_stride(const moe_shape *shape);
 
 /* Bytes of workspace the entry points need for T tokens (moe_layer needs the most; every
- * other call needs no more).  Returns 0 for a bad shape or T. */
+ * other call needs no more).  Returns 0 for a bad shape or T.  A workspace must be zero-filled
+ * once before its first use (a memset at allocation): moe_layer keeps a completion counter in
+ * it that every call leaves at zero again.  Calls that overlap in time need distinct
+ * workspaces. */
 size_t moe_workspace_bytes(const moe_shape *shape, int32_t T);
 
 /* Fill a DEVICE expert table from n_experts blobs laid out at base + e * stride (stride >=
@@ -177,7 +180,10 @@ typedef void (*moe_trace_hook)(void *user, const char *kernel, int phase, hipStr
 void moe_set_trace_hook(moe_trace_hook hook, void *user);
 
 /* The whole layer: moe_route, moe_permute, moe_expert_ffn and moe_combine on the stream,
- * with the intermediates in the workspace.  topk_idx_out / topk_w_out ([T][top_k], device)
+ * with the intermediates in the workspace (zero-filled before its first use).  For T <= 16
+ * (and T * top_k <= 512, top_k <= 64) the layer runs as three launches: the router fused with
+ * the permute, the tile plan and the activation split; the gate/up GEMM; and the down GEMM
+ * fused with the combine.  topk_idx_out / topk_w_out ([T][top_k], device)
  * are optional copies of the routing.  staging: unused for now (pass NULL).  y may not
  * alias x; it may alias residual. */
 moe_status moe_layer(const moe_shape *shape, const void *x, int32_t T, const float *w_router,

@@ -153,10 +153,10 @@ def moe_workspace_bytes(shape: moe_shape, T: int) -> int:
 
 
 def workspace(shape: moe_shape, T: int, device="cuda"):
-    """A uint8 device tensor of moe_workspace_bytes(shape, T) bytes (at least 256)."""
+    """A zero-filled uint8 device tensor of moe_workspace_bytes(shape, T) bytes (at least 256)."""
     import torch
     n = max(moe_workspace_bytes(shape, T), 256)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def moe_fill_table(shape, base, stride: int, table, stream=None):

@@ -7,6 +7,8 @@
 
 namespace moe {
 
+constexpr int kSmallTokens = 16;   // moe_layer's fused three-launch path
+
 static moe_trace_hook g_hook = nullptr;
 static void* g_hook_user = nullptr;
 
@@ -29,6 +31,7 @@ WsLayout ws_layout(const moe_shape* s, int32_t T) {
     L.max_tiles = (int)((E < P ? E : P) + P / tt + 1);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
+    L.counter = take(4);
     L.logits = take(8 * (size_t)T * E);
     L.idx = take(4 * P);
     L.w = take(4 * P);
@@ -80,19 +83,8 @@ static moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : M
         if ((expr) != hipSuccess) return MOE_ERR_HIP; \
     } while (0)
 
-// sequence shared by moe_expert_ffn and moe_layer
-static moe_status run_ffn(const moe_shape* s, const moe_expert* table, const void* x, int32_t T,
-                          const int32_t* offsets, const int32_t* sorted_pick, float* o, uint8_t* ws,
-                          const WsLayout& L, hipStream_t st) {
-    const int variant = gemm_variant(s, T);
-    const int NT = L.nt;
-    const int tt = gemm_tile_tokens(variant, NT);
-    int32_t* tiles = (int32_t*)(ws + L.tiles);
-    int32_t* ntiles = (int32_t*)(ws + L.ntiles);
-    MOE_HIP(launch_plan(s, offsets, tt, tiles, ntiles, st));
-    const int ks1 = (variant == 0 && (s->d_model / 4) % 128 == 0) ? 4 : 1;
-    const int SS1 = super_step(s->d_model, ks1);
-    MOE_HIP(launch_act_split(s, x, T, s->d_model, SS1, NT, ws + L.xq, ws + L.xs, st));
+static GemmArgs gemm_args(const moe_shape* s, const moe_expert* table, int32_t T, const int32_t* sorted_pick,
+                          const int32_t* offsets, uint8_t* ws, const WsLayout& L, float* o) {
     GemmArgs a;
     a.table = table;
     a.d = s->d_model;
@@ -101,14 +93,28 @@ static moe_status run_ffn(const moe_shape* s, const moe_expert* table, const voi
     a.k = s->top_k;
     a.P = T * s->top_k;
     a.sorted_pick = sorted_pick;
-    a.tiles = tiles;
-    a.ntiles = ntiles;
+    a.tiles = (const int32_t*)(ws + L.tiles);
+    a.ntiles = (const int32_t*)(ws + L.ntiles);
     a.offsets = offsets;
     a.aq = ws + L.xq;
     a.as = ws + L.xs;
     a.hq = ws + L.hq;
     a.hs = ws + L.hs;
     a.o = o;
+    return a;
+}
+
+// sequence shared by moe_expert_ffn and moe_layer (general token counts)
+static moe_status run_ffn(const moe_shape* s, const moe_expert* table, const void* x, int32_t T,
+                          const int32_t* offsets, const int32_t* sorted_pick, float* o, uint8_t* ws,
+                          const WsLayout& L, hipStream_t st) {
+    const int variant = gemm_variant(s, T);
+    const int NT = L.nt;
+    const int tt = gemm_tile_tokens(variant, NT);
+    MOE_HIP(launch_plan(s, offsets, tt, (int32_t*)(ws + L.tiles), (int32_t*)(ws + L.ntiles), st));
+    const int SS1 = super_step(s->d_model, ksplit_for(s->d_model, variant));
+    MOE_HIP(launch_act_split(s, x, T, s->d_model, SS1, NT, ws + L.xq, ws + L.xs, st));
+    GemmArgs a = gemm_args(s, table, T, sorted_pick, offsets, ws, L, o);
     MOE_HIP(launch_gemm_gateup(a, NT, variant, L.max_tiles, st));
     a.aq = ws + L.hq;
     a.as = ws + L.hs;
@@ -249,6 +255,52 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
     int32_t* sorted_pick = (int32_t*)(w8 + L.sorted_pick);
     int32_t* pick_pos = (int32_t*)(w8 + L.pick_pos);
     float* o = (float*)(w8 + L.o);
+    if (T <= kSmallTokens && s->top_k <= 64 && (long long)T * s->top_k <= kMaxFusedPicks &&
+        s->d_model <= 8192) {
+        // few tokens: fused router (logits, top-k, permute, plan, activation split), the gate/up
+        // GEMM, and the down GEMM fused with the weighted combine: three launches per layer
+        const int NT = L.nt;
+        const int variant = 0;
+        RouteSmallArgs r;
+        r.x = x;
+        r.T = T;
+        r.d = s->d_model;
+        r.E = s->n_experts;
+        r.k = s->top_k;
+        r.wr = w_router;
+        r.bias = logit_bias;
+        r.logits = logits;
+        r.counter = (uint32_t*)(w8 + L.counter);
+        r.idx = idx;
+        r.w = w;
+        r.offsets = offsets;
+        r.sorted_pick = sorted_pick;
+        r.pick_pos = pick_pos;
+        r.tiles = (int32_t*)(w8 + L.tiles);
+        r.ntiles = (int32_t*)(w8 + L.ntiles);
+        r.tt = gemm_tile_tokens(variant, NT);
+        r.xq = w8 + L.xq;
+        r.xs = w8 + L.xs;
+        r.ss1 = super_step(s->d_model, ksplit_for(s->d_model, variant));
+        const bool dec = decode_gemm_ok(s);
+        if (dec) r.ss1 = 4;   // x terms in chunks of 512: the layout k_mx_gateup_dec reads
+        MOE_HIP(launch_route_small(s, r, stream));
+        GemmArgs a = gemm_args(s, d_table, T, sorted_pick, offsets, w8, L, o);
+        if (dec) MOE_HIP(launch_gateup_dec(a, NT, L.max_tiles, stream));
+        else MOE_HIP(launch_gemm_gateup(a, NT, variant, L.max_tiles, stream));
+        a.aq = w8 + L.hq;
+        a.as = w8 + L.hs;
+        CombineArgs c;
+        c.T = T;
+        c.w = w;
+        c.pick_pos = pick_pos;
+        c.residual = residual;
+        c.y = y;
+        c.scaling = s->routed_scaling;
+        if (dec) MOE_HIP(launch_down_dec(s, a, c, NT, stream));
+        else MOE_HIP(launch_down_combine(s, a, c, NT, stream));
+        return MOE_OK;
+    }
     MOE_HIP(launch_router_logits(s, x, T, w_router, logit_bias, logits, stream));
     MOE_HIP(launch_topk(s, logits, T, idx, w, stream));
     MOE_HIP(launch_permute(s, idx, T, offsets, sorted_pick, pick_pos, stream));

@@ -12,6 +12,76 @@ namespace moe {
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------------------------
+// wave reductions on DPP lane permutations (quad_perm xor 1 / xor 2, row half-mirror, row
+// mirror, row broadcast 15 / 31), which avoid the LDS round trip of a shuffle; the result is
+// complete in lane 63 and broadcast with readlane.  Fixed combination order: deterministic.
+// ---------------------------------------------------------------------------------------------
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWMASK, 0xF, false);
+}
+
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = dpp_u32<CTRL, ROWMASK>(0u, (uint32_t)b), hi = dpp_u32<CTRL, ROWMASK>(0u, (uint32_t)(b >> 32));
+    return v + __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// sum over the 64 lanes of a wave, returned in every lane
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v = dpp_add_f64<kDppXor1, 0xF>(v);
+    v = dpp_add_f64<kDppXor2, 0xF>(v);
+    v = dpp_add_f64<kDppHalfMirror, 0xF>(v);
+    v = dpp_add_f64<kDppMirror, 0xF>(v);
+    v = dpp_add_f64<kDppBcast15, 0xA>(v);
+    v = dpp_add_f64<kDppBcast31, 0xC>(v);
+    return readlane_f64(v, 63);
+}
+
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ void argmax_step(unsigned long long& key, int& idx) {
+    const uint32_t lo = dpp_u32<CTRL, ROWMASK>((uint32_t)key, (uint32_t)key);
+    const uint32_t hi = dpp_u32<CTRL, ROWMASK>((uint32_t)(key >> 32), (uint32_t)(key >> 32));
+    const int oi = (int)dpp_u32<CTRL, ROWMASK>((uint32_t)idx, (uint32_t)idx);
+    const unsigned long long ok = ((unsigned long long)hi << 32) | lo;
+    if (ok > key || (ok == key && oi < idx)) { key = ok; idx = oi; }
+}
+
+// the (largest key, then smallest idx) pair of the wave, returned in every lane
+__device__ __forceinline__ void wave_argmax(unsigned long long& key, int& idx) {
+    argmax_step<kDppXor1, 0xF>(key, idx);
+    argmax_step<kDppXor2, 0xF>(key, idx);
+    argmax_step<kDppHalfMirror, 0xF>(key, idx);
+    argmax_step<kDppMirror, 0xF>(key, idx);
+    argmax_step<kDppBcast15, 0xA>(key, idx);
+    argmax_step<kDppBcast31, 0xC>(key, idx);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
+    key = ((unsigned long long)hi << 32) | lo;
+    idx = __builtin_amdgcn_readlane(idx, 63);
+}
+
+// maximum over each 16-lane row, returned in every lane of the row
+__device__ __forceinline__ float row16_max(float m) {
+    m = fmaxf(m, __uint_as_float(dpp_u32<kDppXor1, 0xF>(__float_as_uint(m), __float_as_uint(m))));
+    m = fmaxf(m, __uint_as_float(dpp_u32<kDppXor2, 0xF>(__float_as_uint(m), __float_as_uint(m))));
+    m = fmaxf(m, __uint_as_float(dpp_u32<kDppHalfMirror, 0xF>(__float_as_uint(m), __float_as_uint(m))));
+    m = fmaxf(m, __uint_as_float(dpp_u32<kDppMirror, 0xF>(__float_as_uint(m), __float_as_uint(m))));
+    return m;
+}
+
+// ---------------------------------------------------------------------------------------------
 // element formats (device side)
 // ---------------------------------------------------------------------------------------------
 
@@ -34,6 +104,45 @@ __device__ __forceinline__ float load_act<uint16_t>(const uint16_t* p, size_t i)
 
 template <typename XT>
 __device__ __forceinline__ double load_act_f64(const XT* p, size_t i) { return (double)load_act<XT>(p, i); }
+
+// four consecutive activations starting at a multiple of 4
+template <typename XT>
+__device__ __forceinline__ float4 load_act4(const XT* p, size_t i);
+template <>
+__device__ __forceinline__ float4 load_act4<float>(const float* p, size_t i) { return *(const float4*)(p + i); }
+template <>
+__device__ __forceinline__ float4 load_act4<uint16_t>(const uint16_t* p, size_t i) {
+    const uint2 u = *(const uint2*)(p + i);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+// Router logit of one expert row for token t, fp64 accumulation of exact products, in every
+// lane of the wave.  The row is read in chunks of 8 float4 per lane with all loads of a chunk
+// issued together; loops over chunks and tokens stay rolled to keep the code small.
+template <typename XT>
+__device__ __forceinline__ double wave_logit(const XT* __restrict__ xt, int d, const float* __restrict__ row) {
+    const int lane = threadIdx.x & 63;
+    double acc = 0.0;
+#pragma unroll 1
+    for (int base = 0; base < d; base += 256 * 8) {
+        float4 w4[8], x4[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = base + u * 256 + lane * 4;
+            w4[u] = (i < d) ? *(const float4*)(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+            x4[u] = (i < d) ? load_act4(xt, i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            acc = fma((double)x4[u].x, (double)w4[u].x, acc);
+            acc = fma((double)x4[u].y, (double)w4[u].y, acc);
+            acc = fma((double)x4[u].z, (double)w4[u].z, acc);
+            acc = fma((double)x4[u].w, (double)w4[u].w, acc);
+        }
+    }
+    return wave_sum_f64(acc);
+}
 
 template <typename XT>
 __device__ __forceinline__ void store_act(XT* p, size_t i, float v);
@@ -121,6 +230,43 @@ __device__ __forceinline__ void split_terms(float (&v)[N], uint32_t (&codes)[NT]
     }
 }
 
+// The same split with one element per lane: 32 lanes (half a wave) share a block, the block
+// maximum comes from xor-shuffles, and lanes 4i..4i+3 pack their four code bytes into one word.
+// Rows [0, T) of x (length d) are covered by the threads of workgroups wg, wg + nwg, ...
+template <typename XT, int NT>
+__device__ __forceinline__ void split_rows_lanewise(const XT* __restrict__ x, int T, int d, int SS,
+                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
+                                                    int wg, int nwg) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 31;
+    const int groups = d / 32;
+    const size_t nblk = (size_t)T * groups;
+    const size_t per_wg = (blockDim.x / 32);
+    for (size_t b0 = (size_t)wg * per_wg; b0 < nblk; b0 += (size_t)nwg * per_wg) {
+        const size_t blk_all = b0 + (threadIdx.x >> 5);
+        const bool ok = blk_all < nblk;          // uniform per 32-lane half
+        const int row = ok ? (int)(blk_all / groups) : 0, blk = ok ? (int)(blk_all % groups) : 0;
+        float v = ok ? load_act(x, (size_t)row * d + blk * 32 + i) : 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            float m = row16_max(fabsf(v));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            const int S = split_exponent(m);
+            const uint32_t c = e4m3_encode(ldexpf(v, -S));
+            v -= ldexpf(e4m3_decode(c), S);
+            uint32_t word = c << (8 * (i & 3));
+            word |= dpp_u32<kDppXor1, 0xF>(word, word);
+            word |= dpp_u32<kDppXor2, 0xF>(word, word);
+            if (ok && (i & 3) == 0) {
+                const int half = i >> 4;
+                uint8_t* base = q + ((size_t)row * NT + t) * d;
+                *(uint32_t*)(base + act_half_offset(SS, blk, half) + (i & 15)) = word;
+            }
+            if (ok && i == 0) sc[((size_t)row * NT + t) * groups + blk] = (uint8_t)(S + 127);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------------------
 // launchers (one per kernel family); all return hipGetLastError() of their launch
 // ---------------------------------------------------------------------------------------------
@@ -129,7 +275,7 @@ __device__ __forceinline__ void split_terms(float (&v)[N], uint32_t (&codes)[NT]
 void trace(const char* kernel, int phase, hipStream_t st);
 
 struct WsLayout {
-    size_t logits, idx, w, offsets, sorted_pick, pick_pos, tiles, ntiles, xq, xs, hq, hs, o, total;
+    size_t counter, logits, idx, w, offsets, sorted_pick, pick_pos, tiles, ntiles, xq, xs, hq, hs, o, total;
     int nt;        // activation terms
     int max_tiles;
 };
@@ -149,6 +295,28 @@ hipError_t launch_permute(const moe_shape* s, const int32_t* idx, int T, int32_t
 hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int tile_tokens, int32_t* tiles,
                        int32_t* ntiles, hipStream_t st);
 
+// fused few-token router (route + permute + plan + activation split); T <= 16, P <= 1024
+struct RouteSmallArgs {
+    const void* x;
+    int T, d, E, k;
+    const float* wr;
+    const float* bias;
+    double* logits;
+    uint32_t* counter;        // zero before the launch; the launch leaves it zero
+    int32_t* idx;
+    float* w;
+    int32_t* offsets;
+    int32_t* sorted_pick;
+    int32_t* pick_pos;
+    int32_t* tiles;
+    int32_t* ntiles;
+    int tt;                   // tokens per GEMM tile
+    uint8_t* xq;
+    uint8_t* xs;
+    int ss1;                  // MFMAs per chunk of the gate/up GEMM (activation layout)
+};
+hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipStream_t st);
+
 struct GemmArgs {
     const moe_expert* table;
     int d, f, E, k, P;
@@ -163,12 +331,33 @@ struct GemmArgs {
     float* o;                 // down output [P][d]
 };
 
+// picks whose per-row outputs the fused down+combine kernel keeps in LDS (P = T * top_k)
+constexpr int kMaxFusedPicks = 512;
+constexpr int kMaxDecSlices = 2;          // d_ff / 1024 K slices kept in LDS by the down kernel
+
+struct CombineArgs {
+    int T;
+    const float* w;           // [T][k] route weights
+    const int32_t* pick_pos;  // [T][k] sorted position of each pick
+    const void* residual;     // [T][d] or null
+    void* y;                  // [T][d]
+    float scaling;
+};
+
 // variant: 0 = few tokens per expert (16 columns per tile, K split over the 4 waves when
 // possible); 1 = many tokens per expert (128 columns per tile)
 int gemm_variant(const moe_shape* s, int T);
 int gemm_tile_tokens(int variant, int NT);
 hipError_t launch_gemm_gateup(const GemmArgs& a, int NT, int variant, int max_tiles, hipStream_t st);
 hipError_t launch_gemm_down(const GemmArgs& a, int NT, int variant, int max_tiles, hipStream_t st);
+hipError_t launch_down_combine(const moe_shape* s, const GemmArgs& a, const CombineArgs& c, int NT,
+                               hipStream_t st);
+int ksplit_for(int K, int variant);
+// few-token GEMMs with 16 small waves per workgroup (d_model / 4 a multiple of 512, d_ff a
+// multiple of 1024 and at most 2048)
+bool decode_gemm_ok(const moe_shape* s);
+hipError_t launch_gateup_dec(const GemmArgs& a, int NT, int max_tiles, hipStream_t st);
+hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineArgs& c, int NT, hipStream_t st);
 
 hipError_t launch_combine(const moe_shape* s, const float* o, const float* w, const int32_t* pick_pos,
                           int T, const void* residual, void* y, hipStream_t st);
