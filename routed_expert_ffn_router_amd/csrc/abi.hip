@@ -27,7 +27,9 @@ WsLayout ws_layout(const moe_shape* s, int32_t T) {
     const size_t P = (size_t)T * k;
     L.nt = act_terms(s);
     const int variant = gemm_variant(s, T);
-    const size_t tt = (size_t)gemm_tile_tokens(variant, L.nt);
+    size_t tt = (size_t)gemm_tile_tokens(variant, L.nt);
+    // the fused few-token path tiles with the smaller few-token tile: bound for both
+    if (T <= kSmallTokens && (size_t)gemm_tile_tokens(0, L.nt) < tt) tt = (size_t)gemm_tile_tokens(0, L.nt);
     L.max_tiles = (int)((E < P ? E : P) + P / tt + 1);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
@@ -40,6 +42,7 @@ WsLayout ws_layout(const moe_shape* s, int32_t T) {
     L.pick_pos = take(4 * P);
     L.tiles = take(8 * (size_t)L.max_tiles);
     L.ntiles = take(4);
+    L.desc = take(sizeof(TileDesc) * (size_t)L.max_tiles);
     L.xq = take((size_t)T * L.nt * d);
     L.xs = take((size_t)T * L.nt * d / 32);
     L.hq = take(P * L.nt * f);
@@ -96,6 +99,8 @@ static GemmArgs gemm_args(const moe_shape* s, const moe_expert* table, int32_t T
     a.tiles = (const int32_t*)(ws + L.tiles);
     a.ntiles = (const int32_t*)(ws + L.ntiles);
     a.offsets = offsets;
+    a.desc = (const TileDesc*)(ws + L.desc);
+    a.max_tiles = L.max_tiles;
     a.aq = ws + L.xq;
     a.as = ws + L.xs;
     a.hq = ws + L.hq;
@@ -278,6 +283,9 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
         r.pick_pos = pick_pos;
         r.tiles = (int32_t*)(w8 + L.tiles);
         r.ntiles = (int32_t*)(w8 + L.ntiles);
+        r.desc = (TileDesc*)(w8 + L.desc);
+        r.table = d_table;
+        r.max_tiles = L.max_tiles;
         r.tt = gemm_tile_tokens(variant, NT);
         r.xq = w8 + L.xq;
         r.xs = w8 + L.xs;

@@ -26,6 +26,19 @@ namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+// loads through global-address-space pointers: global_load rather than flat_load (pointers read
+// from memory are generic otherwise, and a flat load also holds up LDS waits)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(const void* p) {
+    const u32x4_t v = *(__attribute__((address_space(1))) const u32x4_t*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t gload4(const void* p) {
+    return *(__attribute__((address_space(1))) const uint32_t*)p;
+}
+__device__ __forceinline__ int32_t gload_i32(const void* p) {
+    return *(__attribute__((address_space(1))) const int32_t*)p;
+}
 
 template <int SS>
 __device__ __forceinline__ uint32_t load_scale_word(const uint8_t* p) {
@@ -41,7 +54,7 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const uint4& a, const uint4& b0, con
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 0, 0, sa, 0, sb);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // acc[f][n] += A_f x B_n over nss super-steps (SS MFMAs each), CH super-steps per load burst.
 // aq/as: per-lane pointers to this lane's first weight block/scale; bq/bs: activation columns.
@@ -107,12 +120,7 @@ __device__ __forceinline__ void sum_terms(v4f (&acc)[NA][NTN]) {
 #pragma unroll
         for (int n = 0; n < NTN; ++n)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = acc[f][n][r];
-                v += __shfl_xor(v, 1);
-                if (NT == 4) v += __shfl_xor(v, 2);
-                acc[f][n][r] = v;
-            }
+            for (int r = 0; r < 4; ++r) acc[f][n][r] = sum_adjacent<NT>(acc[f][n][r]);
 }
 
 template <int NT, int NTN, int KSPLIT, int SS, bool GATEUP>
@@ -210,10 +218,7 @@ __global__ __launch_bounds__(256) void k_mx_gemm(GemmArgs a, int ss2) {
             }
             uint32_t codes[NT][2];
             int S[NT];
-            split_terms<NT>(v, codes, S, [](float m) {
-                m = fmaxf(m, __shfl_xor(m, 16));
-                return fmaxf(m, __shfl_xor(m, 32));
-            });
+            split_terms<NT>(v, codes, S, [](float m) { return max_xor32(max_xor16(m)); });
             const int tc = n * (16 / NT) + li / NT, tme = li % NT;
             if (tc < ntok) {
                 const size_t pos = (size_t)i0 + tc;
@@ -302,42 +307,144 @@ __global__ __launch_bounds__(512) void k_mx_down_combine(GemmArgs a, CombineArgs
 constexpr int kDecKSlice = 1024;          // K elements per wave (512 bytes of codes per row)
 
 // gate/up for one tile of picks and one 32-row block: eight waves, wave w = (16-row tile
-// f = w/2: gate rows 0-15, gate 16-31, up 0-15, up 16-31; K half ks = w%2).  512 threads and at
-// most 128 VGPRs per wave let two workgroups share a CU, so one workgroup's epilogue overlaps
-// the other's loads.
+// f = w/2: gate rows 0-15, gate 16-31, up 0-15, up 16-31; K half ks = w%2).  Every wave issues
+// all of its weight loads (16 MFMAs' worth, 64 VGPRs) at once; the tile's x terms are staged in
+// LDS by the whole workgroup meanwhile, so the FP8 operand costs no registers.  512 threads and
+// at most 128 VGPRs per wave (four waves per SIMD: the second launch bound) let two workgroups
+// share a CU, so one's epilogue overlaps the other's loads.
+constexpr int kDecCols = 16;              // MFMA columns: (token, term) pairs of a tile
+constexpr int kDecMaxD = 4096;            // d_model staged per column
+constexpr int kDecSteps = 16;             // MFMAs per wave (K / 2 = 2048 at d_model 4096)
+
 template <int NT>
-__global__ __launch_bounds__(512, 2) void k_mx_gateup_dec(GemmArgs a, int ss2) {
-    constexpr int SS = 4, TT = 16 / NT;
-    const int tile = blockIdx.x;
-    if (tile >= *a.ntiles) return;
-    const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
-    const int ntok = min(TT, a.offsets[e + 1] - i0);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, int nwg) {
+    constexpr int SS = 4, NSS = kDecSteps / SS;
+    __shared__ __align__(16) uint8_t b_lds[kDecCols][kDecMaxD + 16];
+    __shared__ __align__(16) uint8_t bs_lds[kDecCols][kDecMaxD / 32];
+    __shared__ float4 part[8][64];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int f = wave >> 1, ks = wave & 1;
     const int K = a.d;
-    const int rg = blockIdx.y;
+    const int nss = (K / 2) / (128 * SS);     // super-steps of this wave (<= NSS)
+    // (tile, 32-row block) pairs p = tile * nrg + rg, taken by the workgroups in turn; the grid
+    // never exceeds the pairs of max_tiles tiles, so the first record read is always in bounds
+    const int nrg = a.f / 32;
+    for (int pair = blockIdx.x;; pair += nwg) {          // nwg = grid size, passed as an argument
+    const int tile = __builtin_amdgcn_readfirstlane(pair / nrg), rg = __builtin_amdgcn_readfirstlane(pair % nrg);
+    // one round trip: the 128-byte tile record (lane l holds bytes 16(l%8)..+16) and the tile count
+    const uint8_t* rec_base = (const uint8_t*)(a.desc + tile);
+    const uint4 rec = gload16(rec_base + 16 * (lane & 7));
+    const int nt = gload_i32(a.ntiles);
+    asm volatile("" ::"v"(rec.x), "v"(rec.y), "v"(rec.z), "v"(rec.w), "v"(nt));
+    auto field64 = [&](int byte) -> const uint8_t* {
+        const uint32_t comp[4] = {rec.x, rec.y, rec.z, rec.w};
+        const int l = byte / 16, c = (byte % 16) / 4;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)comp[c], l);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)comp[c + 1], l);
+        return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+    };
+    const int ntile_count = __builtin_amdgcn_readfirstlane(nt);
+    if (tile >= ntile_count) break;
+    const uint8_t* const gq = field64(offsetof(moe_expert, gate_q));
+    const uint8_t* const uq = field64(offsetof(moe_expert, up_q));
+    const uint8_t* const gs = field64(offsetof(moe_expert, gate_s));
+    const uint8_t* const us = field64(offsetof(moe_expert, up_s));
+    const int i0 = __builtin_amdgcn_readlane((int)rec.x, offsetof(TileDesc, i0) / 16);
+    const int ntok = __builtin_amdgcn_readlane((int)rec.y, offsetof(TileDesc, i0) / 16);
     const int row = 32 * rg + 16 * (f & 1) + li;
-    const int nss = (K / 2) / (128 * SS);
     const int kss0 = ks * nss;
-    const moe_expert ex = a.table[e];
-    const uint8_t* mq = (f >= 2) ? ex.up_q : ex.gate_q;
-    const uint8_t* ms = (f >= 2) ? ex.up_s : ex.gate_s;
-    const uint8_t* const aq[1] = {mq + (size_t)row * (K / 2) + lg * 16 * SS + (size_t)kss0 * 64 * SS};
-    const uint8_t* const as[1] = {ms + (size_t)row * (K / 32) + lg * SS + (size_t)kss0 * 4 * SS};
-    const int tc = li / NT, t = li % NT;
-    const bool bval[1] = {tc < ntok};
-    const size_t arow = bval[0] ? (size_t)(a.sorted_pick[i0 + tc] / a.k) : 0;
-    const uint8_t* const bq[1] = {a.aq + (arow * NT + t) * K + lg * 32 * SS + (size_t)kss0 * 128 * SS};
-    const uint8_t* const bs[1] = {a.as + (arow * NT + t) * (K / 32) + lg * SS + (size_t)kss0 * 4 * SS};
-    v4f acc[1][1] = {{v4f{0.f, 0.f, 0.f, 0.f}}};
-    mx_accumulate<1, 1, SS, 2>(aq, as, bq, bs, bval, nss, acc);
-
-    __shared__ float4 part[8][64];
-    part[wave][lane] = make_float4(acc[0][0][0], acc[0][0][1], acc[0][0][2], acc[0][0][3]);
+    // 1. the tile's x terms (ncol columns of K code bytes and K/32 scale bytes) are staged in LDS,
+    // one 16-byte chunk per thread and round; the token of this thread's first chunk is read
+    // before the weights are requested
+    const int ncol = ntok * NT;
+    const int nchunk = ncol * (K / 16), ntotal = nchunk + ncol * (K / 512);
+    auto chunk_col = [&](int g, int& off) {
+        const bool data = g < nchunk;
+        const int per = data ? K / 16 : K / 512;
+        const int gg = data ? g : g - nchunk;
+        off = (gg % per) * 16;
+        return gg / per;
+    };
+    auto chunk_src = [&](int g, int tok, int c, int off) -> const uint8_t* {
+        const size_t tokrow = (size_t)tok * NT + c % NT;
+        return g < nchunk ? a.aq + tokrow * K + off : a.as + tokrow * (K / 32) + off;
+    };
+    auto chunk_dst = [&](int g, int c, int off) -> uint4* {
+        return g < nchunk ? (uint4*)&b_lds[c][off] : (uint4*)&bs_lds[c][off];
+    };
+    // token of a chunk's column: tok[c / NT] of the record, fetched from lanes 5-6 of `rec`
+    auto chunk_tok = [&](int c) {
+        const int ti = c / NT, src = (5 + (ti >> 2)) << 2;
+        const int cx = __builtin_amdgcn_ds_bpermute(src, (int)rec.x);
+        const int cy = __builtin_amdgcn_ds_bpermute(src, (int)rec.y);
+        const int cz = __builtin_amdgcn_ds_bpermute(src, (int)rec.z);
+        const int cw = __builtin_amdgcn_ds_bpermute(src, (int)rec.w);
+        const int sel = ti & 3;
+        return sel == 0 ? cx : (sel == 1 ? cy : (sel == 2 ? cz : cw));
+    };
+    const int g0 = tid < ntotal ? tid : ntotal - 1;
+    int off0;
+    const int c0 = chunk_col(g0, off0);
+    const int tok0 = chunk_tok(c0);
+    // 2. this wave's weights: all loads at once (super-steps past nss re-read the last one)
+    const uint8_t* mq = (f >= 2) ? uq : gq;
+    const uint8_t* ms = (f >= 2) ? us : gs;
+    const uint8_t* aq = (mq + (size_t)row * (K / 2) + lg * 16 * SS + (size_t)kss0 * 64 * SS);
+    const uint8_t* as = (ms + (size_t)row * (K / 32) + lg * SS + (size_t)kss0 * 4 * SS);
+    uint4 A[NSS][SS];
+    uint32_t sa[NSS];
+#pragma unroll
+    for (int q = 0; q < NSS; ++q) {
+        const int qq = q < nss ? q : nss - 1;
+#pragma unroll
+        for (int h = 0; h < SS; ++h) A[q][h] = gload16(aq + (size_t)qq * 64 * SS + 16 * h);
+        sa[q] = gload4(as + (size_t)qq * 4 * SS);
+    }
+    // 3. the x-term chunks (their data arrives with the weights; stored to LDS after)
+    {
+        const uint4 v = gload16(chunk_src(g0, tok0, c0, off0));
+        if (tid < ntotal) *chunk_dst(g0, c0, off0) = v;
+    }
+    for (int g = tid + 512; g < ntotal; g += 512) {      // more than 512 chunks: tiles of many picks
+        int off;
+        const int c = chunk_col(g, off);
+        const int tok = gload_i32(&(a.desc + tile)->tok[c / NT]);   // divergent: no lane permute here
+        const uint4 v = gload16(chunk_src(g, tok, c, off));
+        *chunk_dst(g, c, off) = v;
+    }
     __syncthreads();
-    if (wave > 0) return;
+    // 4. MFMAs, FP8 operand from LDS, one super-step's operands read before its MFMAs (columns
+    // past the tile read its last column; their results are not used)
+    const int col = li < ncol ? li : ncol - 1;
+    const uint8_t* bl = &b_lds[col][(size_t)kss0 * 128 * SS + lg * 32 * SS];
+    const uint8_t* bsl = &bs_lds[col][kss0 * 4 * SS + lg * SS];
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NSS; ++q) {
+        if (q < nss) {
+            const uint32_t sb = *(const uint32_t*)(bsl + q * 4 * SS);
+            uint4 B[SS][2];
+#pragma unroll
+            for (int h = 0; h < SS; ++h) {
+                B[h][0] = *(const uint4*)(bl + q * 128 * SS + 32 * h);
+                B[h][1] = *(const uint4*)(bl + q * 128 * SS + 32 * h + 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h = 0; h < SS; ++h)
+                acc = mfma_fp4_fp8(A[q][h], B[h][0], B[h][1], acc, (int)((sa[q] >> (8 * h)) & 0xffu),
+                                   (int)((sb >> (8 * h)) & 0xffu));
+        }
+    }
+
+    part[wave][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+    if (wave == 0) {
     // wave 0: add the two K halves of each 16-row tile, then SwiGLU and the split of the block
+    // (the other waves go on to the next pair; its LDS fill barrier waits for this wave)
+    const int tc = li / NT, t = li % NT;
     v4f gu[4][1];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -353,10 +460,7 @@ __global__ __launch_bounds__(512, 2) void k_mx_gateup_dec(GemmArgs a, int ss2) {
     }
     uint32_t codes[NT][2];
     int S[NT];
-    split_terms<NT>(v, codes, S, [](float mm) {
-        mm = fmaxf(mm, __shfl_xor(mm, 16));
-        return fmaxf(mm, __shfl_xor(mm, 32));
-    });
+    split_terms<NT>(v, codes, S, [](float mm) { return max_xor32(max_xor16(mm)); });
     if (tc < ntok) {
         const size_t pos = (size_t)i0 + tc;
         uint32_t w0 = codes[0][0], w1 = codes[0][1];
@@ -369,6 +473,9 @@ __global__ __launch_bounds__(512, 2) void k_mx_gateup_dec(GemmArgs a, int ss2) {
         *(uint32_t*)(dst + act_half_offset(ss2, rg, 1) + 4 * lg) = w1;
         if (lg == 0) a.hs[(pos * NT + t) * (size_t)(a.f / 32) + rg] = (uint8_t)(Sme + 127);
     }
+    }
+    if (pair + nwg >= ntile_count * nrg) break;
+    }
 }
 
 // down projection + weighted combine for few picks: workgroup = 16 output rows; its 16 waves
@@ -376,23 +483,24 @@ __global__ __launch_bounds__(512, 2) void k_mx_gateup_dec(GemmArgs a, int ss2) {
 // per pick in LDS, and the workgroup sums slices and picks in a fixed order.
 template <typename XT, int NT>
 __global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs c) {
-    constexpr int SS = 4, TT = 16 / NT;
+    constexpr int SS = 4;
     __shared__ float o_part[kMaxDecSlices][kMaxFusedPicks][16];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int r0 = blockIdx.x * 16;
     const int K = a.f;
     const int nsl = K / kDecKSlice;
     const int nss = kDecKSlice / (128 * SS);
-    const int units = *a.ntiles * nsl;
+    const int units = a.max_tiles * nsl;
     for (int unit = wave; unit < units; unit += 8) {
         const int tile = unit / nsl, ks = unit % nsl;
-        const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
-        const int ntok = min(TT, a.offsets[e + 1] - i0);
-        const moe_expert ex = a.table[e];
+        const TileDesc& D = a.desc[tile];
+        const int ntok = D.ntok;
+        if (ntok == 0) continue;
+        const int i0 = D.i0;
         const int kss0 = ks * nss;
-        const uint8_t* const aq[1] = {ex.down_q + (size_t)(r0 + li) * (K / 2) + lg * 16 * SS + (size_t)kss0 * 64 * SS};
-        const uint8_t* const as[1] = {ex.down_s + (size_t)(r0 + li) * (K / 32) + lg * SS + (size_t)kss0 * 4 * SS};
+        const uint8_t* const aq[1] = {D.ex.down_q + (size_t)(r0 + li) * (K / 2) + lg * 16 * SS + (size_t)kss0 * 64 * SS};
+        const uint8_t* const as[1] = {D.ex.down_s + (size_t)(r0 + li) * (K / 32) + lg * SS + (size_t)kss0 * 4 * SS};
         const int tc = li / NT, t = li % NT;
         const bool bval[1] = {tc < ntok};
         const size_t arow = bval[0] ? (size_t)(i0 + tc) : 0;
@@ -425,16 +533,199 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs 
     }
 }
 
+// down projection + weighted combine for very few picks (P * NT <= 32, d_ff <= 2048): one
+// workgroup of 16 output rows per CU.  Round trip 1 fetches the tile records and the combine's
+// inputs; then every pick's h terms are requested (for LDS) ahead of each wave's weight loads for
+// two (tile, K slice) units, so the FP8 operand comes from LDS and costs no registers.
+constexpr int kDownLdsCols = 32;
+constexpr int kDownMaxF = 2048;
+constexpr int kDownMaxTiles = 32;
+constexpr int kDownFillRounds = (kDownLdsCols * (kDownMaxF / 16 + kDownMaxF / 512) + 511) / 512;
+
+template <typename XT, int NT>
+__global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineArgs c) {
+    constexpr int SS = 4, NSS = kDecKSlice / (128 * SS);
+    constexpr int MAXP = kDownLdsCols / NT;
+    __shared__ __align__(16) uint8_t b_lds[kDownLdsCols][kDownMaxF + 16];
+    __shared__ __align__(16) uint8_t bs_lds[kDownLdsCols][kDownMaxF / 32];
+    __shared__ __align__(16) TileDesc d_lds[kDownMaxTiles];
+    __shared__ float o_part[kMaxDecSlices][MAXP][16];
+    __shared__ float s_wq[MAXP];
+    __shared__ int s_posq[MAXP];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int r0 = blockIdx.x * 16;
+    const int K = a.f;
+    const int nsl = K / kDecKSlice;
+    const int P = a.P, ncols = P * NT;
+    // 1. tile records (16-byte chunks, one per thread), this thread's pick weight and position,
+    // and the residual of the output it will write (thread q = tid writes token q/16, row
+    // r0 + q%16): one round trip
+    const int nd = a.max_tiles * 8;
+    const uint4 dv = gload16((const uint8_t*)a.desc + (size_t)(tid < nd ? tid : nd - 1) * 16);
+    const int pq = tid < P ? tid : P - 1;
+    const float wq = c.w[pq];
+    const int posq = c.pick_pos[pq];
+    const int oq = tid < c.T * 16 ? tid : c.T * 16 - 1;
+    const size_t yoff = (size_t)(oq >> 4) * a.d + r0 + (oq & 15);
+    const XT* rsrc = c.residual ? (const XT*)c.residual : (const XT*)c.y;   // read, used only with a residual
+    const float resq = load_act(rsrc, yoff);
+    asm volatile("" ::"v"(dv.x), "v"(dv.y), "v"(dv.z), "v"(dv.w), "v"(wq), "v"(posq), "v"(resq));
+    if (tid < nd) *((uint4*)&d_lds[0] + tid) = dv;
+    if (tid < P) {
+        s_wq[tid] = wq;
+        s_posq[tid] = posq;
+    }
+    __syncthreads();
+    // 2. every pick's h codes and scales (first P*NT rows of the h terms) for LDS: requested
+    // before the weights, so that waiting for them does not wait for the weights
+    const int nb = ncols * (K / 16), ntot = nb + ncols * (K / 512);
+    uint4 v[kDownFillRounds];
+#pragma unroll
+    for (int r = 0; r < kDownFillRounds; ++r) {
+        int g = r * 512 + tid;
+        g = g < ntot ? g : ntot - 1;
+        // one address by selects, one load: no branch between the loads of the round
+        const uintptr_t base = g < nb ? (uintptr_t)a.aq : (uintptr_t)a.as;
+        const int gi = g < nb ? g : g - nb;
+        v[r] = gload16((const void*)(base + (size_t)gi * 16));
+    }
+    // 3. the weights of this wave's first two units (tile, K slice): u0 = wave, u1 = wave + 8
+    const int units = a.max_tiles * nsl;
+    const int tc = li / NT, t = li % NT;
+    auto unit_ok = [&](int u) { return u < units && d_lds[u / nsl].ntok > 0; };
+    // loads of units u0 and u0 + 8; a unit without a tile re-reads the other one's weights, and
+    // nothing is read when neither has a tile (records of absent tiles are never dereferenced)
+    auto load_units = [&](int u0, uint4 (&A)[2][NSS][SS], uint32_t (&sa)[2][NSS], bool& ok0, bool& ok1,
+                          int (&us)[2]) {
+        const int u1 = u0 + 8;
+        ok0 = unit_ok(u0);
+        ok1 = unit_ok(u1);
+        if (!ok0 && !ok1) return;
+        us[1] = ok1 ? u1 : u0;
+        us[0] = ok0 ? u0 : us[1];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const TileDesc& D = d_lds[us[j] / nsl];
+            const int kss0 = (us[j] % nsl) * NSS;
+            const uint8_t* aq = D.ex.down_q + (size_t)(r0 + li) * (K / 2) + lg * 16 * SS + (size_t)kss0 * 64 * SS;
+            const uint8_t* as = D.ex.down_s + (size_t)(r0 + li) * (K / 32) + lg * SS + (size_t)kss0 * 4 * SS;
+#pragma unroll
+            for (int q = 0; q < NSS; ++q) {
+#pragma unroll
+                for (int h = 0; h < SS; ++h) A[j][q][h] = gload16(aq + (size_t)q * 64 * SS + 16 * h);
+                sa[j][q] = gload4(as + (size_t)q * 4 * SS);
+            }
+        }
+    };
+    auto run_units = [&](const uint4 (&A)[2][NSS][SS], const uint32_t (&sa)[2][NSS], bool ok0, bool ok1,
+                         const int (&us)[2]) {
+        if (!ok0 && !ok1) return;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (!(j == 0 ? ok0 : ok1)) continue;
+            const TileDesc& D = d_lds[us[j] / nsl];
+            const int ks = us[j] % nsl, kss0 = ks * NSS;
+            const int ntok = D.ntok, i0 = D.i0;
+            const int colp = i0 + (tc < ntok ? tc : ntok - 1);
+            const uint8_t* bl = &b_lds[colp * NT + t][(size_t)kss0 * 128 * SS + lg * 32 * SS];
+            const uint8_t* bsl = &bs_lds[colp * NT + t][kss0 * 4 * SS + lg * SS];
+            v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < NSS; ++q) {
+                const uint32_t sb = *(const uint32_t*)(bsl + q * 4 * SS);
+                uint4 B[SS][2];
+#pragma unroll
+                for (int h = 0; h < SS; ++h) {
+                    B[h][0] = *(const uint4*)(bl + q * 128 * SS + 32 * h);
+                    B[h][1] = *(const uint4*)(bl + q * 128 * SS + 32 * h + 16);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int h = 0; h < SS; ++h)
+                    acc = mfma_fp4_fp8(A[j][q][h], B[h][0], B[h][1], acc, (int)((sa[j][q] >> (8 * h)) & 0xffu),
+                                       (int)((sb >> (8 * h)) & 0xffu));
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = sum_adjacent<NT>(acc[r]);
+            if (tc < ntok && t == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o_part[ks][i0 + tc][4 * lg + r] = acc[r];
+            }
+        }
+    };
+    uint4 A[2][NSS][SS];
+    uint32_t sa[2][NSS];
+    bool ok0, ok1;
+    int us[2];
+    load_units(wave, A, sa, ok0, ok1, us);
+    __builtin_amdgcn_sched_barrier(0);
+    // 4. h terms into LDS (their loads were issued first), then the MFMAs of the first units
+#pragma unroll
+    for (int r = 0; r < kDownFillRounds; ++r) asm volatile("" ::"v"(v[r].x), "v"(v[r].y), "v"(v[r].z), "v"(v[r].w));
+#pragma unroll
+    for (int r = 0; r < kDownFillRounds; ++r) {
+        const int g = r * 512 + tid;
+        if (g < nb) {
+            const int col = g / (K / 16);
+            *(uint4*)&b_lds[col][(g % (K / 16)) * 16] = v[r];
+        } else if (g < ntot) {
+            const int gg = g - nb, col = gg / (K / 512);
+            *(uint4*)&bs_lds[col][(gg % (K / 512)) * 16] = v[r];
+        }
+    }
+    __syncthreads();
+    run_units(A, sa, ok0, ok1, us);
+    for (int u0 = wave + 16; u0 < units; u0 += 16) {      // more than sixteen units: further pairs
+        load_units(u0, A, sa, ok0, ok1, us);
+        run_units(A, sa, ok0, ok1, us);
+    }
+    __syncthreads();
+    // 5. y[t][r] = scaling * sum_j w[t,j] * (sum over K slices of o) (+ residual), rank order j
+    const int k = a.k;
+    if (tid < c.T * 16) {
+        const int tok = tid >> 4, r = tid & 15;
+        float accv = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int p = tok * k + j;
+            const int pos = s_posq[p];
+            float o = 0.f;
+            for (int sl = 0; sl < nsl; ++sl) o += o_part[sl][pos][r];
+            accv = fmaf(s_wq[p], o, accv);
+        }
+        float val = accv * c.scaling;
+        if (c.residual) val += resq;
+        store_act((XT*)c.y, yoff, val);
+    }
+}
+
 bool decode_gemm_ok(const moe_shape* s) {
-    return (s->d_model / 2) % 512 == 0 && s->d_ff % kDecKSlice == 0 && s->d_ff / kDecKSlice <= kMaxDecSlices;
+    return (s->d_model / 2) % 512 == 0 && s->d_model <= kDecMaxD && s->d_ff % kDecKSlice == 0 &&
+           s->d_ff / kDecKSlice <= kMaxDecSlices;
+}
+
+// compute units of the current device (cached per device)
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
 }
 
 hipError_t launch_gateup_dec(const GemmArgs& a, int NT, int max_tiles, hipStream_t st) {
     trace("gemm_gate_up", 0, st);
     const int ss2 = 4;   // h terms in chunks of 512: the layout k_mx_down_dec reads
-    dim3 grid(max_tiles, a.f / 32);
-    if (NT == 2) hipLaunchKernelGGL(k_mx_gateup_dec<2>, grid, dim3(512), 0, st, a, ss2);
-    else hipLaunchKernelGGL(k_mx_gateup_dec<4>, grid, dim3(512), 0, st, a, ss2);
+    // two workgroups per CU, each taking (tile, row block) pairs in turn
+    const long long pairs = (long long)max_tiles * (a.f / 32);
+    dim3 grid((unsigned)(pairs < 2LL * device_cus() ? pairs : 2LL * device_cus()));
+    if (NT == 2) hipLaunchKernelGGL(k_mx_gateup_dec<2>, grid, dim3(512), 0, st, a, ss2, (int)grid.x);
+    else hipLaunchKernelGGL(k_mx_gateup_dec<4>, grid, dim3(512), 0, st, a, ss2, (int)grid.x);
     trace("gemm_gate_up", 1, st);
     return hipGetLastError();
 }
@@ -443,6 +734,17 @@ hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineA
     trace("down_combine", 0, st);
     dim3 grid(a.d / 16);
     const bool bf = s->act_dtype == MOE_DT_BF16;
+    if (a.P * NT <= kDownLdsCols && a.f <= kDownMaxF && a.max_tiles <= kDownMaxTiles) {
+        if (bf) {
+            if (NT == 2) hipLaunchKernelGGL((k_mx_down_dec_lds<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
+            else hipLaunchKernelGGL((k_mx_down_dec_lds<uint16_t, 4>), grid, dim3(512), 0, st, a, c);
+        } else {
+            if (NT == 2) hipLaunchKernelGGL((k_mx_down_dec_lds<float, 2>), grid, dim3(512), 0, st, a, c);
+            else hipLaunchKernelGGL((k_mx_down_dec_lds<float, 4>), grid, dim3(512), 0, st, a, c);
+        }
+        trace("down_combine", 1, st);
+        return hipGetLastError();
+    }
     if (bf) {
         if (NT == 2) hipLaunchKernelGGL((k_mx_down_dec<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
         else hipLaunchKernelGGL((k_mx_down_dec<uint16_t, 4>), grid, dim3(512), 0, st, a, c);

@@ -55,7 +55,10 @@ __device__ __forceinline__ void argmax_step(unsigned long long& key, int& idx) {
     const uint32_t hi = dpp_u32<CTRL, ROWMASK>((uint32_t)(key >> 32), (uint32_t)(key >> 32));
     const int oi = (int)dpp_u32<CTRL, ROWMASK>((uint32_t)idx, (uint32_t)idx);
     const unsigned long long ok = ((unsigned long long)hi << 32) | lo;
-    if (ok > key || (ok == key && oi < idx)) { key = ok; idx = oi; }
+    // bitwise, not short-circuit: selects instead of branches
+    const bool better = (ok > key) | ((ok == key) & (oi < idx));
+    key = better ? ok : key;
+    idx = better ? oi : idx;
 }
 
 // the (largest key, then smallest idx) pair of the wave, returned in every lane
@@ -79,6 +82,24 @@ __device__ __forceinline__ float row16_max(float m) {
     m = fmaxf(m, __uint_as_float(dpp_u32<kDppHalfMirror, 0xF>(__float_as_uint(m), __float_as_uint(m))));
     m = fmaxf(m, __uint_as_float(dpp_u32<kDppMirror, 0xF>(__float_as_uint(m), __float_as_uint(m))));
     return m;
+}
+
+// value of lane l ^ 16 and of lane l ^ 32 (gfx950 permlane swaps: no LDS round trip)
+__device__ __forceinline__ float max_xor16(float m) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float m) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// sum over lanes l and l ^ 1 (and l ^ 2 for NT = 4): the NT adjacent columns of one token
+template <int NT>
+__device__ __forceinline__ float sum_adjacent(float v) {
+    v += __uint_as_float(dpp_u32<kDppXor1, 0xF>(0u, __float_as_uint(v)));
+    if constexpr (NT == 4) v += __uint_as_float(dpp_u32<kDppXor2, 0xF>(0u, __float_as_uint(v)));
+    return v;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -151,31 +172,26 @@ __device__ __forceinline__ void store_act<float>(float* p, size_t i, float v) { 
 template <>
 __device__ __forceinline__ void store_act<uint16_t>(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16_bits(v); }
 
-// E4M3FN code (sign | exponent<<3 | mantissa) of v, round to nearest even, saturating to
-// +-448.  v must be finite.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-    uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-    float a = fabsf(v);
-    uint32_t code;
-    if (a >= 0.015625f) {                       // normal range (>= 2^-6)
-        int e;
-        float m = frexpf(a, &e);                // a = m * 2^e, m in [0.5, 1)
-        float q = rintf((2.0f * m - 1.0f) * 8.0f);
-        int E = e - 1;
-        int mi = (int)q;
-        if (mi == 8) { mi = 0; E += 1; }
-        int biased = E + 7;
-        code = (biased > 15 || (biased == 15 && mi == 7)) ? 0x7Eu : (uint32_t)((biased << 3) | mi);
-    } else {
-        code = (uint32_t)rintf(a * 512.0f);     // subnormal step 2^-9; 8 -> 0x08 = 2^-6
-    }
-    return sign | code;
+// E4M3FN codes on the gfx950 conversion unit.  V_CVT_SCALEF32_PK_FP8_F32 writes the codes of
+// round-to-nearest-even(a / scale) and (b / scale) into the low (HI = false) or high 16 bits of
+// `old`; V_CVT_SCALEF32_PK_F32_FP8 returns code * scale for the two codes of the selected half.
+// For a power-of-two scale (a normal float) and |v| / scale <= 448 both are exact
+// (checked against a software encoder on gfx950).
+typedef short v2i16_t __attribute__((ext_vector_type(2)));
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_encode(uint32_t old, float a, float b, float scale) {
+    v2i16_t o;
+    o[0] = (short)(old & 0xffffu);
+    o[1] = (short)(old >> 16);
+    const v2i16_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, scale, HI);
+    return (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
 }
 
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-    uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    float mag = e ? ldexpf(1.0f + (float)m * 0.125f, (int)e - 7) : ldexpf((float)m * 0.125f, -6);
-    return (c & 0x80u) ? -mag : mag;
+template <bool HI>
+__device__ __forceinline__ v2f_t fp8x2_decode(uint32_t codes, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(codes, scale, HI);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -199,13 +215,14 @@ __device__ __forceinline__ int act_half_offset(int SS, int blk, int half) {
     return c * 128 * SS + q * 32 + 16 * (B >> 1);
 }
 
+// exponent S of a term: |v| / 2^S < 256 <= 448 for every v of the block (amax = max |v|),
+// clamped at -126 so that 2^S is a normal float (also for an all-zero block)
 __device__ __forceinline__ int split_exponent(float amax) {
-    if (!(amax > 0.0f)) return 0;
-    int e;
-    frexpf(amax, &e);
-    int S = e - 1 - 7;                      // |v| / 2^S < 256 <= 448
-    return S < -127 ? -127 : (S > 127 ? 127 : S);
+    const int be = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+    return be - 134 < -126 ? -126 : be - 134;
 }
+
+__device__ __forceinline__ float pow2f(int S) { return __uint_as_float((uint32_t)(S + 127) << 23); }
 
 // Split n values (registers) of one block into NT terms: code bytes packed 4 per word,
 // exponents S[t]; residuals are exact.  `amax_reduce` combines the per-lane max across the
@@ -213,19 +230,26 @@ __device__ __forceinline__ int split_exponent(float amax) {
 template <int NT, int N, typename Reduce>
 __device__ __forceinline__ void split_terms(float (&v)[N], uint32_t (&codes)[NT][N / 4], int (&S)[NT],
                                             Reduce amax_reduce) {
+    static_assert(N % 4 == 0, "values come in words of four codes");
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < N; ++i) amax = fmaxf(amax, fabsf(v[i]));
         S[t] = split_exponent(amax_reduce(amax));
+        const float sc = pow2f(S[t]);
 #pragma unroll
-        for (int i = 0; i < N / 4; ++i) codes[t][i] = 0;
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            uint32_t c = e4m3_encode(ldexpf(v[i], -S[t]));
-            v[i] -= ldexpf(e4m3_decode(c), S[t]);
-            codes[t][i >> 2] |= c << (8 * (i & 3));
+        for (int i = 0; i < N / 4; ++i) {
+            uint32_t w = fp8x2_encode<false>(0u, v[4 * i], v[4 * i + 1], sc);
+            w = fp8x2_encode<true>(w, v[4 * i + 2], v[4 * i + 3], sc);
+            codes[t][i] = w;
+            if (t + 1 < NT) {       // the last term's residual is not needed
+                const v2f_t lo = fp8x2_decode<false>(w, sc), hi = fp8x2_decode<true>(w, sc);
+                v[4 * i] -= lo[0];
+                v[4 * i + 1] -= lo[1];
+                v[4 * i + 2] -= hi[0];
+                v[4 * i + 3] -= hi[1];
+            }
         }
     }
 }
@@ -249,11 +273,11 @@ __device__ __forceinline__ void split_rows_lanewise(const XT* __restrict__ x, in
         float v = ok ? load_act(x, (size_t)row * d + blk * 32 + i) : 0.0f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            float m = row16_max(fabsf(v));
-            m = fmaxf(m, __shfl_xor(m, 16));
+            const float m = max_xor16(row16_max(fabsf(v)));
             const int S = split_exponent(m);
-            const uint32_t c = e4m3_encode(ldexpf(v, -S));
-            v -= ldexpf(e4m3_decode(c), S);
+            const float scale = pow2f(S);
+            const uint32_t c = fp8x2_encode<false>(0u, v, 0.0f, scale) & 0xffu;
+            if (t + 1 < NT) v -= fp8x2_decode<false>(c, scale)[0];
             uint32_t word = c << (8 * (i & 3));
             word |= dpp_u32<kDppXor1, 0xF>(word, word);
             word |= dpp_u32<kDppXor2, 0xF>(word, word);
@@ -274,8 +298,20 @@ __device__ __forceinline__ void split_rows_lanewise(const XT* __restrict__ x, in
 // tracing hook (set through moe_set_trace_hook); every launcher brackets its launch with these
 void trace(const char* kernel, int phase, hipStream_t st);
 
+// One grouped-GEMM tile of the few-token path, written by the fused router: the expert's
+// table entry, the tile's first sorted position and pick count (0 = no tile), and the token
+// row of each of its picks, so that a GEMM workgroup's set-up is a single 128-byte read.
+constexpr int kDescTokens = 8;            // tokens per few-token tile at most (16 / terms)
+struct TileDesc {
+    moe_expert ex;
+    int32_t i0, ntok, e, pad0;
+    int32_t tok[kDescTokens];
+    int32_t pad1[4];
+};
+static_assert(sizeof(TileDesc) == 128, "tile record is 128 bytes");
+
 struct WsLayout {
-    size_t counter, logits, idx, w, offsets, sorted_pick, pick_pos, tiles, ntiles, xq, xs, hq, hs, o, total;
+    size_t counter, logits, idx, w, offsets, sorted_pick, pick_pos, tiles, ntiles, desc, xq, xs, hq, hs, o, total;
     int nt;        // activation terms
     int max_tiles;
 };
@@ -310,6 +346,9 @@ struct RouteSmallArgs {
     int32_t* pick_pos;
     int32_t* tiles;
     int32_t* ntiles;
+    TileDesc* desc;           // [max_tiles]; entries past the last tile get ntok = 0
+    const moe_expert* table;
+    int max_tiles;
     int tt;                   // tokens per GEMM tile
     uint8_t* xq;
     uint8_t* xs;
@@ -324,6 +363,8 @@ struct GemmArgs {
     const int32_t* tiles;     // [max_tiles][2] = (expert, first sorted position)
     const int32_t* ntiles;
     const int32_t* offsets;
+    const TileDesc* desc;     // few-token kernels: [max_tiles] tile records
+    int max_tiles;
     const uint8_t* aq;        // activation terms (x terms by token / h terms by sorted position)
     const uint8_t* as;
     uint8_t* hq;              // gate/up output: h terms

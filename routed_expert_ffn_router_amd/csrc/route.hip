@@ -138,34 +138,68 @@ __device__ __forceinline__ double key_to_logit(unsigned long long key) {
     return __longlong_as_double((long long)b);
 }
 
-// Top-k of one token's E logits by one wave (E <= 64 * S), written in rank order to idx[0..k):
-// rank order is (logit descending, expert index ascending), a NaN ranks after every number.
-// w[j] = sigmoid(l_j) / sum_j' sigmoid(l_j'), the sum taken in rank order.  Each lane keeps its
-// S logits as order-preserving keys; a round takes every lane's best remaining key (first
-// maximum in slot order = lowest index) and a DPP arg-max across the wave.  All 64 lanes must
-// call it; lane j%64 stores entries j.
+// Top-k of one token's E logits by one wave (E <= 64 * S, k <= E), written in rank order to
+// idx[0..k): rank order is (logit descending, expert index ascending), a NaN ranks after every
+// number.  w[j] = sigmoid(l_j) / sum_j' sigmoid(l_j'), the sum taken in rank order.  Each lane
+// keeps its S logits as order-preserving keys, sorted; a round takes the best of the lanes'
+// heads by a DPP arg-max across the wave.  All 64 lanes must call it; lane j%64 stores entry j.
 template <int S>
-__device__ void wave_topk(const double* __restrict__ l, int E, int k, int32_t* idx, float* w) {
+__device__ __forceinline__ void topk_load(const double* __restrict__ l, int E, double (&lv)[S]) {
     const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {          // all loads together, none behind a branch
+        const int e = lane + 64 * s;
+        lv[s] = l[e < E ? e : E - 1];
+    }
+}
+
+// rank order of (key, index) pairs: larger key first, then lower index
+__device__ __forceinline__ bool ranks_before(unsigned long long ka, int ia, unsigned long long kb, int ib) {
+    return (ka > kb) | ((ka == kb) & (ia < ib));
+}
+
+template <int S>
+__device__ void topk_select(const double (&lv)[S], const double* __restrict__ l, int E, int k, int32_t* idx,
+                            float* w) {
+    const int lane = threadIdx.x & 63;
+    // this lane's entries in rank order (odd-even transposition sort, S passes); slots past E
+    // hold key 0 and index INT_MAX, which rank after every expert (a NaN logit has key 0 too,
+    // but a real index), and k <= E keeps them from being taken
     unsigned long long key[S];
-    uint32_t avail = 0;
+    int ei[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int e = lane + 64 * s;
-        key[s] = (e < E) ? logit_key(l[e]) : 0ull;
-        if (e < E) avail |= 1u << s;
+        key[s] = (e < E) ? logit_key(lv[s]) : 0ull;
+        ei[s] = (e < E) ? e : 0x7fffffff;
     }
+#pragma unroll
+    for (int pass = 0; pass < S; ++pass) {
+#pragma unroll
+        for (int s = pass & 1; s + 1 < S; s += 2) {
+            const bool sw = ranks_before(key[s + 1], ei[s + 1], key[s], ei[s]);
+            const unsigned long long k0 = key[s], k1 = key[s + 1];
+            const int i0 = ei[s], i1 = ei[s + 1];
+            key[s] = sw ? k1 : k0;
+            key[s + 1] = sw ? k0 : k1;
+            ei[s] = sw ? i1 : i0;
+            ei[s + 1] = sw ? i0 : i1;
+        }
+    }
+    // k rounds: the wave's best head entry is taken, and its lane's list shifts up by one
     unsigned long long my_key = 0ull;
     for (int j = 0; j < k; ++j) {
-        unsigned long long bk = 0ull;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const bool ok = (avail >> s) & 1u;
-            if (ok && (be == 0x7fffffff || key[s] > bk)) { bk = key[s]; be = lane + 64 * s; }
-        }
+        unsigned long long bk = key[0];
+        int be = ei[0];
         wave_argmax(bk, be);
-        if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
+        const bool win = (be & 63) == lane;
+#pragma unroll
+        for (int s = 0; s + 1 < S; ++s) {
+            key[s] = win ? key[s + 1] : key[s];
+            ei[s] = win ? ei[s + 1] : ei[s];
+        }
+        key[S - 1] = win ? 0ull : key[S - 1];
+        ei[S - 1] = win ? 0x7fffffff : ei[S - 1];
         if ((j & 63) == lane) {
             idx[j] = be;
             if (j < 64) my_key = bk;
@@ -178,6 +212,13 @@ __device__ void wave_topk(const double* __restrict__ l, int E, int k, int32_t* i
     for (int j = 64; j < k; ++j) ssum += 1.0 / (1.0 + exp(-l[idx[j]]));   // k > 64 only
     if (lane < k) w[lane] = (float)(sg / ssum);
     for (int j = lane + 64; j < k; j += 64) w[j] = (float)((1.0 / (1.0 + exp(-l[idx[j]]))) / ssum);
+}
+
+template <int S>
+__device__ void wave_topk(const double* __restrict__ l, int E, int k, int32_t* idx, float* w) {
+    double lv[S];
+    topk_load<S>(l, E, lv);
+    topk_select<S>(lv, l, E, k, idx, w);
 }
 
 template <int S>
@@ -202,64 +243,43 @@ hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t*
 
 // ---------------------------------------------------------------------------------------------
 // fused router for few tokens (T <= 16), one launch per layer: every workgroup computes the fp64
-// logits of 4 experts (one wave each) and splits part of x into fp8 terms; the last workgroup to
-// finish (device-scope counter) does the top-k, the permute, and the grouped-GEMM tile plan,
-// then resets the counter to zero for the next launch.
+// logits of 4 experts (one wave each); the last workgroup to finish (device-scope counter) does
+// the top-k, the grouping and the tile records, then resets the counter to zero for the next
+// launch, while the others split x into fp8 terms.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallT = 16;
-constexpr int kRouteRowChunks = 32;   // float4 per lane: router rows of up to 8192
 
-// exclusive scan over 256 threads; returns this thread's prefix, *total = sum (LDS scratch[4])
-__device__ int block_scan_256(int v, int* scratch, int* total) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) scratch[wv] = incl;
-    __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        if (w < wv) base += scratch[w];
-        tot += scratch[w];
-    }
-    __syncthreads();
-    *total = tot;
-    return base + incl - v;
-}
-
-template <typename XT, int NT, int S>
+// NC = float4 chunks per lane of a router row (d <= 256 * NC).  Every load is issued without a
+// condition (chunks past the row re-read its last chunk and are not used), so that no branch
+// separates them and all of a wave's loads are in flight together.
+template <typename XT, int NT, int S, int NC>
 __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     const XT* __restrict__ x = (const XT*)a.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
     const int T = a.T, d = a.d, E = a.E, k = a.k;
-    // 1. issue the loads of this wave's whole router row (d <= 8192: up to 32 float4 per lane)
+    // 1. issue the loads of this wave's whole router row
     const int e = blockIdx.x * 4 + wave;
     const int nw = d / 256;
-    float4 w4[kRouteRowChunks];
+    float4 w4[NC];
     const float* row = a.wr + (size_t)(e < E ? e : 0) * d;
 #pragma unroll
-    for (int u = 0; u < kRouteRowChunks; ++u)
-        w4[u] = (u < nw) ? *(const float4*)(row + u * 256 + lane * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    // 2. while they are in flight, split x into fp8 terms for the gate/up GEMM
-    split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, blockIdx.x, gridDim.x);
-    // 3. logits, fp64 accumulation of exact products
+    for (int u = 0; u < NC; ++u) w4[u] = *(const float4*)(row + (u < nw ? u : nw - 1) * 256 + lane * 4);
+    // 2. logits, fp64 accumulation of exact products
     if (e < E) {
 #pragma unroll 1
         for (int t = 0; t < T; ++t) {
             const XT* xt = x + (size_t)t * d;
+            float4 x4[NC];
+#pragma unroll
+            for (int u = 0; u < NC; ++u) x4[u] = load_act4(xt, (u < nw ? u : nw - 1) * 256 + lane * 4);
             double acc = 0.0;
 #pragma unroll
-            for (int u = 0; u < kRouteRowChunks; ++u) {
+            for (int u = 0; u < NC; ++u) {
                 if (u < nw) {
-                    const float4 x4 = load_act4(xt, u * 256 + lane * 4);
-                    acc = fma((double)x4.x, (double)w4[u].x, acc);
-                    acc = fma((double)x4.y, (double)w4[u].y, acc);
-                    acc = fma((double)x4.z, (double)w4[u].z, acc);
-                    acc = fma((double)x4.w, (double)w4[u].w, acc);
+                    acc = fma((double)x4[u].x, (double)w4[u].x, acc);
+                    acc = fma((double)x4[u].y, (double)w4[u].y, acc);
+                    acc = fma((double)x4[u].z, (double)w4[u].z, acc);
+                    acc = fma((double)x4[u].w, (double)w4[u].w, acc);
                 }
             }
             acc = wave_sum_f64(acc);
@@ -267,79 +287,140 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         }
     }
 
-    // the last workgroup to arrive finishes the routing
-    __shared__ int s_last;
-    __threadfence();
+    // the last workgroup to arrive finishes the routing: every thread makes its stores visible
+    // device-wide (release), one atomic per workgroup counts arrivals, and only the last one
+    // acquires, so the other workgroups leave without invalidating their cache
+    // acquires, so the other workgroups leave without invalidating their cache.  Those others, in
+    // arrival order, then split x into fp8 terms for the gate/up GEMM while the last one routes.
+    __shared__ int s_ticket;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(a.counter, 1u) == gridDim.x - 1);
+    if (tid == 0) s_ticket = (int)__hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+    const int G = (int)gridDim.x, ticket = s_ticket;
+    if (ticket != G - 1) {
+        split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, ticket, G - 1);
+        return;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (G == 1) split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, 0, 1);
 
-    __shared__ int32_t s_idx[kSmallT * 64];
-    __shared__ float s_w[kSmallT * 64];
-    __shared__ int s_cnt[1024];
-    __shared__ int s_off[1024];
-    __shared__ int scratch[4];
-    const int P = T * k;
-    for (int i = tid; i < E; i += 256) s_cnt[i] = 0;
-    for (int t = wave; t < T; t += 4) wave_topk<S>(a.logits + (size_t)t * E, E, k, s_idx + t * k, s_w + t * k);
-    __syncthreads();
-    for (int p = tid; p < P; p += 256) {
-        a.idx[p] = s_idx[p];
-        a.w[p] = s_w[p];
-        atomicAdd(&s_cnt[s_idx[p]], 1);
-    }
-    __syncthreads();
-    // offsets: exclusive scan of the counts, 4 experts per thread
-    int c4[4], sum4 = 0;
+    __shared__ int32_t s_idx[kMaxFusedPicks];
+    __shared__ float s_w[kMaxFusedPicks];
+    __shared__ int32_t s_sorted[kMaxFusedPicks];    // sorted position -> pick
+    __shared__ uint8_t s_start[kMaxFusedPicks];     // sorted position starts a tile
+    const int P = T * k, tt = a.tt;
+    // the routed tokens' logits (up to four per wave) and, for E <= kTabLds, the whole expert
+    // table are requested in one round; the table goes to LDS while the top-k runs
+    constexpr int kTabLds = 320, kTabRounds = (kTabLds * 4 + 255) / 256;
+    constexpr bool tab_lds = S <= 5;
+    __shared__ uint4 s_tab[tab_lds ? kTabLds * 4 : 1];
+    uint4 tab[tab_lds ? kTabRounds : 1];
+    if constexpr (tab_lds) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int ee = tid * 4 + u;
-        c4[u] = ee < E ? s_cnt[ee] : 0;
-        sum4 += c4[u];
-    }
-    int total;
-    int run = block_scan_256(sum4, scratch, &total);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int ee = tid * 4 + u;
-        if (ee < E) {
-            s_off[ee] = run;
-            a.offsets[ee] = run;
+        for (int r = 0; r < kTabRounds; ++r) {
+            const int g = r * 256 + tid;
+            tab[r] = ((const uint4*)a.table)[g < 4 * E ? g : 4 * E - 1];
         }
-        run += c4[u];
     }
-    if (tid == 0) a.offsets[E] = total;
-    __syncthreads();
-    // stable positions: rank of pick p among the earlier picks of its expert
-    for (int p = tid; p < P; p += 256) {
-        const int ep = s_idx[p];
-        int r = 0;
-        for (int q = 0; q < p; ++q) r += (s_idx[q] == ep);
-        const int pos = s_off[ep] + r;
-        a.sorted_pick[pos] = p;
-        a.pick_pos[p] = pos;
-    }
-    // tile plan: ceil(count / tt) tiles per expert
-    int n4[4], nsum = 0;
+    constexpr int J = tab_lds ? kSmallT / 4 : 1;     // tokens whose logits are preloaded per wave
+    double lv[J][S];
+    if (wave < T) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        n4[u] = (c4[u] + a.tt - 1) / a.tt;
-        nsum += n4[u];
-    }
-    int first = block_scan_256(nsum, scratch, &total);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int ee = tid * 4 + u;
-        for (int j = 0; j < n4[u]; ++j) {
-            a.tiles[2 * (first + j)] = ee;
-            a.tiles[2 * (first + j) + 1] = s_off[ee] + j * a.tt;
+        for (int j = 0; j < J; ++j) {
+            const int t = wave + 4 * j;
+            topk_load<S>(a.logits + (size_t)(t < T ? t : T - 1) * E, E, lv[j]);
         }
-        first += n4[u];
+    }
+    if constexpr (tab_lds) {
+#pragma unroll
+        for (int r = 0; r < kTabRounds; ++r) asm volatile("" ::"v"(tab[r].x), "v"(tab[r].y), "v"(tab[r].z), "v"(tab[r].w));
+#pragma unroll
+        for (int r = 0; r < kTabRounds; ++r) {
+            const int g = r * 256 + tid;
+            if (g < 4 * E) s_tab[g] = tab[r];
+        }
+    }
+    if (wave < T) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int t = wave + 4 * j;
+            if (t < T) topk_select<S>(lv[j], a.logits + (size_t)t * E, E, k, s_idx + t * k, s_w + t * k);
+        }
+        for (int t = wave + 4 * J; t < T; t += 4)
+            wave_topk<S>(a.logits + (size_t)t * E, E, k, s_idx + t * k, s_w + t * k);
+    }
+    __syncthreads();
+    // Grouping without atomics or scans (P <= 512, two picks per thread): a pick's sorted
+    // position is the number of picks of lower experts plus its rank among the picks of its own
+    // expert; it starts a tile when that rank is a multiple of tt.
+    moe_expert ex[2];
+    int pos[2], rank[2], cnt[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int p = tid + 256 * u;
+        pos[u] = -1;
+        if (p < P) {
+            const int e = s_idx[p];
+            if constexpr (tab_lds) ex[u] = *(const moe_expert*)&s_tab[4 * e];
+            else ex[u] = a.table[e];
+            int lower = 0, before = 0, same = 0;
+            for (int q = 0; q < P; ++q) {
+                const int eq = s_idx[q];
+                lower += eq < e;
+                same += eq == e;
+                before += (eq == e) & (q < p);
+            }
+            pos[u] = lower + before;
+            rank[u] = before;
+            cnt[u] = same;
+            s_sorted[pos[u]] = p;
+            s_start[pos[u]] = (before % tt) == 0;
+            a.idx[p] = e;
+            a.w[p] = s_w[p];
+            a.pick_pos[p] = pos[u];
+            a.sorted_pick[pos[u]] = p;
+        }
+    }
+    for (int e = tid; e <= E; e += 256) {
+        int lower = 0;
+        for (int q = 0; q < P; ++q) lower += s_idx[q] < e;
+        a.offsets[e] = lower;
+    }
+    __syncthreads();
+    // tiles: numbered by sorted position of their first pick
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (pos[u] >= 0 && s_start[pos[u]]) {
+            int id = 0;
+            for (int q = 0; q < pos[u]; ++q) id += s_start[q];
+            const int ntok = min(tt, cnt[u] - rank[u]);
+            TileDesc* D = a.desc + id;
+            D->ex = ex[u];
+            D->i0 = pos[u];
+            D->ntok = ntok;
+            D->e = s_idx[s_sorted[pos[u]]];
+            D->pad0 = 0;
+            for (int c = 0; c < kDescTokens; ++c) D->tok[c] = c < ntok ? s_sorted[pos[u] + c] / k : 0;
+            a.tiles[2 * id] = D->e;
+            a.tiles[2 * id + 1] = pos[u];
+        }
+    }
+    // the tile count, and empty records up to max_tiles
+    int nt = 0;
+    for (int q = 0; q < P; ++q) nt += s_start[q];
+    for (int id = nt + tid; id < a.max_tiles; id += 256) {
+        // an empty record still names a real expert (the first pick's), so that a stray read of
+        // its pointers stays inside the weights
+        TileDesc* D = a.desc + id;
+        if constexpr (tab_lds) D->ex = *(const moe_expert*)&s_tab[4 * s_idx[0]];
+        else D->ex = a.table[s_idx[0]];
+        D->i0 = 0;
+        D->ntok = 0;
+        D->e = s_idx[0];
     }
     if (tid == 0) {
-        *a.ntiles = total;
+        *a.ntiles = nt;
         *a.counter = 0u;
     }
 }
@@ -348,16 +429,19 @@ hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipSt
     trace("route_small", 0, st);
     dim3 grid((s->n_experts + 3) / 4);
     const bool bf = s->act_dtype == MOE_DT_BF16;
-    const int NT = act_terms(s);
-#define MOE_RS(XT, N)                                                                                \
+#define MOE_RS(XT, N, NC)                                                                            \
     do {                                                                                             \
-        if (s->n_experts <= 320) hipLaunchKernelGGL((k_route_small<XT, N, 5>), grid, dim3(256), 0, st, a); \
-        else hipLaunchKernelGGL((k_route_small<XT, N, 16>), grid, dim3(256), 0, st, a);              \
+        if (s->n_experts <= 320) hipLaunchKernelGGL((k_route_small<XT, N, 5, NC>), grid, dim3(256), 0, st, a); \
+        else hipLaunchKernelGGL((k_route_small<XT, N, 16, NC>), grid, dim3(256), 0, st, a);              \
     } while (0)
-    if (bf && NT == 2) MOE_RS(uint16_t, 2);
-    else if (bf) MOE_RS(uint16_t, 4);
-    else if (NT == 2) MOE_RS(float, 2);
-    else MOE_RS(float, 4);
+    // activation terms: 2 for bf16 activations, 4 for fp32 (act_terms)
+    if (bf) {
+        if (s->d_model <= 4096) MOE_RS(uint16_t, 2, 16);
+        else MOE_RS(uint16_t, 2, 32);
+    } else {
+        if (s->d_model <= 4096) MOE_RS(float, 4, 16);
+        else MOE_RS(float, 4, 32);
+    }
 #undef MOE_RS
     trace("route_small", 1, st);
     return hipGetLastError();

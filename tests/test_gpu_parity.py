@@ -195,7 +195,10 @@ def glm_layer():
     return DeviceLayer(m, wl, layer=0, host_gen=False)
 
 
-@pytest.mark.parametrize("T", [1, 64])
+# T=1 and 2: few-token kernels with the h terms staged in LDS; 5 and 16: the same gate/up kernel
+# with the down kernel reading h from memory (and tiles of several picks of one expert); 64: the
+# general grouped path
+@pytest.mark.parametrize("T", [1, 2, 5, 16, 64])
 def test_glm_decode_layer(glm_layer, T):
     dl = glm_layer
     wl = dl.wl
