@@ -87,71 +87,32 @@ class Hip:
         self._ok(self.lib.hipStreamSynchronize(stream), "hipStreamSynchronize")
 
 
-class KernelTimer:
-    """Trace hook that records a HIP event pair around every kernel the library enqueues."""
+def kernel_times(hip, m, stream, step, reps=3):
+    """Per-kernel durations (us) of step(): the library launches each kernel with a pair of HIP
+    events that the kernel's own dispatch records at its start and end (hipExtLaunchKernel), on
+    the stream it runs on, so a duration holds no launch gap (the same timestamps a profiler
+    reads).  The step runs eagerly, reps times."""
+    pairs = []
+    pool = []
 
-    def __init__(self, hip, names=None):
-        self.hip = hip
-        self.names = names
-        self.pairs = []          # (kernel, ev_begin, ev_end)
-        self.pool = []
-        self._open = {}
+    def hook(kernel):
+        a = pool.pop() if pool else hip.event()
+        b = pool.pop() if pool else hip.event()
+        pairs.append((kernel, a, b))
+        return a, b
 
-    def _ev(self):
-        if self.pool:
-            return self.pool.pop()
-        return self.hip.event()
-
-    def __call__(self, kernel, phase, stream):
-        if self.names is not None and kernel not in self.names:
-            return
-        if phase == 0:
-            ev = self._ev()
-            self.hip.record(ev, stream)
-            self._open[kernel] = ev
-        else:
-            ev = self._ev()
-            self.hip.record(ev, stream)
-            self.pairs.append((kernel, self._open.pop(kernel), ev))
-
-    def durations_us(self):
-        """Durations of the recorded pairs; recycles their events."""
-        out = {}
-        for k, a, b in self.pairs:
-            out.setdefault(k, []).append(1000.0 * self.hip.elapsed_ms(a, b))
-            self.pool += [a, b]
-        self.pairs = []
-        return out
-
-
-def timed_kernels(hip, m, torch, stream, step, reps=3, log=print):
-    """Per-kernel durations (us) of step(), each kernel bracketed by HIP events on its stream.
-
-    The step is enqueued eagerly behind a GPU sleep that outlasts the host-side enqueue, so the
-    kernels then run back to back and no host latency falls between an event pair."""
-    timer = KernelTimer(hip)
     per = {}
-    cycles = 200_000_000
-    m.moe_set_trace_hook(timer)
+    m.moe_set_event_hook(hook)
     try:
         for _ in range(reps):
-            s0, s1 = hip.event(), hip.event()
-            hip.record(s0, stream.cuda_stream)
-            with torch.cuda.stream(stream):
-                torch.cuda._sleep(cycles)
-            hip.record(s1, stream.cuda_stream)
-            t0 = time.perf_counter()
             step()
-            host_ms = 1000.0 * (time.perf_counter() - t0)
-            hip.sync(stream.cuda_stream)
-            sleep_ms = hip.elapsed_ms(s0, s1)
-            if host_ms > sleep_ms:
-                log(f"# warning: host enqueue {host_ms:.1f} ms outlasted the {sleep_ms:.1f} ms GPU sleep")
-                cycles *= 2
-            for k, v in timer.durations_us().items():
-                per.setdefault(k, []).extend(v)
+            hip.sync(stream)
+            for k, a, b in pairs:
+                per.setdefault(k, []).append(1000.0 * hip.elapsed_ms(a, b))
+                pool += [a, b]
+            pairs.clear()
     finally:
-        m.moe_set_trace_hook(None)
+        m.moe_set_event_hook(None)
     return per
 
 
@@ -185,6 +146,22 @@ class Stack:
         torch.cuda.synchronize()
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary (profiles/), or None when
+    the kernel sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "routed_expert_ffn_router_amd", "csrc", rec["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
 def algorithmic_layer_bytes(wl, experts_touched, T):
     """Bytes a layer must move at least: touched experts' blobs, the router, x and y."""
     B = 32 if wl.wformat == 0 else 16
@@ -210,6 +187,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--only", choices=["decode", "prefill", "batched"], default=None)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -226,6 +205,16 @@ def main():
         print(*a, file=sys.stderr, flush=True)
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        # a plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for it scales the counters
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+        return
     hip = Hip()
     stream = torch.cuda.Stream()
     S = stream.cuda_stream
@@ -284,8 +273,8 @@ def main():
             hip.record(e1, S)
             ms = hip.elapsed_ms(e0, e1) / args.steps
             torch.cuda.synchronize()
-            # per-kernel durations, HIP events around every kernel of an eager step
-            per = timed_kernels(hip, m, torch, stream, run_stack(T, biases, x0, bufs, ws), log=log)
+            # per-kernel durations: events recorded by each kernel's own dispatch, same step
+            per = kernel_times(hip, m, S, run_stack(T, biases, x0, bufs, ws))
             kern = {k: float(np.mean(v)) for k, v in per.items()}
             touched = [len(np.unique(idx_keep[l].cpu().numpy())) for l in range(nl)]
             layer_bytes = float(np.mean([algorithmic_layer_bytes(wl, u, T) for u in touched]))
@@ -329,7 +318,7 @@ def main():
             call()
         hip.record(e1, S)
         ms = hip.elapsed_ms(e0, e1) / steps
-        per = timed_kernels(hip, m, torch, stream, call, log=log)
+        per = kernel_times(hip, m, S, call)
         kern = {k: float(np.mean(v)) for k, v in per.items()}
         flops = 2.0 * 3 * wl.d_model * wl.d_ff * T * wl.top_k
         touched = len(np.unique(idx.cpu().numpy()))
@@ -409,9 +398,10 @@ def main():
                        "layers": nl, "tokens_per_step": 1, "parallelism": "single GPU"},
             "stack_tokens_per_s": dec["stack_tokens_per_s"], "us_per_layer": dec["us_per_layer"],
             "hbm_frac_layer": dec["hbm_frac_layer"],
-            "roofline": {"bound": "hbm", "kernel": "gemm_gate_up (k_mx_gemm gate/up, 8 experts x 8.9 MB)",
+            "roofline": {"bound": "hbm", "kernel": "gemm_gate_up (k_mx_gateup_dec: gate and up of 8 experts, "
+                                                  "8.9 MB each)",
                          "achieved": dec["gate_up_roofline"]["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dec["gate_up_roofline"]["frac"], "traffic": None,
+                         "frac": dec["gate_up_roofline"]["frac"], "traffic": measured_traffic("k_mx_gateup_dec"),
                          "bytes_per_launch": dec["gate_up_roofline"]["bytes_per_launch"],
                          "avg_launch_us": dec["kernels_us"]["gemm_gate_up"]},
             "kernels_us": dec["kernels_us"],

@@ -179,6 +179,16 @@ moe_status moe_combine(const moe_shape *shape, const float *o, const float *topk
 typedef void (*moe_trace_hook)(void *user, const char *kernel, int phase, hipStream_t stream);
 void moe_set_trace_hook(moe_trace_hook hook, void *user);
 
+/* Kernel timing hook.  When set, every entry point calls hook(user, kernel, &start, &stop) right
+ * before it enqueues each kernel (same names as the tracing hook), with start = stop = NULL.
+ * If the hook sets both to HIP events it created, the kernel is enqueued with
+ * hipExtLaunchKernel, which records them when the kernel itself starts and ends (the dispatch
+ * timestamps a profiler reads), so hipEventElapsedTime(start, stop) is the kernel's duration
+ * without any launch gap.  Leave them NULL to launch normally.  Do not set events while the
+ * stream is being captured.  Process-wide, like the tracing hook. */
+typedef void (*moe_event_hook)(void *user, const char *kernel, hipEvent_t *start, hipEvent_t *stop);
+void moe_set_event_hook(moe_event_hook hook, void *user);
+
 /* The whole layer: moe_route, moe_permute, moe_expert_ffn and moe_combine on the stream,
  * with the intermediates in the workspace (zero-filled before its first use).  For T <= 16
  * (and T * top_k <= 512, top_k <= 64) the layer runs as three launches: the router fused with

@@ -67,6 +67,7 @@ _SIGS = {
     "moe_combine": (ctypes.c_int, [_SP, _P, _P, _P, _i32, _P, _P, _P]),
     "moe_layer": (ctypes.c_int, [_SP, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
     "moe_set_trace_hook": (None, [_P, _P]),
+    "moe_set_event_hook": (None, [_P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -89,6 +90,29 @@ def moe_set_trace_hook(hook):
         return
     _hook_ref = TRACE_HOOK(lambda user, name, phase, stream: hook(name.decode(), phase, stream or 0))
     _lib.moe_set_trace_hook(ctypes.cast(_hook_ref, ctypes.c_void_p), None)
+
+
+EVENT_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p),
+                              ctypes.POINTER(ctypes.c_void_p))
+_ev_hook_ref = None
+
+
+def moe_set_event_hook(hook):
+    """Install hook(kernel: str) -> (start_event, stop_event) or None (raw hipEvent_t handles as
+    ints), or None to clear.  A returned pair is recorded at the kernel's own start and end."""
+    global _ev_hook_ref
+    if hook is None:
+        _ev_hook_ref = None
+        _lib.moe_set_event_hook(None, None)
+        return
+
+    def _cb(user, name, start, stop):
+        pair = hook(name.decode())
+        if pair is not None:
+            start[0], stop[0] = pair
+
+    _ev_hook_ref = EVENT_HOOK(_cb)
+    _lib.moe_set_event_hook(ctypes.cast(_ev_hook_ref, ctypes.c_void_p), None)
 
 
 def header_functions() -> list:

@@ -12,9 +12,20 @@ constexpr int kSmallTokens = 16;   // moe_layer's fused three-launch path
 static moe_trace_hook g_hook = nullptr;
 static void* g_hook_user = nullptr;
 
+static moe_event_hook g_ev_hook = nullptr;
+static void* g_ev_user = nullptr;
+static thread_local hipEvent_t t_launch_ev[2] = {nullptr, nullptr};
+
 void trace(const char* kernel, int phase, hipStream_t st) {
     if (g_hook) g_hook(g_hook_user, kernel, phase, st);
+    t_launch_ev[0] = t_launch_ev[1] = nullptr;
+    if (phase == 0 && g_ev_hook) {
+        g_ev_hook(g_ev_user, kernel, &t_launch_ev[0], &t_launch_ev[1]);
+        if (!t_launch_ev[0] || !t_launch_ev[1]) t_launch_ev[0] = t_launch_ev[1] = nullptr;
+    }
 }
+
+hipEvent_t launch_event(int which) { return t_launch_ev[which]; }
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
@@ -138,6 +149,11 @@ int moe_abi_version(void) { return MOE_ABI_VERSION; }
 void moe_set_trace_hook(moe_trace_hook hook, void* user) {
     g_hook = hook;
     g_hook_user = user;
+}
+
+void moe_set_event_hook(moe_event_hook hook, void* user) {
+    g_ev_hook = hook;
+    g_ev_user = user;
 }
 
 const char* moe_status_string(moe_status status) {

@@ -38,10 +38,10 @@ hipError_t launch_combine(const moe_shape* s, const float* o, const float* w, co
     const int d = s->d_model;
     dim3 grid((d / 4 + 255) / 256, T);
     if (s->act_dtype == MOE_DT_BF16)
-        hipLaunchKernelGGL(k_combine<uint16_t>, grid, dim3(256), 0, st, o, w, pick_pos, T, s->top_k, d,
+        MOE_LAUNCH(k_combine<uint16_t>, grid, dim3(256), 0, st, o, w, pick_pos, T, s->top_k, d,
                            s->routed_scaling, (const uint16_t*)residual, (uint16_t*)y);
     else
-        hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, st, o, w, pick_pos, T, s->top_k, d,
+        MOE_LAUNCH(k_combine<float>, grid, dim3(256), 0, st, o, w, pick_pos, T, s->top_k, d,
                            s->routed_scaling, (const float*)residual, (float*)y);
     trace("combine", 1, st);
     return hipGetLastError();
@@ -87,7 +87,7 @@ hipError_t launch_fill_table(const moe_shape* s, const uint8_t* base, size_t str
                              hipStream_t st) {
     trace("fill_table", 0, st);
     const BlobSizes z = blob_sizes(s);
-    hipLaunchKernelGGL(k_fill_table, dim3((s->n_experts + 255) / 256), dim3(256), 0, st, base, stride,
+    MOE_LAUNCH(k_fill_table, dim3((s->n_experts + 255) / 256), dim3(256), 0, st, base, stride,
                        s->n_experts, z.nq, z.ns, (int)(s->wformat == MOE_WF_NVFP4), table);
     trace("fill_table", 1, st);
     return hipGetLastError();
@@ -143,7 +143,7 @@ hipError_t launch_gather(const moe_shape* s, const moe_expert* table, const int3
     trace("gather", 0, st);
     const BlobSizes z = blob_sizes(s);
     dim3 grid(64, n);
-    hipLaunchKernelGGL(k_gather, grid, dim3(256), 0, st, table, list, n, z.nq, z.ns, stride, staging, staged);
+    MOE_LAUNCH(k_gather, grid, dim3(256), 0, st, table, list, n, z.nq, z.ns, stride, staging, staged);
     trace("gather", 1, st);
     return hipGetLastError();
 }

@@ -724,8 +724,8 @@ hipError_t launch_gateup_dec(const GemmArgs& a, int NT, int max_tiles, hipStream
     // two workgroups per CU, each taking (tile, row block) pairs in turn
     const long long pairs = (long long)max_tiles * (a.f / 32);
     dim3 grid((unsigned)(pairs < 2LL * device_cus() ? pairs : 2LL * device_cus()));
-    if (NT == 2) hipLaunchKernelGGL(k_mx_gateup_dec<2>, grid, dim3(512), 0, st, a, ss2, (int)grid.x);
-    else hipLaunchKernelGGL(k_mx_gateup_dec<4>, grid, dim3(512), 0, st, a, ss2, (int)grid.x);
+    if (NT == 2) MOE_LAUNCH(k_mx_gateup_dec<2>, grid, dim3(512), 0, st, a, ss2, (int)grid.x);
+    else MOE_LAUNCH(k_mx_gateup_dec<4>, grid, dim3(512), 0, st, a, ss2, (int)grid.x);
     trace("gemm_gate_up", 1, st);
     return hipGetLastError();
 }
@@ -736,21 +736,21 @@ hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineA
     const bool bf = s->act_dtype == MOE_DT_BF16;
     if (a.P * NT <= kDownLdsCols && a.f <= kDownMaxF && a.max_tiles <= kDownMaxTiles) {
         if (bf) {
-            if (NT == 2) hipLaunchKernelGGL((k_mx_down_dec_lds<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
-            else hipLaunchKernelGGL((k_mx_down_dec_lds<uint16_t, 4>), grid, dim3(512), 0, st, a, c);
+            if (NT == 2) MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
+            else MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 4>), grid, dim3(512), 0, st, a, c);
         } else {
-            if (NT == 2) hipLaunchKernelGGL((k_mx_down_dec_lds<float, 2>), grid, dim3(512), 0, st, a, c);
-            else hipLaunchKernelGGL((k_mx_down_dec_lds<float, 4>), grid, dim3(512), 0, st, a, c);
+            if (NT == 2) MOE_LAUNCH((k_mx_down_dec_lds<float, 2>), grid, dim3(512), 0, st, a, c);
+            else MOE_LAUNCH((k_mx_down_dec_lds<float, 4>), grid, dim3(512), 0, st, a, c);
         }
         trace("down_combine", 1, st);
         return hipGetLastError();
     }
     if (bf) {
-        if (NT == 2) hipLaunchKernelGGL((k_mx_down_dec<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
-        else hipLaunchKernelGGL((k_mx_down_dec<uint16_t, 4>), grid, dim3(512), 0, st, a, c);
+        if (NT == 2) MOE_LAUNCH((k_mx_down_dec<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
+        else MOE_LAUNCH((k_mx_down_dec<uint16_t, 4>), grid, dim3(512), 0, st, a, c);
     } else {
-        if (NT == 2) hipLaunchKernelGGL((k_mx_down_dec<float, 2>), grid, dim3(512), 0, st, a, c);
-        else hipLaunchKernelGGL((k_mx_down_dec<float, 4>), grid, dim3(512), 0, st, a, c);
+        if (NT == 2) MOE_LAUNCH((k_mx_down_dec<float, 2>), grid, dim3(512), 0, st, a, c);
+        else MOE_LAUNCH((k_mx_down_dec<float, 4>), grid, dim3(512), 0, st, a, c);
     }
     trace("down_combine", 1, st);
     return hipGetLastError();
@@ -774,9 +774,9 @@ int ksplit_for(int K, int variant) { return (variant == 0 && (K / 4) % 128 == 0)
 
 template <bool GATEUP, int NT, int NTN, int KS>
 static hipError_t launch_one(const GemmArgs& a, int SS, int ss2, dim3 grid, hipStream_t st) {
-    if (SS == 4) hipLaunchKernelGGL((k_mx_gemm<NT, NTN, KS, 4, GATEUP>), grid, dim3(256), 0, st, a, ss2);
-    else if (SS == 2) hipLaunchKernelGGL((k_mx_gemm<NT, NTN, KS, 2, GATEUP>), grid, dim3(256), 0, st, a, ss2);
-    else hipLaunchKernelGGL((k_mx_gemm<NT, NTN, KS, 1, GATEUP>), grid, dim3(256), 0, st, a, ss2);
+    if (SS == 4) MOE_LAUNCH((k_mx_gemm<NT, NTN, KS, 4, GATEUP>), grid, dim3(256), 0, st, a, ss2);
+    else if (SS == 2) MOE_LAUNCH((k_mx_gemm<NT, NTN, KS, 2, GATEUP>), grid, dim3(256), 0, st, a, ss2);
+    else MOE_LAUNCH((k_mx_gemm<NT, NTN, KS, 1, GATEUP>), grid, dim3(256), 0, st, a, ss2);
     return hipGetLastError();
 }
 
@@ -819,7 +819,7 @@ hipError_t launch_down_combine(const moe_shape* s, const GemmArgs& a, const Comb
     const int SS = super_step(a.f, ksplit_for(a.f, 0));
     dim3 grid(a.d / 16);
     const bool bf = s->act_dtype == MOE_DT_BF16;
-#define MOE_DC(XT, N, S) hipLaunchKernelGGL((k_mx_down_combine<XT, N, S>), grid, dim3(512), 0, st, a, c)
+#define MOE_DC(XT, N, S) MOE_LAUNCH((k_mx_down_combine<XT, N, S>), grid, dim3(512), 0, st, a, c)
 #define MOE_DC_SS(XT, N) \
     do { if (SS == 4) MOE_DC(XT, N, 4); else if (SS == 2) MOE_DC(XT, N, 2); else MOE_DC(XT, N, 1); } while (0)
     if (bf) {

@@ -1,6 +1,7 @@
 // Internal declarations of the routed-MoE HIP library (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -297,6 +298,13 @@ __device__ __forceinline__ void split_rows_lanewise(const XT* __restrict__ x, in
 
 // tracing hook (set through moe_set_trace_hook); every launcher brackets its launch with these
 void trace(const char* kernel, int phase, hipStream_t st);
+
+// timing events for the launch being enqueued (from the event hook, at trace phase 0; null when
+// there is none): every launch goes through MOE_LAUNCH, which hands them to hipExtLaunchKernel
+hipEvent_t launch_event(int which);
+#define MOE_LAUNCH(kernel, grid, block, shm, st, ...)                                                  \
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)(shm), st, ::moe::launch_event(0),            \
+                          ::moe::launch_event(1), 0, __VA_ARGS__)
 
 // One grouped-GEMM tile of the few-token path, written by the fused router: the expert's
 // table entry, the tile's first sorted position and pick count (0 = no tile), and the token

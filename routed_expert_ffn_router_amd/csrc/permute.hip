@@ -94,7 +94,7 @@ hipError_t launch_permute(const moe_shape* s, const int32_t* idx, int T, int32_t
                           int32_t* sorted_pick, int32_t* pick_pos, hipStream_t st) {
     trace("permute", 0, st);
     const int P = T * s->top_k;
-    hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), 0, st, idx, P, s->n_experts, offsets,
+    MOE_LAUNCH(k_permute, dim3(1), dim3(kPermThreads), 0, st, idx, P, s->n_experts, offsets,
                        sorted_pick, pick_pos);
     trace("permute", 1, st);
     return hipGetLastError();
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kPermThreads) void k_plan(const int32_t* __restrict
 hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int tile_tokens, int32_t* tiles,
                        int32_t* ntiles, hipStream_t st) {
     trace("plan", 0, st);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPermThreads), 0, st, offsets, s->n_experts, tile_tokens,
+    MOE_LAUNCH(k_plan, dim3(1), dim3(kPermThreads), 0, st, offsets, s->n_experts, tile_tokens,
                        tiles, ntiles);
     trace("plan", 1, st);
     return hipGetLastError();

@@ -95,18 +95,18 @@ hipError_t launch_router_logits(const moe_shape* s, const void* x, int T, const 
     if (T <= 8) {
         dim3 grid((E + 3) / 4);
         if (bf)
-            hipLaunchKernelGGL((k_logits_gemv<uint16_t>), grid, dim3(256), 0, st,
+            MOE_LAUNCH((k_logits_gemv<uint16_t>), grid, dim3(256), 0, st,
                                (const uint16_t*)x, T, d, wr, bias, E, logits);
         else
-            hipLaunchKernelGGL((k_logits_gemv<float>), grid, dim3(256), 0, st,
+            MOE_LAUNCH((k_logits_gemv<float>), grid, dim3(256), 0, st,
                                (const float*)x, T, d, wr, bias, E, logits);
     } else {
         dim3 grid((T + 63) / 64, (E + 63) / 64);
         if (bf)
-            hipLaunchKernelGGL((k_logits_tiled<uint16_t>), grid, dim3(256), 0, st,
+            MOE_LAUNCH((k_logits_tiled<uint16_t>), grid, dim3(256), 0, st,
                                (const uint16_t*)x, T, d, wr, bias, E, logits);
         else
-            hipLaunchKernelGGL((k_logits_tiled<float>), grid, dim3(256), 0, st,
+            MOE_LAUNCH((k_logits_tiled<float>), grid, dim3(256), 0, st,
                                (const float*)x, T, d, wr, bias, E, logits);
     }
     trace("router_logits", 1, st);
@@ -234,9 +234,9 @@ hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t*
     trace("topk", 0, st);
     dim3 grid((T + 3) / 4);
     if (s->n_experts <= 320)
-        hipLaunchKernelGGL(k_topk<5>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, idx, w);
+        MOE_LAUNCH(k_topk<5>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, idx, w);
     else
-        hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, idx, w);
+        MOE_LAUNCH(k_topk<16>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, idx, w);
     trace("topk", 1, st);
     return hipGetLastError();
 }
@@ -431,8 +431,8 @@ hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipSt
     const bool bf = s->act_dtype == MOE_DT_BF16;
 #define MOE_RS(XT, N, NC)                                                                            \
     do {                                                                                             \
-        if (s->n_experts <= 320) hipLaunchKernelGGL((k_route_small<XT, N, 5, NC>), grid, dim3(256), 0, st, a); \
-        else hipLaunchKernelGGL((k_route_small<XT, N, 16, NC>), grid, dim3(256), 0, st, a);              \
+        if (s->n_experts <= 320) MOE_LAUNCH((k_route_small<XT, N, 5, NC>), grid, dim3(256), 0, st, a); \
+        else MOE_LAUNCH((k_route_small<XT, N, 16, NC>), grid, dim3(256), 0, st, a);              \
     } while (0)
     // activation terms: 2 for bf16 activations, 4 for fp32 (act_terms)
     if (bf) {
@@ -463,7 +463,7 @@ hipError_t launch_act_split(const moe_shape* s, const void* x, int rows, int K, 
     dim3 grid((unsigned)((n + 7) / 8));
     const bool bf = s->act_dtype == MOE_DT_BF16;
 #define MOE_SPLIT(XT, N)                                                                    \
-    hipLaunchKernelGGL((k_act_split<XT, N>), grid, dim3(256), 0, st, (const XT*)x, rows, K, SS, q, sc)
+    MOE_LAUNCH((k_act_split<XT, N>), grid, dim3(256), 0, st, (const XT*)x, rows, K, SS, q, sc)
     if (bf && NT == 2) MOE_SPLIT(uint16_t, 2);
     else if (bf && NT == 4) MOE_SPLIT(uint16_t, 4);
     else if (!bf && NT == 2) MOE_SPLIT(float, 2);
