@@ -41,6 +41,8 @@ extern "C" {
 
 struct ihipStream_t;
 typedef struct ihipStream_t *hipStream_t;
+struct ihipEvent_t;
+typedef struct ihipEvent_t *hipEvent_t;
 
 #define MOE_ABI_VERSION 1
 
