@@ -157,7 +157,9 @@ moe_status moe_gather_experts(const moe_shape *shape, const moe_expert *d_table,
  *   o_i = W_down,e (silu(W_gate,e x_t) * (W_up,e x_t)),  silu(g) = g * sigmoid(g),
  * for each sorted position i with pick p = sorted_pick[i], token t = p / top_k, and e the
  * expert whose range [expert_offsets[e], expert_offsets[e+1]) holds i.
- * o: [T*top_k][d_model] fp32, row i = sorted position i. */
+ * o: [T*top_k][d_model] fp32, row i = sorted position i.  MXFP4 weights enter the scaled FP4
+ * matrix cores as they are; NVFP4 weights are dequantised in registers to bf16 (code x E4M3
+ * block scale is exact in bf16), the tensor scales applied to the fp32 sums. */
 moe_status moe_expert_ffn(const moe_shape *shape, const moe_expert *d_table, const void *x,
                           int32_t T, const int32_t *expert_offsets, const int32_t *sorted_pick,
                           float *o, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -192,12 +194,17 @@ typedef void (*moe_event_hook)(void *user, const char *kernel, hipEvent_t *start
 void moe_set_event_hook(moe_event_hook hook, void *user);
 
 /* The whole layer: moe_route, moe_permute, moe_expert_ffn and moe_combine on the stream,
- * with the intermediates in the workspace (zero-filled before its first use).  For T <= 16
- * (and T * top_k <= 512, top_k <= 64) the layer runs as three launches: the router fused with
- * the permute, the tile plan and the activation split; the gate/up GEMM; and the down GEMM
- * fused with the combine.  topk_idx_out / topk_w_out ([T][top_k], device)
- * are optional copies of the routing.  staging: unused for now (pass NULL).  y may not
- * alias x; it may alias residual. */
+ * with the intermediates in the workspace (zero-filled before its first use).  For MXFP4 with
+ * T <= 16 (and T * top_k <= 512, top_k <= 64) the layer runs as three launches: the router fused
+ * with the grouping, the tile records and the activation split; the gate/up GEMM; and the down
+ * GEMM fused with the combine.  topk_idx_out / topk_w_out ([T][top_k], device) are optional
+ * copies of the routing.  y may not alias x; it may alias residual.
+ * staging: NULL, or (NVFP4 only) a device buffer of min(n_experts, 64) * moe_blob_stride bytes,
+ * 16-byte aligned: the distinct selected experts are then copied into it 64 at a time by a
+ * device-resident list (moe_gather_experts' copy), and each group's tiles read the staged copies
+ * ("A hot expert cache made a 181 GiB model faster ...", sections "A gather kernel that reads
+ * wide" and "Prefill in groups of 64 experts").  A non-NULL staging with MXFP4 is
+ * MOE_ERR_INVALID. */
 moe_status moe_layer(const moe_shape *shape, const void *x, int32_t T, const float *w_router,
                      const float *logit_bias, const moe_expert *d_table, void *staging,
                      const void *residual, void *y, int32_t *topk_idx_out, float *topk_w_out,

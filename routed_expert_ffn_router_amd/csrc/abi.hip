@@ -37,10 +37,12 @@ WsLayout ws_layout(const moe_shape* s, int32_t T) {
     const size_t E = s->n_experts, k = s->top_k, d = s->d_model, f = s->d_ff;
     const size_t P = (size_t)T * k;
     L.nt = act_terms(s);
+    const bool nv = s->wformat == MOE_WF_NVFP4;
     const int variant = gemm_variant(s, T);
     size_t tt = (size_t)gemm_tile_tokens(variant, L.nt);
     // the fused few-token path tiles with the smaller few-token tile: bound for both
     if (T <= kSmallTokens && (size_t)gemm_tile_tokens(0, L.nt) < tt) tt = (size_t)gemm_tile_tokens(0, L.nt);
+    if (nv) tt = kNvTilePicks;
     L.max_tiles = (int)((E < P ? E : P) + P / tt + 1);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
@@ -54,11 +56,25 @@ WsLayout ws_layout(const moe_shape* s, int32_t T) {
     L.tiles = take(8 * (size_t)L.max_tiles);
     L.ntiles = take(4);
     L.desc = take(sizeof(TileDesc) * (size_t)L.max_tiles);
-    L.xq = take((size_t)T * L.nt * d);
-    L.xs = take((size_t)T * L.nt * d / 32);
-    L.hq = take(P * L.nt * f);
-    L.hs = take(P * L.nt * f / 32);
+    if (nv) {
+        // bf16 terms: x as two terms when it is fp32, h always as two
+        L.xq = take((size_t)T * 2 * d * 2);
+        L.xs = take(0);
+        L.hq = take(P * 2 * f * 2);
+        L.hs = take(0);
+    } else {
+        L.xq = take((size_t)T * L.nt * d);
+        L.xs = take((size_t)T * L.nt * d / 32);
+        L.hq = take(P * L.nt * f);
+        L.hs = take(P * L.nt * f / 32);
+    }
     L.o = take(4 * P * d);
+    if (nv) {
+        L.stage_table = take(sizeof(moe_expert) * E);
+        L.stage_list = take(4 * E);
+        L.stage_n = take(4);
+        L.stage_ranges = take(8 * ((E + kStageGroup - 1) / kStageGroup));
+    }
     L.total = o;
     return L;
 }
@@ -117,13 +133,58 @@ static GemmArgs gemm_args(const moe_shape* s, const moe_expert* table, int32_t T
     a.hq = ws + L.hq;
     a.hs = ws + L.hs;
     a.o = o;
+    a.tile_range = nullptr;
     return a;
+}
+
+// NVFP4: plan tiles of kNvTilePicks picks, bf16 terms of an fp32 x, then gate/up and down on the
+// bf16 matrix cores; with staging, the distinct experts are first copied into the staging buffer
+// kStageGroup at a time and each group's tiles run from the staged copies
+static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const void* x, int32_t T,
+                             const int32_t* offsets, const int32_t* sorted_pick, float* o, uint8_t* ws,
+                             const WsLayout& L, void* staging, hipStream_t st) {
+    const int tt = kNvTilePicks;
+    int32_t* tiles = (int32_t*)(ws + L.tiles);
+    int32_t* ntiles = (int32_t*)(ws + L.ntiles);
+    MOE_HIP(launch_plan(s, offsets, tt, tiles, ntiles, st));
+    const bool bf = s->act_dtype == MOE_DT_BF16;
+    const int NT = bf ? 1 : 2;
+    if (!bf) MOE_HIP(launch_bf16_terms((const float*)x, T, s->d_model, (uint16_t*)(ws + L.xq), st));
+    GemmArgs a = gemm_args(s, table, T, sorted_pick, offsets, ws, L, o);
+    const uint8_t* xin = bf ? (const uint8_t*)x : ws + L.xq;
+    if (!staging) {
+        a.aq = xin;
+        MOE_HIP(launch_nv_gemm(a, true, NT, L.max_tiles, st));
+        a.aq = ws + L.hq;
+        MOE_HIP(launch_nv_gemm(a, false, 2, L.max_tiles, st));
+        return MOE_OK;
+    }
+    int32_t* list = (int32_t*)(ws + L.stage_list);
+    int32_t* nlist = (int32_t*)(ws + L.stage_n);
+    int32_t* ranges = (int32_t*)(ws + L.stage_ranges);
+    moe_expert* staged = (moe_expert*)(ws + L.stage_table);
+    MOE_HIP(launch_stage_plan(s, offsets, tt, ntiles, list, nlist, ranges, st));
+    const size_t stride = moe_blob_stride(s);
+    const long long P = (long long)T * s->top_k;
+    const long long distinct = P < s->n_experts ? P : s->n_experts;
+    const int groups = (int)((distinct + kStageGroup - 1) / kStageGroup);
+    a.table = staged;
+    for (int g = 0; g < groups; ++g) {
+        MOE_HIP(launch_gather_group(s, table, list, nlist, g, (uint8_t*)staging, stride, staged, st));
+        a.tile_range = ranges + 2 * g;
+        a.aq = xin;
+        MOE_HIP(launch_nv_gemm(a, true, NT, L.max_tiles, st));
+        a.aq = ws + L.hq;
+        MOE_HIP(launch_nv_gemm(a, false, 2, L.max_tiles, st));
+    }
+    return MOE_OK;
 }
 
 // sequence shared by moe_expert_ffn and moe_layer (general token counts)
 static moe_status run_ffn(const moe_shape* s, const moe_expert* table, const void* x, int32_t T,
                           const int32_t* offsets, const int32_t* sorted_pick, float* o, uint8_t* ws,
                           const WsLayout& L, hipStream_t st) {
+    if (s->wformat == MOE_WF_NVFP4) return run_ffn_nv(s, table, x, T, offsets, sorted_pick, o, ws, L, nullptr, st);
     const int variant = gemm_variant(s, T);
     const int NT = L.nt;
     const int tt = gemm_tile_tokens(variant, NT);
@@ -236,7 +297,6 @@ moe_status moe_expert_ffn(const moe_shape* s, const moe_expert* d_table, const v
     if (T == 0) return MOE_OK;
     if (!d_table || !x || !expert_offsets || !sorted_pick || !o || !ws) return MOE_ERR_INVALID;
     if (!aligned(x, 16) || !aligned(o, 16) || !aligned(ws, 256)) return MOE_ERR_INVALID;
-    if (s->wformat != MOE_WF_MXFP4) return MOE_ERR_UNSUPPORTED;
     const WsLayout L = ws_layout(s, T);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     return run_ffn(s, d_table, x, T, expert_offsets, sorted_pick, o, (uint8_t*)ws, L, stream);
@@ -258,14 +318,14 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
                      hipStream_t stream) {
     MOE_TRY(check_shape(s));
     MOE_TRY(check_T(s, T));
-    (void)staging;
     if (T == 0) return MOE_OK;
     if (!x || !w_router || !d_table || !y || !ws) return MOE_ERR_INVALID;
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w_router, 16) || !aligned(ws, 256) ||
-        (residual && !aligned(residual, 16)))
+        (residual && !aligned(residual, 16)) || (staging && !aligned(staging, 16)))
         return MOE_ERR_INVALID;
     if (x == y) return MOE_ERR_INVALID;
-    if (s->wformat != MOE_WF_MXFP4) return MOE_ERR_UNSUPPORTED;
+    const bool nv = s->wformat == MOE_WF_NVFP4;
+    if (staging && !nv) return MOE_ERR_INVALID;      // staging is the NVFP4 gather path
     const WsLayout L = ws_layout(s, T);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     uint8_t* w8 = (uint8_t*)ws;
@@ -276,7 +336,7 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
     int32_t* sorted_pick = (int32_t*)(w8 + L.sorted_pick);
     int32_t* pick_pos = (int32_t*)(w8 + L.pick_pos);
     float* o = (float*)(w8 + L.o);
-    if (T <= kSmallTokens && s->top_k <= 64 && (long long)T * s->top_k <= kMaxFusedPicks &&
+    if (!nv && T <= kSmallTokens && s->top_k <= 64 && (long long)T * s->top_k <= kMaxFusedPicks &&
         s->d_model <= 8192) {
         // few tokens: fused router (logits, top-k, permute, plan, activation split), the gate/up
         // GEMM, and the down GEMM fused with the weighted combine: three launches per layer
@@ -328,7 +388,8 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
     MOE_HIP(launch_router_logits(s, x, T, w_router, logit_bias, logits, stream));
     MOE_HIP(launch_topk(s, logits, T, idx, w, stream));
     MOE_HIP(launch_permute(s, idx, T, offsets, sorted_pick, pick_pos, stream));
-    MOE_TRY(run_ffn(s, d_table, x, T, offsets, sorted_pick, o, w8, L, stream));
+    if (nv) MOE_TRY(run_ffn_nv(s, d_table, x, T, offsets, sorted_pick, o, w8, L, staging, stream));
+    else MOE_TRY(run_ffn(s, d_table, x, T, offsets, sorted_pick, o, w8, L, stream));
     MOE_HIP(launch_combine(s, o, w, pick_pos, T, residual, y, stream));
     return MOE_OK;
 }

@@ -97,13 +97,9 @@ hipError_t launch_fill_table(const moe_shape* s, const uint8_t* base, size_t str
 // gather: copy the listed experts into contiguous staging with 16-byte loads ("A hot expert
 // cache ...", section "A gather kernel that reads wide": wide reads from a device-resident list)
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_gather(const moe_expert* __restrict__ table,
-                                                const int32_t* __restrict__ list, int n, size_t nq,
-                                                size_t ns, size_t stride, uint8_t* __restrict__ staging,
-                                                moe_expert* __restrict__ staged) {
-    const int i = blockIdx.y;
-    const moe_expert src = table[list[i]];
-    uint8_t* dst = staging + (size_t)i * stride;
+// copy one expert's six sub-tensors into dst (its canonical blob) with 16-byte loads; returns the
+// staged table entry
+__device__ moe_expert gather_one(const moe_expert& src, uint8_t* dst, size_t nq, size_t ns, size_t stride) {
     const size_t n16 = (3 * nq + 3 * ns) / 16;
     for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n16; u += (size_t)gridDim.x * 256) {
         const size_t off = u * 16;
@@ -116,26 +112,60 @@ __global__ __launch_bounds__(256) void k_gather(const moe_expert* __restrict__ t
         else sp = src.down_s + (off - 3 * nq - 2 * ns);
         *(uint4*)(dst + off) = *(const uint4*)sp;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        moe_expert m;
-        m.gate_q = dst;
-        m.up_q = dst + nq;
-        m.down_q = dst + 2 * nq;
-        m.gate_s = dst + 3 * nq;
-        m.up_s = dst + 3 * nq + ns;
-        m.down_s = dst + 3 * nq + 2 * ns;
-        m.gate_ts = src.gate_ts;
-        m.up_ts = src.up_ts;
-        m.down_ts = src.down_ts;
-        m.reserved = 0.0f;
+    moe_expert m;
+    m.gate_q = dst;
+    m.up_q = dst + nq;
+    m.down_q = dst + 2 * nq;
+    m.gate_s = dst + 3 * nq;
+    m.up_s = dst + 3 * nq + ns;
+    m.down_s = dst + 3 * nq + 2 * ns;
+    m.gate_ts = src.gate_ts;
+    m.up_ts = src.up_ts;
+    m.down_ts = src.down_ts;
+    m.reserved = 0.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && stride >= 3 * nq + 3 * ns + 12) {
         float* ts = (float*)(dst + 3 * nq + 3 * ns);
-        if (stride >= 3 * nq + 3 * ns + 12) {
-            ts[0] = src.gate_ts;
-            ts[1] = src.up_ts;
-            ts[2] = src.down_ts;
-        }
-        staged[i] = m;
+        ts[0] = src.gate_ts;
+        ts[1] = src.up_ts;
+        ts[2] = src.down_ts;
     }
+    return m;
+}
+
+__global__ __launch_bounds__(256) void k_gather(const moe_expert* __restrict__ table,
+                                                const int32_t* __restrict__ list, int n, size_t nq,
+                                                size_t ns, size_t stride, uint8_t* __restrict__ staging,
+                                                moe_expert* __restrict__ staged) {
+    const int i = blockIdx.y;
+    const moe_expert m = gather_one(table[list[i]], staging + (size_t)i * stride, nq, ns, stride);
+    if (blockIdx.x == 0 && threadIdx.x == 0) staged[i] = m;
+}
+
+// group `group` of the distinct-expert list: expert list[group * G + i] goes to staging slot i and
+// its staged entry to staged_by_expert[expert] (the table the grouped GEMMs read)
+__global__ __launch_bounds__(256) void k_gather_group(const moe_expert* __restrict__ table,
+                                                      const int32_t* __restrict__ list,
+                                                      const int32_t* __restrict__ nlist, int group, size_t nq,
+                                                      size_t ns, size_t stride, uint8_t* __restrict__ staging,
+                                                      moe_expert* __restrict__ staged_by_expert) {
+    const int i = blockIdx.y;
+    const int li = group * kStageGroup + i;
+    if (li >= *nlist) return;
+    const int e = list[li];
+    const moe_expert m = gather_one(table[e], staging + (size_t)i * stride, nq, ns, stride);
+    if (blockIdx.x == 0 && threadIdx.x == 0) staged_by_expert[e] = m;
+}
+
+hipError_t launch_gather_group(const moe_shape* s, const moe_expert* table, const int32_t* list,
+                               const int32_t* nlist, int group, uint8_t* staging, size_t stride,
+                               moe_expert* staged_by_expert, hipStream_t st) {
+    trace("gather", 0, st);
+    const BlobSizes z = blob_sizes(s);
+    const int G = s->n_experts < kStageGroup ? s->n_experts : kStageGroup;
+    MOE_LAUNCH(k_gather_group, dim3(64, G), dim3(256), 0, st, table, list, nlist, group, z.nq, z.ns, stride, staging,
+               staged_by_expert);
+    trace("gather", 1, st);
+    return hipGetLastError();
 }
 
 hipError_t launch_gather(const moe_shape* s, const moe_expert* table, const int32_t* list, int n,

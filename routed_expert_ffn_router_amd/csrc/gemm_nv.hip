@@ -1,0 +1,214 @@
+// Grouped expert GEMMs for NVFP4 weights: E2M1 codes with one E4M3 scale per 16 elements along
+// each row and one fp32 scale per weight tensor ("A hot expert cache made a 181 GiB model
+// faster ...", section "The wall: one PCIe transfer per token": the NVFP4 build of the model).
+//
+// The scaled FP4 matrix cores take only power-of-two scales per 32 elements, so an NVFP4 weight
+// is dequantised in registers instead: V_CVT_SCALEF32_PK_F32_FP4 decodes two codes, an fp32
+// multiply applies the E4M3 block scale, and the product is rounded to bf16.  That product is
+// exact in bf16 (at most 2 + 4 significant bits), so the bf16 matrix cores
+// (V_MFMA_F32_16X16X32_BF16) see the weights exactly;
+// the tensor scale multiplies the fp32 accumulator.  Activations are the bf16 operand: bf16 x as
+// it is, an fp32 x or the SwiGLU output h as two bf16 terms (hi = bf16(v), lo = bf16(v - hi)),
+// each term one MFMA column.
+//
+// K order of one MFMA: lane l supplies 8 consecutive K of row (A) or column (B) l % 16; any
+// assignment of K to lane groups works when both operands share it (measured on gfx950).  Here a
+// super-step covers 128 K of a row (64 code bytes): lane group g takes elements [32g, 32g + 32)
+// (16 code bytes, two NVFP4 blocks) and MFMA h of the super-step its elements [8h, 8h + 8).
+//
+// Work decomposition: a tile is up to 8 consecutive sorted picks of one expert; a workgroup of
+// four waves owns one tile and one 32-row block of the output and splits K four ways, the partial
+// sums reduced through LDS in a fixed order.
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float v4f_nv __attribute__((ext_vector_type(4)));
+
+constexpr int kNvTileTokens = 8;     // picks per tile: 16 MFMA columns of (pick, term)
+
+// 8 codes (one dword, element 2i in the low nibble of byte i) x block scale -> 8 bf16.  The
+// conversion unit's scale operand acts as a power of two only, so codes are converted at scale 1
+// and multiplied by the E4M3 block scale in fp32 (exact: at most 2 + 4 significant bits), then
+// rounded to bf16 (exact as well).
+__device__ __forceinline__ bf16x8_t nv_dequant8(uint32_t codes, float scale) {
+    bf16x8_t r;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const v2f_t v = b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0)
+                      : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1)
+                      : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2)
+                               : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+        r[2 * b] = (__bf16)(v[0] * scale);
+        r[2 * b + 1] = (__bf16)(v[1] * scale);
+    }
+    return r;
+}
+
+// two E4M3 scale bytes (low byte first) -> two floats (exact)
+__device__ __forceinline__ v2f_t e4m3x2_to_f32(uint32_t two) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(two, 1.0f, false);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+    bf16x8_t r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) { return f32_to_bf16_bits(f); }
+
+// bf16 terms of fp32 activations: hi = bf16(v), lo = bf16(v - hi); layout [rows][2][K]
+__global__ __launch_bounds__(256) void k_bf16_terms(const float* __restrict__ x, size_t n, int K,
+                                                   uint16_t* __restrict__ terms) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float v = x[i];
+    const uint16_t hi = bf16_rne(v);
+    const uint16_t lo = bf16_rne(v - bf16_bits_to_f32(hi));
+    const size_t r = i / K, c = i % K;
+    terms[(r * 2) * K + c] = hi;
+    terms[(r * 2 + 1) * K + c] = lo;
+}
+
+hipError_t launch_bf16_terms(const float* x, int rows, int K, uint16_t* terms, hipStream_t st) {
+    trace("act_split", 0, st);
+    const size_t n = (size_t)rows * K;
+    MOE_LAUNCH(k_bf16_terms, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, n, K, terms);
+    trace("act_split", 1, st);
+    return hipGetLastError();
+}
+
+// NT: bf16 terms per activation (1: bf16 x read in place; 2: hi/lo terms).  GATEUP: the gate and
+// up rows of one 32-row block, SwiGLU, and h as two bf16 terms; else the down rows, o in fp32.
+template <int NT, bool GATEUP>
+__global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
+    constexpr int NA = GATEUP ? 4 : 2;      // 16-row fragments: gate lo/hi, up lo/hi (or down lo/hi)
+    constexpr int TT = kNvTileTokens;
+    const int tile = blockIdx.x;
+    int t0 = 0, t1 = *a.ntiles;
+    if (a.tile_range) {
+        t0 = a.tile_range[0];
+        t1 = a.tile_range[1];
+    }
+    if (tile < t0 || tile >= t1) return;
+    const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
+    const int ntok = min(TT, a.offsets[e + 1] - i0);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int K = GATEUP ? a.d : a.f;
+    const moe_expert ex = a.table[e];
+    const int rg = blockIdx.y;
+    const int T0 = 32 * rg;
+    const int NS = K / 128;                  // super-steps of the row, shared out over the 4 waves
+    const int s0 = (wave * NS) / 4, nss = ((wave + 1) * NS) / 4 - s0;
+
+    // weights: fragment f = rows T0 + 16 (f & 1) + li of gate (f < 2) or up (f >= 2)
+    const uint8_t* aq[NA];
+    const uint8_t* as[NA];
+#pragma unroll
+    for (int f = 0; f < NA; ++f) {
+        const int row = T0 + 16 * (f & 1) + li;
+        const uint8_t* mq = GATEUP ? (f < 2 ? ex.gate_q : ex.up_q) : ex.down_q;
+        const uint8_t* ms = GATEUP ? (f < 2 ? ex.gate_s : ex.up_s) : ex.down_s;
+        aq[f] = mq + (size_t)row * (K / 2) + (size_t)s0 * 64 + lg * 16;
+        as[f] = ms + (size_t)row * (K / 16) + (size_t)s0 * 8 + lg * 2;
+    }
+    // activations: column li = (pick tc, term t); columns past the tile read the tile's first
+    // pick (their results are not used)
+    const int tc = li / NT, t = li % NT;
+    const bool valid = tc < ntok;
+    const int tcc = valid ? tc : 0;
+    const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tcc] / a.k) : (size_t)(i0 + tcc);
+    const uint16_t* bp = (const uint16_t*)a.aq + (arow * NT + t) * (size_t)K + (size_t)s0 * 128 + lg * 32;
+
+    v4f_nv acc[NA];
+#pragma unroll
+    for (int f = 0; f < NA; ++f) acc[f] = v4f_nv{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nss; ++s) {
+        uint4 A[NA];
+        uint32_t sc[NA];
+#pragma unroll
+        for (int f = 0; f < NA; ++f) {
+            A[f] = *(const uint4*)(aq[f] + (size_t)s * 64);
+            sc[f] = *(const uint16_t*)(as[f] + (size_t)s * 8);
+        }
+        uint4 B[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) B[h] = *(const uint4*)(bp + (size_t)s * 128 + 8 * h);
+#pragma unroll
+        for (int f = 0; f < NA; ++f) {
+            const v2f_t bs = e4m3x2_to_f32(sc[f]);
+            const uint32_t w[4] = {A[f].x, A[f].y, A[f].z, A[f].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nv_dequant8(w[h], h < 2 ? bs[0] : bs[1]),
+                                                                 as_bf16x8(B[h]), acc[f], 0, 0, 0);
+        }
+    }
+    // K quarters summed through LDS in wave order
+    __shared__ float red[3][NA * 4][64];
+    if (wave > 0) {
+#pragma unroll
+        for (int f = 0; f < NA; ++f)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave - 1][f * 4 + r][lane] = acc[f][r];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int f = 0; f < NA; ++f)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[f][r] += red[w][f * 4 + r][lane];
+    if constexpr (NT == 2) {
+#pragma unroll
+        for (int f = 0; f < NA; ++f)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[f][r] = sum_adjacent<2>(acc[f][r]);
+    }
+    if (!valid || t != 0) return;
+    const size_t pos = (size_t)i0 + tc;
+    if constexpr (GATEUP) {
+        // h = silu(g) u for rows T0 + 4 lg + r (f = 0) and T0 + 16 + 4 lg + r (f = 1), as two
+        // bf16 terms [P][2][f]
+        uint16_t* hb = (uint16_t*)a.hq + pos * 2 * (size_t)a.f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float g = acc[half][r] * ex.gate_ts, u = acc[2 + half][r] * ex.up_ts;
+                const float hv = g / (1.0f + __expf(-g)) * u;
+                const uint16_t hi = bf16_rne(hv);
+                const uint16_t lo = bf16_rne(hv - bf16_bits_to_f32(hi));
+                const int row = T0 + 16 * half + 4 * lg + r;
+                hb[row] = hi;
+                hb[a.f + row] = lo;
+            }
+    } else {
+        float* dst = a.o + pos * (size_t)a.d + T0 + 4 * lg;
+        *(float4*)dst = make_float4(acc[0][0] * ex.down_ts, acc[0][1] * ex.down_ts, acc[0][2] * ex.down_ts,
+                                    acc[0][3] * ex.down_ts);
+        *(float4*)(dst + 16) = make_float4(acc[1][0] * ex.down_ts, acc[1][1] * ex.down_ts,
+                                           acc[1][2] * ex.down_ts, acc[1][3] * ex.down_ts);
+    }
+}
+
+hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int max_tiles, hipStream_t st) {
+    const char* name = gateup ? "gemm_gate_up" : "gemm_down";
+    trace(name, 0, st);
+    const int rows = gateup ? a.f : a.d;
+    dim3 grid(max_tiles, rows / 32);
+    if (gateup) {
+        if (NT == 1) MOE_LAUNCH((k_nv_gemm<1, true>), grid, dim3(256), 0, st, a);
+        else MOE_LAUNCH((k_nv_gemm<2, true>), grid, dim3(256), 0, st, a);
+    } else {
+        MOE_LAUNCH((k_nv_gemm<2, false>), grid, dim3(256), 0, st, a);
+    }
+    trace(name, 1, st);
+    return hipGetLastError();
+}
+
+}  // namespace moe

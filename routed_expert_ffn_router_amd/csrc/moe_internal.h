@@ -319,7 +319,9 @@ struct TileDesc {
 static_assert(sizeof(TileDesc) == 128, "tile record is 128 bytes");
 
 struct WsLayout {
-    size_t counter, logits, idx, w, offsets, sorted_pick, pick_pos, tiles, ntiles, desc, xq, xs, hq, hs, o, total;
+    size_t counter, logits, idx, w, offsets, sorted_pick, pick_pos, tiles, ntiles, desc, xq, xs, hq, hs, o;
+    size_t stage_table, stage_list, stage_n, stage_ranges;   // NVFP4 staging (moe_layer)
+    size_t total;
     int nt;        // activation terms
     int max_tiles;
 };
@@ -378,6 +380,7 @@ struct GemmArgs {
     uint8_t* hq;              // gate/up output: h terms
     uint8_t* hs;
     float* o;                 // down output [P][d]
+    const int32_t* tile_range;  // NVFP4 staged groups: [t0, t1) of the tiles to run, or null (all)
 };
 
 // picks whose per-row outputs the fused down+combine kernel keeps in LDS (P = T * top_k)
@@ -407,6 +410,18 @@ int ksplit_for(int K, int variant);
 bool decode_gemm_ok(const moe_shape* s);
 hipError_t launch_gateup_dec(const GemmArgs& a, int NT, int max_tiles, hipStream_t st);
 hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineArgs& c, int NT, hipStream_t st);
+
+// NVFP4 (gemm_nv.hip): bf16 terms of fp32 activations, and the grouped GEMMs
+constexpr int kNvTilePicks = 8;
+constexpr int kStageGroup = 64;           // experts staged per group (NVFP4 layer with staging)
+hipError_t launch_bf16_terms(const float* x, int rows, int K, uint16_t* terms, hipStream_t st);
+hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int max_tiles, hipStream_t st);
+// the distinct experts of a plan, in groups of kStageGroup, with each group's tile range
+hipError_t launch_stage_plan(const moe_shape* s, const int32_t* offsets, int tt, const int32_t* ntiles,
+                             int32_t* list, int32_t* nlist, int32_t* ranges, hipStream_t st);
+hipError_t launch_gather_group(const moe_shape* s, const moe_expert* table, const int32_t* list,
+                               const int32_t* nlist, int group, uint8_t* staging, size_t stride,
+                               moe_expert* staged_by_expert, hipStream_t st);
 
 hipError_t launch_combine(const moe_shape* s, const float* o, const float* w, const int32_t* pick_pos,
                           int T, const void* residual, void* y, hipStream_t st);

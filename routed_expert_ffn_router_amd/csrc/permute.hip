@@ -130,4 +130,50 @@ hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int tile_toke
     return hipGetLastError();
 }
 
+// The distinct experts of a tile plan in ascending order, cut into groups of kStageGroup, with
+// each group's tile range [first tile of its first expert, first tile of the next group): the
+// tiles of a plan are ordered by expert, so a group's tiles are contiguous.  Unused groups (up
+// to max_groups) get an empty range.
+__global__ __launch_bounds__(kPermThreads) void k_stage_plan(const int32_t* __restrict__ offsets, int E, int tt,
+                                                             const int32_t* __restrict__ ntiles,
+                                                             int32_t* __restrict__ list, int32_t* __restrict__ nlist,
+                                                             int32_t* __restrict__ ranges, int max_groups) {
+    __shared__ int scratch[kPermWaves];
+    const int e = threadIdx.x;
+    const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+    const int active = cnt > 0 ? 1 : 0;
+    int total_tiles, n;
+    const int first_tile = block_excl_scan((cnt + tt - 1) / tt, scratch, &total_tiles);
+    const int pos = block_excl_scan(active, scratch, &n);
+    const int G = kStageGroup;
+    const int groups = (n + G - 1) / G;
+    for (int g = e; g < max_groups; g += kPermThreads) {
+        if (g >= groups) {
+            ranges[2 * g] = 0;
+            ranges[2 * g + 1] = 0;
+        }
+    }
+    if (active) {
+        list[pos] = e;
+        if (pos % G == 0) {
+            ranges[2 * (pos / G)] = first_tile;
+            if (pos > 0) ranges[2 * (pos / G - 1) + 1] = first_tile;
+        }
+    }
+    if (e == 0) {
+        *nlist = n;
+        if (n > 0) ranges[2 * (groups - 1) + 1] = *ntiles;
+    }
+}
+
+hipError_t launch_stage_plan(const moe_shape* s, const int32_t* offsets, int tt, const int32_t* ntiles,
+                             int32_t* list, int32_t* nlist, int32_t* ranges, hipStream_t st) {
+    trace("stage_plan", 0, st);
+    const int max_groups = (s->n_experts + kStageGroup - 1) / kStageGroup;
+    MOE_LAUNCH(k_stage_plan, dim3(1), dim3(kPermThreads), 0, st, offsets, s->n_experts, tt, ntiles, list, nlist,
+               ranges, max_groups);
+    trace("stage_plan", 1, st);
+    return hipGetLastError();
+}
+
 }  // namespace moe

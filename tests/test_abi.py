@@ -70,7 +70,12 @@ def test_validation_other_entry_points():
     b = ctypes.byref
     assert L.moe_permute(b(sh), None, 4, FAKE, FAKE, FAKE, None, 0, 0) == m.MOE_ERR_INVALID
     assert L.moe_expert_ffn(b(sh), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 16, 0) == m.MOE_ERR_WORKSPACE
-    assert L.moe_expert_ffn(b(nv), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 1 << 40, 0) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_ffn(b(nv), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 16, 0) == m.MOE_ERR_WORKSPACE
+    # staging belongs to the NVFP4 gather path; it must be 16-byte aligned
+    assert L.moe_layer(b(sh), FAKE, 4, FAKE, None, FAKE, FAKE, None, 2 * FAKE, None, None, FAKE, 1 << 40, 0) \
+        == m.MOE_ERR_INVALID
+    assert L.moe_layer(b(nv), FAKE, 4, FAKE, None, FAKE, FAKE + 8, None, 2 * FAKE, None, None, FAKE, 1 << 40, 0) \
+        == m.MOE_ERR_INVALID
     assert L.moe_combine(b(sh), FAKE, FAKE, None, 4, None, FAKE, 0) == m.MOE_ERR_INVALID
     assert L.moe_layer(b(sh), FAKE, 4, FAKE, None, FAKE, None, None, 2 * FAKE, None, None, FAKE, 16, 0) \
         == m.MOE_ERR_WORKSPACE
