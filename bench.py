@@ -185,7 +185,8 @@ def main():
     ap.add_argument("--layers", type=int, default=42)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--only", choices=["decode", "prefill", "batched"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "batched", "nvfp4"], default=None)
+    ap.add_argument("--nv-layers", type=int, default=8, help="NVFP4 decode stack depth")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
@@ -224,8 +225,10 @@ def main():
     # ---------------- decode stack (headline) ----------------
     wl_dec = synth.WORKLOADS["decode"]
     nl = args.layers
-    log(f"# building the {nl}-layer decode stack in HBM")
-    stack = Stack(m, synth, torch, wl_dec, nl, args.seed, log)
+    stack = None
+    if want("decode") or want("batched") or want("prefill"):
+        log(f"# building the {nl}-layer decode stack in HBM")
+        stack = Stack(m, synth, torch, wl_dec, nl, args.seed, log)
 
     def run_stack(T, biases, x0, bufs, ws, keep=None):
         """One step: T tokens through every layer, x_{l+1} = x_l + y_l (residual fused)."""
@@ -335,6 +338,61 @@ def main():
             f"{100 * out['prefill']['roofline_frac']:.1f}% of the roofline bound")
         log(f"#   kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern.items()))
 
+    # ---------------- NVFP4 configuration: decode T=1 and a 2048-token chunk, staged or not ------
+    if want("nvfp4"):
+        wl = synth.WORKLOADS["nvfp4_decode"]
+        nvl = args.nv_layers
+        log(f"# building the {nvl}-layer NVFP4 stack in HBM")
+        nst = Stack(m, synth, torch, wl, nvl, args.seed, log)
+        stride = m.moe_blob_stride(nst.shape)
+        staging = torch.empty(min(wl.n_experts, 64), nst.blob.shape[2], dtype=torch.uint8, device="cuda")
+        rec = {}
+        for T in (1, 2048):
+            x0 = synth.make_x(wl, args.seed, "cuda", tokens=T, tag=f"x_nv{T}")
+            bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+            ws = m.workspace(nst.shape, T)
+            idx = torch.empty(nvl, T, wl.top_k, dtype=torch.int32, device="cuda")
+            for staged in (False, True):
+                def step(staged=staged):
+                    cur = x0
+                    for l in range(nvl):
+                        nxt = bufs[l % 2]
+                        m.moe_layer(nst.shape, cur, T, nst.router[l], None, nst.table[l],
+                                    staging if staged else None, cur, nxt, idx[l], None, ws, stream=S)
+                        cur = nxt
+                with torch.cuda.stream(stream):
+                    step()
+                hip.sync(S)
+                if T == 1:
+                    gexec, _ = hip.capture(S, step)
+                    run = lambda: hip.launch(gexec, S)
+                else:
+                    run = step
+                reps = max(3, args.steps // (1 if T == 1 else 10))
+                for _ in range(2):
+                    run()
+                hip.sync(S)
+                e0, e1 = hip.event(), hip.event()
+                hip.record(e0, S)
+                for _ in range(reps):
+                    run()
+                hip.record(e1, S)
+                ms = hip.elapsed_ms(e0, e1) / reps / nvl
+                kern = {k: float(np.mean(v)) for k, v in kernel_times(hip, m, S, step, reps=2).items()}
+                touched = float(np.mean([len(np.unique(idx[l].cpu().numpy())) for l in range(nvl)]))
+                ffn_bytes = touched * stride + wl.n_experts * wl.d_model * 4
+                stage_bytes = 2 * touched * stride if staged else 0
+                key = f"T{T}_{'staged' if staged else 'in_place'}"
+                rec[key] = {"ms_per_layer": ms, "tokens_per_s": T / (ms * 1e-3), "experts_per_layer": touched,
+                            "bytes_without_staging": ffn_bytes, "staging_bytes": stage_bytes,
+                            "hbm_frac_without_staging": ffn_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                            "hbm_frac_with_staging": (ffn_bytes + stage_bytes) / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                            "kernels_us": kern}
+                log(f"# nvfp4 {key}: {1000 * ms:.1f} us/layer, {T / (ms * 1e-3):.0f} tokens/s, "
+                    f"{touched:.0f} experts/layer; kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern.items()))
+        out["nvfp4"] = rec
+        del nst
+
     # ---------------- oracle on the host cores (bounded sample of the decode stack) ------------
     cpu = None
     parity = None
@@ -407,14 +465,14 @@ def main():
             "kernels_us": dec["kernels_us"],
         })
     else:
-        first = next(k for k in ("prefill", "batched") if k in out)
-        r = out[first]
+        first = next(k for k in ("prefill", "batched", "nvfp4") if k in out)
+        r = out[first] if first != "nvfp4" else out["nvfp4"]["T1_in_place"]
         line.update({"value": r.get("tokens_per_s", r.get("layer_tokens_per_s")), "unit": "tokens/s",
                      "ms_per_step": r.get("ms_per_layer", r.get("ms_per_step")),
                      "config": {"workload": first}})
     line["cpu_baseline"] = cpu
     line["parity"] = parity
-    for k in ("prefill", "batched"):
+    for k in ("prefill", "batched", "nvfp4"):
         if k in out:
             line[k] = {kk: vv for kk, vv in out[k].items()}
     print(json.dumps(line), flush=True)

@@ -47,7 +47,7 @@ WsLayout ws_layout(const moe_shape* s, int32_t T) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
     L.counter = take(4);
-    L.logits = take(8 * (size_t)T * E);
+    L.logits = take(8 * (size_t)T * E * (size_t)logits_splits(s, T));   // partial slices of the tiled router
     L.idx = take(4 * P);
     L.w = take(4 * P);
     L.offsets = take(4 * (E + 1));

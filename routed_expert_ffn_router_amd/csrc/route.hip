@@ -31,60 +31,82 @@ __global__ __launch_bounds__(256) void k_logits_gemv(const XT* __restrict__ x, i
     }
 }
 
-// ---------------------------------------------------------------------------------------------
-// logits, many tokens: 64 tokens x 64 experts per workgroup, K in chunks of 16 through LDS,
-// 4 x 4 outputs per thread, fp64 FMA.
-// ---------------------------------------------------------------------------------------------
+// Router logits on the fp64 matrix cores (V_MFMA_F64_16X16X4_F64), for T > 8.  Products of
+// bf16 (or fp32) x and fp32 Wr are exact in fp64 and summed in fp64, so the top-k decides on the
+// same numbers as a sequential fp64 sum up to the last bits.  A workgroup (4 waves) owns 32
+// tokens x 64 experts and one K slice of the split; wave w computes tokens 16 (w & 1) + [0, 16)
+// against experts 32 (w >> 1) + [0, 32) as two 16x16 blocks.  Operand layout (measured): lane l
+// supplies row or column l % 16 at K = l / 16; result register r of lane l is row 4 r + l / 16,
+// column l % 16.  The K slice is staged through LDS 64 columns at a time as fp32.  Slice z's
+// partial sums go to part[z][t][e]; slice 0 also adds the bias.  The top-k sums the slices in
+// order z = 0, 1, ...
+constexpr int kLgTok = 32, kLgExp = 64, kLgK = 64;
+
 template <typename XT>
-__global__ __launch_bounds__(256) void k_logits_tiled(const XT* __restrict__ x, int T, int d,
-                                                      const float* __restrict__ wr,
-                                                      const float* __restrict__ bias, int E,
-                                                      double* __restrict__ logits) {
-    constexpr int TT = 64, TE = 64, KC = 16;
-    __shared__ double xs[KC][TT + 1];
-    __shared__ double ws[KC][TE + 1];
-    const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    double acc[4][4];
+__global__ __launch_bounds__(256) void k_logits_mfma(const XT* __restrict__ x, int T, int d,
+                                                      const float* __restrict__ wr, const float* __restrict__ bias,
+                                                      int E, int kslice, double* __restrict__ part) {
+    __shared__ float xs[kLgTok][kLgK + 1];
+    __shared__ float ws[kLgExp][kLgK + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * kLgTok, e0 = blockIdx.y * kLgExp, z = blockIdx.z;
+    const int kb = z * kslice;
+    typedef double d4 __attribute__((ext_vector_type(4)));
+    d4 acc[2] = {d4{0, 0, 0, 0}, d4{0, 0, 0, 0}};
+    const int tr = (wave & 1) * 16 + (lane & 15);        // A row (token) of this lane
+    const int ec = (wave >> 1) * 32 + (lane & 15);       // B column (expert) of block 0
+    const int kl = lane >> 4;
+    for (int k0 = kb; k0 < kb + kslice; k0 += kLgK) {
+        // stage: x tile 32 x 64 (8 per thread), Wr tile 64 x 64 (16 per thread); rows past the
+        // end re-read the last row (their results are not stored)
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+        for (int i = 0; i < (kLgTok * kLgK) / 256; ++i) {
+            const int q = i * 256 + tid, r = q / kLgK, c = q % kLgK;
+            const int t = min(t0 + r, T - 1);
+            xs[r][c] = load_act(x, (size_t)t * d + k0 + c);
+        }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-    for (int k0 = 0; k0 < d; k0 += KC) {
-        // 64 rows x 16 k for both operands: 1024 elements each, 4 per thread
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            int idx = threadIdx.x + u * 256;
-            int r = idx >> 4, kk = idx & 15;
-            int t = t0 + r, e = e0 + r;
-            xs[kk][r] = (t < T) ? load_act_f64(x, (size_t)t * d + k0 + kk) : 0.0;
-            ws[kk][r] = (e < E) ? (double)wr[(size_t)e * d + k0 + kk] : 0.0;
+        for (int i = 0; i < (kLgExp * kLgK) / 256 / 4; ++i) {
+            const int q = i * 256 + tid, r = q / (kLgK / 4), c = (q % (kLgK / 4)) * 4;
+            const int e = min(e0 + r, E - 1);
+            const float4 v = *(const float4*)(wr + (size_t)e * d + k0 + c);
+            ws[r][c] = v.x;
+            ws[r][c + 1] = v.y;
+            ws[r][c + 2] = v.z;
+            ws[r][c + 3] = v.w;
         }
         __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < KC; ++kk) {
-            double xa[4], wb[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) xa[a] = xs[kk][ty + 16 * a];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) wb[b] = ws[kk][tx + 16 * b];
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = fma(xa[a], wb[b], acc[a][b]);
+#pragma unroll 4
+        for (int kk = 0; kk < kLgK; kk += 4) {
+            const double a = (double)xs[tr][kk + kl];
+            const double b0 = (double)ws[ec][kk + kl];
+            const double b1 = (double)ws[ec + 16][kk + kl];
+            acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b0, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b1, acc[1], 0, 0, 0);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        int t = t0 + ty + 16 * a;
-        if (t >= T) continue;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            int e = e0 + tx + 16 * b;
-            if (e < E) logits[(size_t)t * E + e] = bias ? acc[a][b] + (double)bias[e] : acc[a][b];
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + (wave & 1) * 16 + 4 * r + (lane >> 4);
+            const int e = e0 + (wave >> 1) * 32 + 16 * j + (lane & 15);
+            if (t < T && e < E) {
+                double v = acc[j][r];
+                if (z == 0 && bias) v += (double)bias[e];
+                part[((size_t)z * T + t) * E + e] = v;
+            }
         }
-    }
+}
+
+// K slices for the tiled router: enough workgroups to cover the chip, slices of >= 128 columns
+int logits_splits(const moe_shape* s, int T) {
+    if (T <= 8) return 1;
+    const long long tiles = (long long)((T + kLgTok - 1) / kLgTok) * ((s->n_experts + kLgExp - 1) / kLgExp);
+    int S = 1;
+    while (tiles * S < 512 && s->d_model % (2 * S * 128) == 0 && S < 64) S *= 2;
+    return S;
 }
 
 hipError_t launch_router_logits(const moe_shape* s, const void* x, int T, const float* wr,
@@ -101,13 +123,14 @@ hipError_t launch_router_logits(const moe_shape* s, const void* x, int T, const 
             MOE_LAUNCH((k_logits_gemv<float>), grid, dim3(256), 0, st,
                                (const float*)x, T, d, wr, bias, E, logits);
     } else {
-        dim3 grid((T + 63) / 64, (E + 63) / 64);
+        const int S = logits_splits(s, T);
+        dim3 grid((T + kLgTok - 1) / kLgTok, (E + kLgExp - 1) / kLgExp, S);
         if (bf)
-            MOE_LAUNCH((k_logits_tiled<uint16_t>), grid, dim3(256), 0, st,
-                               (const uint16_t*)x, T, d, wr, bias, E, logits);
+            MOE_LAUNCH((k_logits_mfma<uint16_t>), grid, dim3(256), 0, st, (const uint16_t*)x, T, d, wr, bias, E,
+                       d / S, logits);
         else
-            MOE_LAUNCH((k_logits_tiled<float>), grid, dim3(256), 0, st,
-                               (const float*)x, T, d, wr, bias, E, logits);
+            MOE_LAUNCH((k_logits_mfma<float>), grid, dim3(256), 0, st, (const float*)x, T, d, wr, bias, E, d / S,
+                       logits);
     }
     trace("router_logits", 1, st);
     return hipGetLastError();
@@ -221,22 +244,43 @@ __device__ void wave_topk(const double* __restrict__ l, int E, int k, int32_t* i
     topk_select<S>(lv, l, E, k, idx, w);
 }
 
+// one wave per token; the logits are the sum, in slice order, of nsplit partial slices
+// [nsplit][T][E] (nsplit = 1: the logits themselves)
 template <int S>
-__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int T, int E, int k,
+__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int T, int E, int k, int nsplit,
                                               int32_t* __restrict__ idx, float* __restrict__ wout) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    wave_topk<S>(logits + (size_t)t * E, E, k, idx + (size_t)t * k, wout + (size_t)t * k);
+    const double* l = logits + (size_t)t * E;
+    double lv[S];
+    topk_load<S>(l, E, lv);
+    for (int z = 1; z < nsplit; ++z) {
+        double pz[S];
+        topk_load<S>(l + (size_t)z * T * E, E, pz);
+#pragma unroll
+        for (int s = 0; s < S; ++s) lv[s] += pz[s];
+    }
+    if (nsplit > 1 && k > 64) {
+        // the weights of picks past 64 re-read l[idx]: store the summed logits over slice 0
+        double* lw = const_cast<double*>(l);
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+            if (lane + 64 * s < E) lw[lane + 64 * s] = lv[s];
+        __threadfence_block();
+    }
+    topk_select<S>(lv, l, E, k, idx + (size_t)t * k, wout + (size_t)t * k);
 }
 
 hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t* idx, float* w,
                        hipStream_t st) {
     trace("topk", 0, st);
     dim3 grid((T + 3) / 4);
+    const int nsplit = logits_splits(s, T);
     if (s->n_experts <= 320)
-        MOE_LAUNCH(k_topk<5>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, idx, w);
+        MOE_LAUNCH(k_topk<5>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, nsplit, idx, w);
     else
-        MOE_LAUNCH(k_topk<16>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, idx, w);
+        MOE_LAUNCH(k_topk<16>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, nsplit, idx, w);
     trace("topk", 1, st);
     return hipGetLastError();
 }
