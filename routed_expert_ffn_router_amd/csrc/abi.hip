@@ -189,7 +189,7 @@ static moe_status run_ffn(const moe_shape* s, const moe_expert* table, const voi
     const int NT = L.nt;
     const int tt = gemm_tile_tokens(variant, NT);
     MOE_HIP(launch_plan(s, offsets, tt, (int32_t*)(ws + L.tiles), (int32_t*)(ws + L.ntiles), st));
-    const int SS1 = super_step(s->d_model, ksplit_for(s->d_model, variant));
+    const int SS1 = act_super_step(s->d_model, variant);
     MOE_HIP(launch_act_split(s, x, T, s->d_model, SS1, NT, ws + L.xq, ws + L.xs, st));
     GemmArgs a = gemm_args(s, table, T, sorted_pick, offsets, ws, L, o);
     MOE_HIP(launch_gemm_gateup(a, NT, variant, L.max_tiles, st));

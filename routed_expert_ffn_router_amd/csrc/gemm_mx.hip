@@ -763,6 +763,9 @@ int gemm_variant(const moe_shape* s, int T) {
 
 int gemm_tile_tokens(int variant, int NT) { return (variant == 0 ? 16 : 128) / NT; }
 
+// activation layout super-step for the variant: the LDS-tiled many-picks GEMM reads chunks of 128
+int act_super_step(int K, int variant) { return variant == 1 ? 1 : super_step(K, ksplit_for(K, variant)); }
+
 int super_step(int K, int ksplit) {
     const int span = K / ksplit;
     if (span % 512 == 0) return 4;
@@ -780,6 +783,199 @@ static hipError_t launch_one(const GemmArgs& a, int SS, int ss2, dim3 grid, hipS
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// many picks per expert ("prefill"): an LDS-tiled grouped GEMM.  A workgroup (4 waves, 2 x 2)
+// owns one tile of up to 128 / NT picks (128 MFMA columns) and one block of 128 weight rows: for
+// gate/up the same 64 row indices of gate and of up (so SwiGLU needs no exchange), for down 128
+// rows.  K advances 128 at a time through double-buffered LDS: while the MFMAs of step s read
+// buffer s % 2, the global loads of step s + 1 are in flight.  Wave (wm, wn) computes 64 weight
+// rows x 64 columns (16 MFMAs per step).  Activations use the super-step-1 layout (one 128-byte
+// chunk per column per step).  Workgroups are spread over the 8 XCDs by tile range, with the row
+// block fastest, so one XCD's L2 serves a tile's activations to all its row blocks and the
+// tiles of one expert run together.
+// ---------------------------------------------------------------------------------------------
+constexpr int kPfRows = 128, kPfCols = 128, kPfBStride = 144;
+
+template <int NT, bool GATEUP>
+__global__ __launch_bounds__(256) void k_mx_pf(GemmArgs a, int ss2, int tiles_per_xcd_cap) {
+    __shared__ __align__(16) uint8_t lA[2][kPfRows][64];
+    __shared__ __align__(16) uint32_t lAs[2][kPfRows];
+    __shared__ __align__(16) uint8_t lB[2][kPfCols * kPfBStride];
+    __shared__ __align__(16) uint32_t lBs[2][kPfCols];
+    constexpr int TT = kPfCols / NT;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int K = GATEUP ? a.d : a.f;
+    const int MT = GATEUP ? a.f / 64 : a.d / 128;       // row blocks per tile
+    // workgroup -> (tile, row block): XCD x = id % 8 takes tiles [x * TPX, (x + 1) * TPX)
+    const int nt = *a.ntiles;
+    const int g = blockIdx.x, xcd = g & 7, sidx = g >> 3;
+    const int mblk = sidx % MT, tq = sidx / MT;
+    const int TPX = (nt + 7) >> 3;
+    if (tq >= TPX || tq >= tiles_per_xcd_cap) return;
+    const int tile = xcd * TPX + tq;
+    if (tile >= nt) return;
+    const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
+    const int ntok = min(TT, a.offsets[e + 1] - i0);
+    const moe_expert ex = a.table[e];
+
+    // staging sources: A rows (2 chunks per thread), A scales (threads < 128), B columns (4 chunks
+    // per thread), B scales (threads < 128); columns past the tile re-read its first column
+    auto a_row_ptr = [&](int r, bool scale) -> const uint8_t* {
+        int mr;
+        const uint8_t* base;
+        if (GATEUP) {
+            mr = mblk * 64 + (r & 63);
+            base = (r < 64) ? (scale ? ex.gate_s : ex.gate_q) : (scale ? ex.up_s : ex.up_q);
+        } else {
+            mr = mblk * 128 + r;
+            base = scale ? ex.down_s : ex.down_q;
+        }
+        return base + (size_t)mr * (scale ? K / 32 : K / 2);
+    };
+    auto b_col_ptr = [&](int c, bool scale) -> const uint8_t* {
+        const int tc = c / NT, t = c % NT;
+        const int tcc = tc < ntok ? tc : 0;
+        const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tcc] / a.k) : (size_t)(i0 + tcc);
+        return scale ? a.as + (arow * NT + t) * (size_t)(K / 32) : a.aq + (arow * NT + t) * (size_t)K;
+    };
+    const uint8_t* srcA[2];
+    int dstA[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = i * 256 + tid, r = q >> 2, part = q & 3;
+        srcA[i] = a_row_ptr(r, false) + part * 16;
+        dstA[i] = r * 64 + part * 16;
+    }
+    const uint8_t* srcB[4];
+    int dstB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = i * 256 + tid, c = q >> 3, part = q & 7;
+        srcB[i] = b_col_ptr(c, false) + part * 16;
+        dstB[i] = c * kPfBStride + part * 16;
+    }
+    const int sr = tid & 127;
+    const uint8_t* srcS = (tid < 128) ? a_row_ptr(sr, true) : b_col_ptr(sr, true);
+
+    uint4 vA[2], vB[4];
+    uint32_t vS;
+    auto load_step = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) vA[i] = gload16(srcA[i] + (size_t)st * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vB[i] = gload16(srcB[i] + (size_t)st * 128);
+        vS = gload4(srcS + (size_t)st * 4);
+    };
+    auto store_step = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *(uint4*)(&lA[buf][0][0] + dstA[i]) = vA[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(uint4*)(&lB[buf][0] + dstB[i]) = vB[i];
+        if (tid < 128) lAs[buf][sr] = vS;
+        else lBs[buf][sr] = vS;
+    };
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[f][n] = v4f{0.f, 0.f, 0.f, 0.f};
+    // this wave's A fragments (LDS rows) and B fragments (LDS columns)
+    int arow[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+        arow[f] = GATEUP ? ((f >> 1) * 64 + wm * 32 + (f & 1) * 16 + li) : (wm * 64 + f * 16 + li);
+    const int nsteps = K / 128;
+    load_step(0);
+    store_step(0);
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nsteps) load_step(st + 1);
+        uint4 A[4];
+        uint32_t sa[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            A[f] = *(const uint4*)&lA[buf][arow[f]][lg * 16];
+            sa[f] = (lAs[buf][arow[f]] >> (8 * lg)) & 0xffu;
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int col = wn * 64 + n * 16 + li;
+            const uint8_t* bp = &lB[buf][col * kPfBStride + lg * 32];
+            const uint4 b0 = *(const uint4*)bp, b1 = *(const uint4*)(bp + 16);
+            const int sb = (int)((lBs[buf][col] >> (8 * lg)) & 0xffu);
+#pragma unroll
+            for (int f = 0; f < 4; ++f) acc[f][n] = mfma_fp4_fp8(A[f], b0, b1, acc[f][n], (int)sa[f], sb);
+        }
+        if (st + 1 < nsteps) store_step(buf ^ 1);
+        __syncthreads();
+    }
+
+    // columns: n * 16 + li of this wave's 64 = (pick tc, term t)
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[f][n][r] = sum_adjacent<NT>(acc[f][n][r]);
+    const int t = li % NT;
+    if constexpr (GATEUP) {
+        // h = silu(g) u for the wave's 32 row indices (one natural block of h), split into NT
+        // terms with one exponent per term and block
+        const int rg = (mblk * 64 + wm * 32) / 32;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            float v[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                v[r] = silu(acc[0][n][r]) * acc[2][n][r];
+                v[4 + r] = silu(acc[1][n][r]) * acc[3][n][r];
+            }
+            uint32_t codes[NT][2];
+            int S[NT];
+            split_terms<NT>(v, codes, S, [](float mm) { return max_xor32(max_xor16(mm)); });
+            const int tc = (wn * 64 + n * 16 + li) / NT;
+            if (tc < ntok) {
+                const size_t pos = (size_t)i0 + tc;
+                uint32_t w0 = codes[0][0], w1 = codes[0][1];
+                int Sme = S[0];
+#pragma unroll
+                for (int q = 1; q < NT; ++q)
+                    if (q == t) { w0 = codes[q][0]; w1 = codes[q][1]; Sme = S[q]; }
+                uint8_t* dst = a.hq + (pos * NT + t) * (size_t)a.f;
+                *(uint32_t*)(dst + act_half_offset(ss2, rg, 0) + 4 * lg) = w0;
+                *(uint32_t*)(dst + act_half_offset(ss2, rg, 1) + 4 * lg) = w1;
+                if (lg == 0) a.hs[(pos * NT + t) * (size_t)(a.f / 32) + rg] = (uint8_t)(Sme + 127);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int tc = (wn * 64 + n * 16 + li) / NT;
+            if (tc < ntok && t == 0) {
+                float* dst = a.o + ((size_t)i0 + tc) * a.d + mblk * 128 + wm * 64 + 4 * lg;
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    *(float4*)(dst + 16 * f) = make_float4(acc[f][n][0], acc[f][n][1], acc[f][n][2], acc[f][n][3]);
+            }
+        }
+    }
+}
+
+template <bool GATEUP>
+static hipError_t launch_pf(const GemmArgs& a, int NT, int max_tiles, hipStream_t st) {
+    const int MT = GATEUP ? a.f / 64 : a.d / 128;
+    const int cap = (max_tiles + 7) / 8;
+    dim3 grid((unsigned)(8 * cap * MT));
+    if (NT == 2) MOE_LAUNCH((k_mx_pf<2, GATEUP>), grid, dim3(256), 0, st, a, 1, cap);
+    else MOE_LAUNCH((k_mx_pf<4, GATEUP>), grid, dim3(256), 0, st, a, 1, cap);
+    return hipGetLastError();
+}
+
 template <bool GATEUP>
 static hipError_t launch_gemm(const GemmArgs& a, int NT, int variant, int max_tiles, hipStream_t st) {
     const int K = GATEUP ? a.d : a.f;
@@ -794,8 +990,7 @@ static hipError_t launch_gemm(const GemmArgs& a, int NT, int variant, int max_ti
         return NT == 2 ? launch_one<GATEUP, 2, 1, 1>(a, SS, ss2, grid, st)
                        : launch_one<GATEUP, 4, 1, 1>(a, SS, ss2, grid, st);
     }
-    return NT == 2 ? launch_one<GATEUP, 2, 8, 1>(a, SS, ss2, grid, st)
-                   : launch_one<GATEUP, 4, 8, 1>(a, SS, ss2, grid, st);
+    return launch_pf<GATEUP>(a, NT, max_tiles, st);
 }
 
 hipError_t launch_gemm_gateup(const GemmArgs& a, int NT, int variant, int max_tiles, hipStream_t st) {

@@ -329,6 +329,7 @@ struct WsLayout {
 int act_terms(const moe_shape* s);
 int logits_splits(const moe_shape* s, int T);   // K slices of the tiled router (1 for T <= 8)
 int super_step(int K, int ksplit);
+int act_super_step(int K, int variant);
 WsLayout ws_layout(const moe_shape* s, int32_t T);
 
 hipError_t launch_router_logits(const moe_shape* s, const void* x, int T, const float* wr,
