@@ -143,7 +143,7 @@ static GemmArgs gemm_args(const moe_shape* s, const moe_expert* table, int32_t T
 static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const void* x, int32_t T,
                              const int32_t* offsets, const int32_t* sorted_pick, float* o, uint8_t* ws,
                              const WsLayout& L, void* staging, hipStream_t st) {
-    const int tt = kNvTilePicks;
+    const int tt = nv_tile_picks(s, T);
     int32_t* tiles = (int32_t*)(ws + L.tiles);
     int32_t* ntiles = (int32_t*)(ws + L.ntiles);
     MOE_HIP(launch_plan(s, offsets, tt, tiles, ntiles, st));
@@ -154,9 +154,9 @@ static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const 
     const uint8_t* xin = bf ? (const uint8_t*)x : ws + L.xq;
     if (!staging) {
         a.aq = xin;
-        MOE_HIP(launch_nv_gemm(a, true, NT, L.max_tiles, st));
+        MOE_HIP(launch_nv_gemm(a, true, NT, tt, L.max_tiles, st));
         a.aq = ws + L.hq;
-        MOE_HIP(launch_nv_gemm(a, false, 2, L.max_tiles, st));
+        MOE_HIP(launch_nv_gemm(a, false, 2, tt, L.max_tiles, st));
         return MOE_OK;
     }
     int32_t* list = (int32_t*)(ws + L.stage_list);
@@ -173,9 +173,9 @@ static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const 
         MOE_HIP(launch_gather_group(s, table, list, nlist, g, (uint8_t*)staging, stride, staged, st));
         a.tile_range = ranges + 2 * g;
         a.aq = xin;
-        MOE_HIP(launch_nv_gemm(a, true, NT, L.max_tiles, st));
+        MOE_HIP(launch_nv_gemm(a, true, NT, tt, L.max_tiles, st));
         a.aq = ws + L.hq;
-        MOE_HIP(launch_nv_gemm(a, false, 2, L.max_tiles, st));
+        MOE_HIP(launch_nv_gemm(a, false, 2, tt, L.max_tiles, st));
     }
     return MOE_OK;
 }

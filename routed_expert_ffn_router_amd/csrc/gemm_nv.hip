@@ -26,7 +26,6 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float v4f_nv __attribute__((ext_vector_type(4)));
 
-constexpr int kNvTileTokens = 8;     // picks per tile: 16 MFMA columns of (pick, term)
 
 // 8 codes (one dword, element 2i in the low nibble of byte i) x block scale -> 8 bf16.  The
 // conversion unit's scale operand acts as a power of two only, so codes are converted at scale 1
@@ -80,12 +79,13 @@ hipError_t launch_bf16_terms(const float* x, int rows, int K, uint16_t* terms, h
     return hipGetLastError();
 }
 
-// NT: bf16 terms per activation (1: bf16 x read in place; 2: hi/lo terms).  GATEUP: the gate and
-// up rows of one 32-row block, SwiGLU, and h as two bf16 terms; else the down rows, o in fp32.
-template <int NT, bool GATEUP>
+// NT: bf16 terms per activation (1: bf16 x read in place; 2: hi/lo terms); TTP: picks per tile
+// (MFMA columns = TTP * NT, in NCF 16-column fragments).  GATEUP: the gate and up rows of one
+// 32-row block, SwiGLU, and h as two bf16 terms; else the down rows, o in fp32.
+template <int NT, bool GATEUP, int TTP>
 __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
     constexpr int NA = GATEUP ? 4 : 2;      // 16-row fragments: gate lo/hi, up lo/hi (or down lo/hi)
-    constexpr int TT = kNvTileTokens;
+    constexpr int NCF = (TTP * NT + 15) / 16;
     const int tile = blockIdx.x;
     int t0 = 0, t1 = *a.ntiles;
     if (a.tile_range) {
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
     }
     if (tile < t0 || tile >= t1) return;
     const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
-    const int ntok = min(TT, a.offsets[e + 1] - i0);
+    const int ntok = min(TTP, a.offsets[e + 1] - i0);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int K = GATEUP ? a.d : a.f;
@@ -115,17 +115,22 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
         aq[f] = mq + (size_t)row * (K / 2) + (size_t)s0 * 64 + lg * 16;
         as[f] = ms + (size_t)row * (K / 16) + (size_t)s0 * 8 + lg * 2;
     }
-    // activations: column li = (pick tc, term t); columns past the tile read the tile's first
-    // pick (their results are not used)
-    const int tc = li / NT, t = li % NT;
-    const bool valid = tc < ntok;
-    const int tcc = valid ? tc : 0;
-    const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tcc] / a.k) : (size_t)(i0 + tcc);
-    const uint16_t* bp = (const uint16_t*)a.aq + (arow * NT + t) * (size_t)K + (size_t)s0 * 128 + lg * 32;
-
-    v4f_nv acc[NA];
+    // activations: column n * 16 + li = (pick tc, term t); columns past the tile read the tile's
+    // first pick (their results are not used)
+    const uint16_t* bp[NCF];
 #pragma unroll
-    for (int f = 0; f < NA; ++f) acc[f] = v4f_nv{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NCF; ++n) {
+        const int c = n * 16 + li, tc = c / NT, t = c % NT;
+        const int tcc = tc < ntok ? tc : 0;
+        const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tcc] / a.k) : (size_t)(i0 + tcc);
+        bp[n] = (const uint16_t*)a.aq + (arow * NT + t) * (size_t)K + (size_t)s0 * 128 + lg * 32;
+    }
+
+    v4f_nv acc[NA][NCF];
+#pragma unroll
+    for (int f = 0; f < NA; ++f)
+#pragma unroll
+        for (int n = 0; n < NCF; ++n) acc[f][n] = v4f_nv{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < nss; ++s) {
         uint4 A[NA];
         uint32_t sc[NA];
@@ -134,26 +139,33 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
             A[f] = *(const uint4*)(aq[f] + (size_t)s * 64);
             sc[f] = *(const uint16_t*)(as[f] + (size_t)s * 8);
         }
-        uint4 B[4];
+        uint4 B[NCF][4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) B[h] = *(const uint4*)(bp + (size_t)s * 128 + 8 * h);
+        for (int n = 0; n < NCF; ++n)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) B[n][h] = *(const uint4*)(bp[n] + (size_t)s * 128 + 8 * h);
 #pragma unroll
         for (int f = 0; f < NA; ++f) {
             const v2f_t bs = e4m3x2_to_f32(sc[f]);
             const uint32_t w[4] = {A[f].x, A[f].y, A[f].z, A[f].w};
 #pragma unroll
-            for (int h = 0; h < 4; ++h)
-                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nv_dequant8(w[h], h < 2 ? bs[0] : bs[1]),
-                                                                 as_bf16x8(B[h]), acc[f], 0, 0, 0);
+            for (int h = 0; h < 4; ++h) {
+                const bf16x8_t af = nv_dequant8(w[h], h < 2 ? bs[0] : bs[1]);
+#pragma unroll
+                for (int n = 0; n < NCF; ++n)
+                    acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, as_bf16x8(B[n][h]), acc[f][n], 0, 0, 0);
+            }
         }
     }
     // K quarters summed through LDS in wave order
-    __shared__ float red[3][NA * 4][64];
+    __shared__ float red[3][NA * NCF * 4][64];
     if (wave > 0) {
 #pragma unroll
         for (int f = 0; f < NA; ++f)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave - 1][f * 4 + r][lane] = acc[f][r];
+            for (int n = 0; n < NCF; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[wave - 1][(f * NCF + n) * 4 + r][lane] = acc[f][n][r];
     }
     __syncthreads();
     if (wave > 0) return;
@@ -162,51 +174,68 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
 #pragma unroll
         for (int f = 0; f < NA; ++f)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[f][r] += red[w][f * 4 + r][lane];
+            for (int n = 0; n < NCF; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[f][n][r] += red[w][(f * NCF + n) * 4 + r][lane];
     if constexpr (NT == 2) {
 #pragma unroll
         for (int f = 0; f < NA; ++f)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[f][r] = sum_adjacent<2>(acc[f][r]);
+            for (int n = 0; n < NCF; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[f][n][r] = sum_adjacent<2>(acc[f][n][r]);
     }
-    if (!valid || t != 0) return;
-    const size_t pos = (size_t)i0 + tc;
-    if constexpr (GATEUP) {
-        // h = silu(g) u for rows T0 + 4 lg + r (f = 0) and T0 + 16 + 4 lg + r (f = 1), as two
-        // bf16 terms [P][2][f]
-        uint16_t* hb = (uint16_t*)a.hq + pos * 2 * (size_t)a.f;
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+    for (int n = 0; n < NCF; ++n) {
+        const int c = n * 16 + li, tc = c / NT, t = c % NT;
+        if (tc >= ntok || t != 0) continue;
+        const size_t pos = (size_t)i0 + tc;
+        if constexpr (GATEUP) {
+            // h = silu(g) u for rows T0 + 4 lg + r (half 0) and T0 + 16 + 4 lg + r (half 1), as two
+            // bf16 terms [P][2][f]
+            uint16_t* hb = (uint16_t*)a.hq + pos * 2 * (size_t)a.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float g = acc[half][r] * ex.gate_ts, u = acc[2 + half][r] * ex.up_ts;
-                const float hv = g / (1.0f + __expf(-g)) * u;
-                const uint16_t hi = bf16_rne(hv);
-                const uint16_t lo = bf16_rne(hv - bf16_bits_to_f32(hi));
-                const int row = T0 + 16 * half + 4 * lg + r;
-                hb[row] = hi;
-                hb[a.f + row] = lo;
-            }
-    } else {
-        float* dst = a.o + pos * (size_t)a.d + T0 + 4 * lg;
-        *(float4*)dst = make_float4(acc[0][0] * ex.down_ts, acc[0][1] * ex.down_ts, acc[0][2] * ex.down_ts,
-                                    acc[0][3] * ex.down_ts);
-        *(float4*)(dst + 16) = make_float4(acc[1][0] * ex.down_ts, acc[1][1] * ex.down_ts,
-                                           acc[1][2] * ex.down_ts, acc[1][3] * ex.down_ts);
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float g = acc[half][n][r] * ex.gate_ts, u = acc[2 + half][n][r] * ex.up_ts;
+                    const float hv = g / (1.0f + __expf(-g)) * u;
+                    const uint16_t hi = bf16_rne(hv);
+                    const uint16_t lo = bf16_rne(hv - bf16_bits_to_f32(hi));
+                    const int row = T0 + 16 * half + 4 * lg + r;
+                    hb[row] = hi;
+                    hb[a.f + row] = lo;
+                }
+        } else {
+            float* dst = a.o + pos * (size_t)a.d + T0 + 4 * lg;
+            *(float4*)dst = make_float4(acc[0][n][0] * ex.down_ts, acc[0][n][1] * ex.down_ts,
+                                        acc[0][n][2] * ex.down_ts, acc[0][n][3] * ex.down_ts);
+            *(float4*)(dst + 16) = make_float4(acc[1][n][0] * ex.down_ts, acc[1][n][1] * ex.down_ts,
+                                               acc[1][n][2] * ex.down_ts, acc[1][n][3] * ex.down_ts);
+        }
     }
 }
 
-hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int max_tiles, hipStream_t st) {
+int nv_tile_picks(const moe_shape* s, int T) {
+    return (long long)T * s->top_k > 8LL * s->n_experts ? kNvTilePicksMany : kNvTilePicks;
+}
+
+hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int tile_picks, int max_tiles, hipStream_t st) {
     const char* name = gateup ? "gemm_gate_up" : "gemm_down";
     trace(name, 0, st);
     const int rows = gateup ? a.f : a.d;
     dim3 grid(max_tiles, rows / 32);
-    if (gateup) {
-        if (NT == 1) MOE_LAUNCH((k_nv_gemm<1, true>), grid, dim3(256), 0, st, a);
-        else MOE_LAUNCH((k_nv_gemm<2, true>), grid, dim3(256), 0, st, a);
+#define MOE_NV(N, G, P) MOE_LAUNCH((k_nv_gemm<N, G, P>), grid, dim3(256), 0, st, a)
+    if (tile_picks == kNvTilePicksMany) {
+        if (!gateup) MOE_NV(2, false, kNvTilePicksMany);
+        else if (NT == 1) MOE_NV(1, true, kNvTilePicksMany);
+        else MOE_NV(2, true, kNvTilePicksMany);
     } else {
-        MOE_LAUNCH((k_nv_gemm<2, false>), grid, dim3(256), 0, st, a);
+        if (!gateup) MOE_NV(2, false, kNvTilePicks);
+        else if (NT == 1) MOE_NV(1, true, kNvTilePicks);
+        else MOE_NV(2, true, kNvTilePicks);
     }
+#undef MOE_NV
     trace(name, 1, st);
     return hipGetLastError();
 }

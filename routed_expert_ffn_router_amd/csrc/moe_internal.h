@@ -414,10 +414,13 @@ hipError_t launch_gateup_dec(const GemmArgs& a, int NT, int max_tiles, hipStream
 hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineArgs& c, int NT, hipStream_t st);
 
 // NVFP4 (gemm_nv.hip): bf16 terms of fp32 activations, and the grouped GEMMs
-constexpr int kNvTilePicks = 8;
+constexpr int kNvTilePicks = 8;          // few picks per expert
+constexpr int kNvTilePicksMany = 32;     // many picks per expert: fewer re-reads of the weights
+int nv_tile_picks(const moe_shape* s, int T);
 constexpr int kStageGroup = 64;           // experts staged per group (NVFP4 layer with staging)
 hipError_t launch_bf16_terms(const float* x, int rows, int K, uint16_t* terms, hipStream_t st);
-hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int max_tiles, hipStream_t st);
+hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int tile_picks, int max_tiles,
+                          hipStream_t st);
 // the distinct experts of a plan, in groups of kStageGroup, with each group's tile range
 hipError_t launch_stage_plan(const moe_shape* s, const int32_t* offsets, int tt, const int32_t* ntiles,
                              int32_t* list, int32_t* nlist, int32_t* ranges, hipStream_t st);
