@@ -26,19 +26,6 @@ namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-// loads through global-address-space pointers: global_load rather than flat_load (pointers read
-// from memory are generic otherwise, and a flat load also holds up LDS waits)
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 gload16(const void* p) {
-    const u32x4_t v = *(__attribute__((address_space(1))) const u32x4_t*)p;
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint32_t gload4(const void* p) {
-    return *(__attribute__((address_space(1))) const uint32_t*)p;
-}
-__device__ __forceinline__ int32_t gload_i32(const void* p) {
-    return *(__attribute__((address_space(1))) const int32_t*)p;
-}
 
 template <int SS>
 __device__ __forceinline__ uint32_t load_scale_word(const uint8_t* p) {

@@ -216,6 +216,176 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
     }
 }
 
+// Many picks per expert: an LDS-tiled version.  A workgroup (4 waves, 2 x 2) owns one tile of up
+// to kNvTilePicksMany picks (64 * NT columns) and 128 weight rows (gate/up: the same 64 row indices
+// of gate and up).  K advances 128 at a time through double-buffered LDS: the global loads of step
+// s + 1 are in flight while step s computes.  Each wave decodes its four 16-row weight fragments
+// once per step (32 bf16 per lane each) and runs them against every column fragment of its half
+// of the tile.  Workgroups are spread over the 8 XCDs by tile range, row block fastest.
+constexpr int kNvPfRows = 128, kNvPfBStride = 272;   // bf16 column: 256 bytes per step + pad
+
+template <int NT, bool GATEUP>
+__global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap) {
+    constexpr int BN = kNvTilePicksMany * NT;       // columns of the tile
+    constexpr int NCF = BN / 32;                     // column fragments per wave (half the tile)
+    __shared__ __align__(16) uint8_t lA[2][kNvPfRows][64];
+    __shared__ __align__(16) uint8_t lAs[2][kNvPfRows][8];
+    __shared__ __align__(16) uint8_t lB[2][BN * kNvPfBStride];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int K = GATEUP ? a.d : a.f;
+    const int MT = GATEUP ? a.f / 64 : a.d / 128;
+    int t_lo = 0, t_hi = *a.ntiles;
+    if (a.tile_range) {
+        t_lo = a.tile_range[0];
+        t_hi = a.tile_range[1];
+    }
+    const int nt = t_hi - t_lo;
+    const int g = blockIdx.x, xcd = g & 7, sidx = g >> 3;
+    const int mblk = sidx % MT, tq = sidx / MT;
+    const int TPX = (nt + 7) >> 3;
+    if (nt <= 0 || tq >= TPX || tq >= tiles_per_xcd_cap) return;
+    const int tile = t_lo + xcd * TPX + tq;
+    if (tile >= t_hi) return;
+    const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
+    const int ntok = min(kNvTilePicksMany, a.offsets[e + 1] - i0);
+    const moe_expert ex = a.table[e];
+
+    auto a_row = [&](int r, bool scale) -> const uint8_t* {
+        int mr;
+        const uint8_t* base;
+        if (GATEUP) {
+            mr = mblk * 64 + (r & 63);
+            base = (r < 64) ? (scale ? ex.gate_s : ex.gate_q) : (scale ? ex.up_s : ex.up_q);
+        } else {
+            mr = mblk * 128 + r;
+            base = scale ? ex.down_s : ex.down_q;
+        }
+        return base + (size_t)mr * (scale ? K / 16 : K / 2);
+    };
+    auto b_col = [&](int c) -> const uint8_t* {
+        const int tc = c / NT, t = c % NT;
+        const int tcc = tc < ntok ? tc : 0;
+        const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tcc] / a.k) : (size_t)(i0 + tcc);
+        return a.aq + (arow * NT + t) * (size_t)K * 2;
+    };
+    // staging: A codes (2 chunks per thread), A scales (threads < 64: 16 bytes = two rows' 8),
+    // B (BN * 16 chunks of 16 bytes: BN / 16 per thread)
+    constexpr int NBC = BN * 16 / 256;
+    const uint8_t* srcA[2];
+    int dstA[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = i * 256 + tid, r = q >> 2, part = q & 3;
+        srcA[i] = a_row(r, false) + part * 16;
+        dstA[i] = r * 64 + part * 16;
+    }
+    const int sq = tid & 63;
+    const uint8_t* srcS0 = a_row(2 * sq, true);
+    const uint8_t* srcS1 = a_row(2 * sq + 1, true);
+    const uint8_t* srcB[NBC];
+    int dstB[NBC];
+#pragma unroll
+    for (int i = 0; i < NBC; ++i) {
+        const int q = i * 256 + tid, c = q >> 4, part = q & 15;
+        srcB[i] = b_col(c) + part * 16;
+        dstB[i] = c * kNvPfBStride + part * 16;
+    }
+    uint4 vA[2], vB[NBC];
+    uint2 vS0, vS1;
+    auto load_step = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) vA[i] = gload16(srcA[i] + (size_t)st * 64);
+        vS0 = *(const uint2*)(srcS0 + (size_t)st * 8);
+        vS1 = *(const uint2*)(srcS1 + (size_t)st * 8);
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) vB[i] = gload16(srcB[i] + (size_t)st * 256);
+    };
+    auto store_step = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *(uint4*)(&lA[buf][0][0] + dstA[i]) = vA[i];
+        if (tid < 64) {
+            *(uint2*)&lAs[buf][2 * sq][0] = vS0;
+            *(uint2*)&lAs[buf][2 * sq + 1][0] = vS1;
+        }
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) *(uint4*)(&lB[buf][0] + dstB[i]) = vB[i];
+    };
+
+    int arow[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+        arow[f] = GATEUP ? ((f >> 1) * 64 + wm * 32 + (f & 1) * 16 + li) : (wm * 64 + f * 16 + li);
+    v4f_nv acc[4][NCF];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int n = 0; n < NCF; ++n) acc[f][n] = v4f_nv{0.f, 0.f, 0.f, 0.f};
+    const int nsteps = K / 128;
+    load_step(0);
+    store_step(0);
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nsteps) load_step(st + 1);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const uint4 codes = *(const uint4*)&lA[buf][arow[f]][lg * 16];
+            const v2f_t bs = e4m3x2_to_f32(*(const uint16_t*)&lAs[buf][arow[f]][2 * lg]);
+            const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const bf16x8_t af = nv_dequant8(w[h], h < 2 ? bs[0] : bs[1]);
+#pragma unroll
+                for (int n = 0; n < NCF; ++n) {
+                    const int col = wn * (BN / 2) + n * 16 + li;
+                    const uint4 bv = *(const uint4*)&lB[buf][col * kNvPfBStride + (lg * 32 + 8 * h) * 2];
+                    acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, as_bf16x8(bv), acc[f][n], 0, 0, 0);
+                }
+            }
+        }
+        if (st + 1 < nsteps) store_step(buf ^ 1);
+        __syncthreads();
+    }
+    if constexpr (NT == 2) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int n = 0; n < NCF; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[f][n][r] = sum_adjacent<2>(acc[f][n][r]);
+    }
+#pragma unroll
+    for (int n = 0; n < NCF; ++n) {
+        const int c = wn * (BN / 2) + n * 16 + li, tc = c / NT, t = c % NT;
+        if (tc >= ntok || t != 0) continue;
+        const size_t pos = (size_t)i0 + tc;
+        if constexpr (GATEUP) {
+            uint16_t* hb = (uint16_t*)a.hq + pos * 2 * (size_t)a.f;
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float gv = acc[half][n][r] * ex.gate_ts, uv = acc[2 + half][n][r] * ex.up_ts;
+                    const float hv = gv / (1.0f + __expf(-gv)) * uv;
+                    const uint16_t hi = bf16_rne(hv);
+                    const uint16_t lo = bf16_rne(hv - bf16_bits_to_f32(hi));
+                    const int row = mblk * 64 + wm * 32 + 16 * half + 4 * lg + r;
+                    hb[row] = hi;
+                    hb[a.f + row] = lo;
+                }
+        } else {
+            float* dst = a.o + pos * (size_t)a.d + mblk * 128 + wm * 64 + 4 * lg;
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+                *(float4*)(dst + 16 * f) = make_float4(acc[f][n][0] * ex.down_ts, acc[f][n][1] * ex.down_ts,
+                                                       acc[f][n][2] * ex.down_ts, acc[f][n][3] * ex.down_ts);
+        }
+    }
+}
+
 int nv_tile_picks(const moe_shape* s, int T) {
     return (long long)T * s->top_k > 8LL * s->n_experts ? kNvTilePicksMany : kNvTilePicks;
 }
@@ -227,9 +397,12 @@ hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int tile_picks
     dim3 grid(max_tiles, rows / 32);
 #define MOE_NV(N, G, P) MOE_LAUNCH((k_nv_gemm<N, G, P>), grid, dim3(256), 0, st, a)
     if (tile_picks == kNvTilePicksMany) {
-        if (!gateup) MOE_NV(2, false, kNvTilePicksMany);
-        else if (NT == 1) MOE_NV(1, true, kNvTilePicksMany);
-        else MOE_NV(2, true, kNvTilePicksMany);
+        const int MT = gateup ? a.f / 64 : a.d / 128;
+        const int cap = (max_tiles + 7) / 8;
+        dim3 g2((unsigned)(8 * cap * MT));
+        if (!gateup) MOE_LAUNCH((k_nv_pf<2, false>), g2, dim3(256), 0, st, a, cap);
+        else if (NT == 1) MOE_LAUNCH((k_nv_pf<1, true>), g2, dim3(256), 0, st, a, cap);
+        else MOE_LAUNCH((k_nv_pf<2, true>), g2, dim3(256), 0, st, a, cap);
     } else {
         if (!gateup) MOE_NV(2, false, kNvTilePicks);
         else if (NT == 1) MOE_NV(1, true, kNvTilePicks);

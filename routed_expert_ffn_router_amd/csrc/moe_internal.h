@@ -103,6 +103,20 @@ __device__ __forceinline__ float sum_adjacent(float v) {
     return v;
 }
 
+// loads through global-address-space pointers: global_load rather than flat_load (pointers read
+// from memory are generic otherwise, and a flat load also holds up LDS waits)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(const void* p) {
+    const u32x4_t v = *(__attribute__((address_space(1))) const u32x4_t*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t gload4(const void* p) {
+    return *(__attribute__((address_space(1))) const uint32_t*)p;
+}
+__device__ __forceinline__ int32_t gload_i32(const void* p) {
+    return *(__attribute__((address_space(1))) const int32_t*)p;
+}
+
 // ---------------------------------------------------------------------------------------------
 // element formats (device side)
 // ---------------------------------------------------------------------------------------------
@@ -415,7 +429,7 @@ hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineA
 
 // NVFP4 (gemm_nv.hip): bf16 terms of fp32 activations, and the grouped GEMMs
 constexpr int kNvTilePicks = 8;          // few picks per expert
-constexpr int kNvTilePicksMany = 32;     // many picks per expert: fewer re-reads of the weights
+constexpr int kNvTilePicksMany = 64;     // many picks per expert: the LDS-tiled GEMM's tile
 int nv_tile_picks(const moe_shape* s, int T);
 constexpr int kStageGroup = 64;           // experts staged per group (NVFP4 layer with staging)
 hipError_t launch_bf16_terms(const float* x, int rows, int K, uint16_t* terms, hipStream_t st);
