@@ -254,11 +254,20 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
     const double* l = logits + (size_t)t * E;
     double lv[S];
     topk_load<S>(l, E, lv);
-    for (int z = 1; z < nsplit; ++z) {
-        double pz[S];
-        topk_load<S>(l + (size_t)z * T * E, E, pz);
+    // slices 1.. in groups of 4: a group's loads are all in flight before its sums, in order
+    for (int z0 = 1; z0 < nsplit; z0 += 4) {
+        double pz[4][S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) lv[s] += pz[s];
+        for (int j = 0; j < 4; ++j) {
+            const int z = z0 + j < nsplit ? z0 + j : z0;     // past the end: re-read, not added
+            topk_load<S>(l + (size_t)z * T * E, E, pz[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (z0 + j < nsplit) {
+#pragma unroll
+                for (int s = 0; s < S; ++s) lv[s] += pz[j][s];
+            }
     }
     if (nsplit > 1 && k > 64) {
         // the weights of picks past 64 re-read l[idx]: store the summed logits over slice 0

@@ -196,9 +196,9 @@ def glm_layer():
 
 
 # T=1 and 2: few-token kernels with the h terms staged in LDS; 5 and 16: the same gate/up kernel
-# with the down kernel reading h from memory (and tiles of several picks of one expert); 64: the
-# general grouped path
-@pytest.mark.parametrize("T", [1, 2, 5, 16, 64])
+# with the down kernel reading h from memory (and tiles of several picks of one expert); 20, 48
+# and 64: the general path (matrix-core router, permute, grouped GEMMs, combine)
+@pytest.mark.parametrize("T", [1, 2, 5, 16, 20, 48, 64])
 def test_glm_decode_layer(glm_layer, T):
     dl = glm_layer
     wl = dl.wl
