@@ -46,8 +46,8 @@ template <typename XT>
 __global__ __launch_bounds__(256) void k_logits_mfma(const XT* __restrict__ x, int T, int d,
                                                       const float* __restrict__ wr, const float* __restrict__ bias,
                                                       int E, int kslice, double* __restrict__ part) {
-    __shared__ float xs[kLgTok][kLgK + 1];
-    __shared__ float ws[kLgExp][kLgK + 1];
+    __shared__ float xs[2][kLgTok][kLgK + 1];
+    __shared__ float ws[2][kLgExp][kLgK + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t0 = blockIdx.x * kLgTok, e0 = blockIdx.y * kLgExp, z = blockIdx.z;
     const int kb = z * kslice;
@@ -56,34 +56,52 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const XT* __restrict__ x, i
     const int tr = (wave & 1) * 16 + (lane & 15);        // A row (token) of this lane
     const int ec = (wave >> 1) * 32 + (lane & 15);       // B column (expert) of block 0
     const int kl = lane >> 4;
-    for (int k0 = kb; k0 < kb + kslice; k0 += kLgK) {
-        // stage: x tile 32 x 64 (8 per thread), Wr tile 64 x 64 (16 per thread); rows past the
-        // end re-read the last row (their results are not stored)
+    // staging: x 32 x 64 (8 consecutive per thread), Wr 64 x 64 (4 float4 per thread); rows past
+    // the end re-read the last row (their results are not stored)
+    const int xr = tid >> 3, xc = (tid & 7) * 8;
+    const XT* xsrc = x + (size_t)min(t0 + xr, T - 1) * d + kb + xc;
+    const float* wsrc[4];
+    int wrow[4], wcol[4];
 #pragma unroll
-        for (int i = 0; i < (kLgTok * kLgK) / 256; ++i) {
-            const int q = i * 256 + tid, r = q / kLgK, c = q % kLgK;
-            const int t = min(t0 + r, T - 1);
-            xs[r][c] = load_act(x, (size_t)t * d + k0 + c);
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int q = i * 256 + tid;
+        wrow[i] = q >> 4;
+        wcol[i] = (q & 15) * 4;
+        wsrc[i] = wr + (size_t)min(e0 + wrow[i], E - 1) * d + kb + wcol[i];
+    }
+    float4 xv0, xv1, wv[4];
+    auto load_chunk = [&](int k0) {
+        xv0 = load_act4(xsrc + k0, 0);
+        xv1 = load_act4(xsrc + k0, 4);
 #pragma unroll
-        for (int i = 0; i < (kLgExp * kLgK) / 256 / 4; ++i) {
-            const int q = i * 256 + tid, r = q / (kLgK / 4), c = (q % (kLgK / 4)) * 4;
-            const int e = min(e0 + r, E - 1);
-            const float4 v = *(const float4*)(wr + (size_t)e * d + k0 + c);
-            ws[r][c] = v.x;
-            ws[r][c + 1] = v.y;
-            ws[r][c + 2] = v.z;
-            ws[r][c + 3] = v.w;
+        for (int i = 0; i < 4; ++i) wv[i] = *(const float4*)(wsrc[i] + k0);
+    };
+    auto store_chunk = [&](int buf) {
+        float* xd = &xs[buf][xr][xc];
+        xd[0] = xv0.x; xd[1] = xv0.y; xd[2] = xv0.z; xd[3] = xv0.w;
+        xd[4] = xv1.x; xd[5] = xv1.y; xd[6] = xv1.z; xd[7] = xv1.w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float* wd = &ws[buf][wrow[i]][wcol[i]];
+            wd[0] = wv[i].x; wd[1] = wv[i].y; wd[2] = wv[i].z; wd[3] = wv[i].w;
         }
-        __syncthreads();
+    };
+    const int nch = kslice / kLgK;
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+        const int buf = ch & 1;
+        if (ch + 1 < nch) load_chunk((ch + 1) * kLgK);
 #pragma unroll 4
         for (int kk = 0; kk < kLgK; kk += 4) {
-            const double a = (double)xs[tr][kk + kl];
-            const double b0 = (double)ws[ec][kk + kl];
-            const double b1 = (double)ws[ec + 16][kk + kl];
+            const double a = (double)xs[buf][tr][kk + kl];
+            const double b0 = (double)ws[buf][ec][kk + kl];
+            const double b1 = (double)ws[buf][ec + 16][kk + kl];
             acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b0, acc[0], 0, 0, 0);
             acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b1, acc[1], 0, 0, 0);
         }
+        if (ch + 1 < nch) store_chunk(buf ^ 1);
         __syncthreads();
     }
 #pragma unroll
@@ -503,17 +521,51 @@ hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipSt
 // ---------------------------------------------------------------------------------------------
 // activation split: 32 lanes per natural 32-element block of one row
 // ---------------------------------------------------------------------------------------------
+// Four consecutive elements per thread, eight lanes per block: the block maximum takes three DPP
+// steps (xor 1, xor 2, half-row mirror), each term's four codes are one dword.
 template <typename XT, int NT>
 __global__ __launch_bounds__(256) void k_act_split(const XT* __restrict__ x, int rows, int K, int SS,
                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
-    split_rows_lanewise<XT, NT>(x, rows, K, SS, q, sc, blockIdx.x, gridDim.x);
+    const size_t n4 = (size_t)rows * (K / 4);
+    const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;     // 4-element group
+    const bool ok = g < n4;                                      // uniform per 8-lane block
+    const size_t gg = ok ? g : 0;
+    const int row = (int)(gg / (K / 4)), c4 = (int)(gg % (K / 4));
+    const int blk = c4 >> 3, j = c4 & 7;                         // block, group within it
+    const float4 v4 = load_act4(x, (size_t)row * K + (size_t)c4 * 4);
+    float v[4] = {v4.x, v4.y, v4.z, v4.w};
+    const int groups = K / 32;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        m = fmaxf(m, __uint_as_float(dpp_u32<kDppXor1, 0xF>(__float_as_uint(m), __float_as_uint(m))));
+        m = fmaxf(m, __uint_as_float(dpp_u32<kDppXor2, 0xF>(__float_as_uint(m), __float_as_uint(m))));
+        m = fmaxf(m, __uint_as_float(dpp_u32<kDppHalfMirror, 0xF>(__float_as_uint(m), __float_as_uint(m))));
+        const int S = split_exponent(m);
+        const float scale = pow2f(S);
+        uint32_t w = fp8x2_encode<false>(0u, v[0], v[1], scale);
+        w = fp8x2_encode<true>(w, v[2], v[3], scale);
+        if (t + 1 < NT) {
+            const v2f_t lo = fp8x2_decode<false>(w, scale), hi = fp8x2_decode<true>(w, scale);
+            v[0] -= lo[0];
+            v[1] -= lo[1];
+            v[2] -= hi[0];
+            v[3] -= hi[1];
+        }
+        if (ok) {
+            uint8_t* base = q + ((size_t)row * NT + t) * K;
+            const int i = 4 * j;                                   // element index in the block
+            *(uint32_t*)(base + act_half_offset(SS, blk, i >> 4) + (i & 15)) = w;
+            if (j == 0) sc[((size_t)row * NT + t) * groups + blk] = (uint8_t)(S + 127);
+        }
+    }
 }
 
 hipError_t launch_act_split(const moe_shape* s, const void* x, int rows, int K, int SS, int NT,
                             uint8_t* q, uint8_t* sc, hipStream_t st) {
     trace("act_split", 0, st);
-    const size_t n = (size_t)rows * (K / 32);          // 32-element blocks, 8 per workgroup
-    dim3 grid((unsigned)((n + 7) / 8));
+    const size_t n = (size_t)rows * (K / 4);           // 4-element groups, one per thread
+    dim3 grid((unsigned)((n + 255) / 256));
     const bool bf = s->act_dtype == MOE_DT_BF16;
 #define MOE_SPLIT(XT, N)                                                                    \
     MOE_LAUNCH((k_act_split<XT, N>), grid, dim3(256), 0, st, (const XT*)x, rows, K, SS, q, sc)
