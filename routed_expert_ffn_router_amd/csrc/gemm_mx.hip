@@ -771,31 +771,120 @@ static hipError_t launch_one(const GemmArgs& a, int SS, int ss2, dim3 grid, hipS
 }
 
 // ---------------------------------------------------------------------------------------------
-// many picks per expert ("prefill"): an LDS-tiled grouped GEMM.  A workgroup (4 waves, 2 x 2)
-// owns one tile of up to 128 / NT picks (128 MFMA columns) and one block of 128 weight rows: for
-// gate/up the same 64 row indices of gate and of up (so SwiGLU needs no exchange), for down 128
-// rows.  K advances 128 at a time through double-buffered LDS: while the MFMAs of step s read
-// buffer s % 2, the global loads of step s + 1 are in flight.  Wave (wm, wn) computes 64 weight
-// rows x 64 columns (16 MFMAs per step).  Activations use the super-step-1 layout (one 128-byte
-// chunk per column per step).  Workgroups are spread over the 8 XCDs by tile range, with the row
-// block fastest, so one XCD's L2 serves a tile's activations to all its row blocks and the
-// tiles of one expert run together.
+// many picks per expert ("prefill"): an LDS-tiled grouped GEMM fed by direct global->LDS loads.
+// A workgroup (4 waves, 2 x 2) owns one tile of up to 128 / NT picks (128 MFMA columns) and one
+// block of 256 weight rows: for gate/up the same 128 row indices of gate and of up (so SwiGLU
+// needs no exchange), for down 256 rows.  K advances 128 at a time through a ring of four LDS
+// stages that global_load_lds fills (no register round trip) four steps before they are
+// consumed; the fragments of step s + 1 are read from LDS into a second register set while the
+// MFMAs of step s run.  Wave (wm, wn) computes 128 weight rows x 64 columns (32 MFMAs per step).
+//
+// The vector L1 serves a load one lane quad at a time, so every direct load has consecutive
+// lanes read consecutive bytes: 4 lanes per 64-byte weight-row chunk, 8 lanes per 128-byte
+// activation chunk.  In LDS a chunk keeps its row, with its 16-byte units XOR-swizzled so that
+// the MFMA fragment reads (16 rows or columns at one unit each) meet no bank conflict.  The
+// scale words (one per row and step) are loaded four steps at a time, consecutive lanes taking
+// consecutive words of a row, into a ring of two slots.  Workgroups are spread over the 8 XCDs
+// by tile range, with the row block fastest, so one XCD's L2 serves a tile's activations to all
+// its row blocks and the tiles of one expert run together.
+//
+// Stage layout (bytes): weight row r (0..255) at 64 r, its 16-byte part p in slot p ^ swz_a(r
+// % 16); activation column c (0..127) at 16384 + 128 c, unit u in slot u ^ swz_b(c % 16).
+// Scale slot layout: row r's words of steps 4m..4m+3 at 16 r + 4 (step % 4); column c's at
+// 4096 + 16 c.
 // ---------------------------------------------------------------------------------------------
-constexpr int kPfRows = 128, kPfCols = 128, kPfBStride = 144;
+constexpr int kPfRows = 256, kPfCols = 128;
+constexpr int kPfA = 0, kPfB = 16384, kPfStage = 32768;
+constexpr int kScA = 0, kScB = 4096, kScSlot = 6144;
+constexpr int kPfLoads = 8;                   // direct loads per wave and stage
+constexpr int kScLoads = 6;                   // direct loads per wave and group of four steps
+
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
+__device__ __forceinline__ int swz_b(int c) { return ((c >> 1) ^ ((c & 1) << 2)) & 7; }
+
+typedef const __attribute__((address_space(1))) void* dma_src_t;
+typedef __attribute__((address_space(3))) void* dma_dst_t;
+// lane l's 16 (4) bytes at src land at lds + 16 l (4 l); lds must be the same in every lane
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds((dma_src_t)src, (dma_dst_t)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds((dma_src_t)src, (dma_dst_t)lds, 4, 0, 0);
+}
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// workgroup barrier for the stage ring: this wave's LDS reads are complete and the compiler
+// moves no memory access across it.  Unlike __syncthreads it does not wait for this wave's
+// direct loads still in flight (they target other stages; each is waited for with wait_vm
+// before the barrier that publishes its stage).
+__device__ __forceinline__ void ring_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0), vmcnt and expcnt unchanged
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+struct PfFrags {
+    uint4 a[8];
+    uint4 b[4][2];
+    int sa[8];
+    int sb[4];
+};
+
+// fragments of one step: stg = its stage, sc = its scale slot, w = the step's index in its group
+template <bool GATEUP>
+__device__ __forceinline__ void pf_read(const uint8_t* stg, const uint8_t* sc, int w, PfFrags& fr, int wm,
+                                        int wn, int lane) {
+    const int lg = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int fa = GATEUP ? ((j >> 2) * 8 + wm * 4 + (j & 3)) : (wm * 8 + j);
+        fr.a[j] = *(const uint4*)(stg + kPfA + (fa * 16 + li) * 64 + ((lg ^ swz_a(li)) * 16));
+        fr.sa[j] = sc[kScA + (fa * 16 + li) * 16 + w * 4 + lg];      // scale byte of K block lg
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int col = (wn * 4 + n) * 16 + li;
+        const uint8_t* cp = stg + kPfB + col * 128;
+        fr.b[n][0] = *(const uint4*)(cp + (((2 * lg) ^ swz_b(li)) * 16));
+        fr.b[n][1] = *(const uint4*)(cp + (((2 * lg + 1) ^ swz_b(li)) * 16));
+        fr.sb[n] = sc[kScB + col * 16 + w * 4 + lg];
+    }
+}
+
+__device__ __forceinline__ void pf_mfma(const PfFrags& fr, v4f (&acc)[8][4]) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[j][n] = mfma_fp4_fp8(fr.a[j], fr.b[n][0], fr.b[n][1], acc[j][n], fr.sa[j], fr.sb[n]);
+}
+
+template <int Q>
+struct StepPos {
+    static constexpr int value = Q;
+};
 
 template <int NT, bool GATEUP>
-__global__ __launch_bounds__(256) void k_mx_pf(GemmArgs a, int ss2, int tiles_per_xcd_cap) {
-    __shared__ __align__(16) uint8_t lA[2][kPfRows][64];
-    __shared__ __align__(16) uint32_t lAs[2][kPfRows];
-    __shared__ __align__(16) uint8_t lB[2][kPfCols * kPfBStride];
-    __shared__ __align__(16) uint32_t lBs[2][kPfCols];
+__global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles_per_xcd_cap) {
+    __shared__ __align__(16) uint8_t stg0[kPfStage];
+    __shared__ __align__(16) uint8_t stg1[kPfStage];
+    __shared__ __align__(16) uint8_t stg2[kPfStage];
+    __shared__ __align__(16) uint8_t stg3[kPfStage];
+    __shared__ __align__(16) uint8_t scr0[kScSlot];
+    __shared__ __align__(16) uint8_t scr1[kScSlot];
     constexpr int TT = kPfCols / NT;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int wm = wave & 1, wn = wave >> 1;
     const int K = GATEUP ? a.d : a.f;
-    const int MT = GATEUP ? a.f / 64 : a.d / 128;       // row blocks per tile
+    const int rows = GATEUP ? a.f : a.d;                 // output rows (h rows / d)
+    const int MT = GATEUP ? a.f / 128 : (a.d + kPfRows - 1) / kPfRows;
     // workgroup -> (tile, row block): XCD x = id % 8 takes tiles [x * TPX, (x + 1) * TPX)
     const int nt = *a.ntiles;
     const int g = blockIdx.x, xcd = g & 7, sidx = g >> 3;
@@ -808,146 +897,184 @@ __global__ __launch_bounds__(256) void k_mx_pf(GemmArgs a, int ss2, int tiles_pe
     const int ntok = min(TT, a.offsets[e + 1] - i0);
     const moe_expert ex = a.table[e];
 
-    // staging sources: A rows (2 chunks per thread), A scales (threads < 128), B columns (4 chunks
-    // per thread), B scales (threads < 128); columns past the tile re-read its first column
+    // tile row r (0..255) -> weight row; down rows past d re-read row d - 1 (not stored)
     auto a_row_ptr = [&](int r, bool scale) -> const uint8_t* {
         int mr;
         const uint8_t* base;
         if (GATEUP) {
-            mr = mblk * 64 + (r & 63);
-            base = (r < 64) ? (scale ? ex.gate_s : ex.gate_q) : (scale ? ex.up_s : ex.up_q);
+            mr = mblk * 128 + (r & 127);
+            base = (r < 128) ? (scale ? ex.gate_s : ex.gate_q) : (scale ? ex.up_s : ex.up_q);
         } else {
-            mr = mblk * 128 + r;
+            mr = min(mblk * kPfRows + r, a.d - 1);
             base = scale ? ex.down_s : ex.down_q;
         }
         return base + (size_t)mr * (scale ? K / 32 : K / 2);
     };
+    // tile column c (0..127) = (pick c / NT, term c % NT); columns past the tile re-read column 0
     auto b_col_ptr = [&](int c, bool scale) -> const uint8_t* {
         const int tc = c / NT, t = c % NT;
         const int tcc = tc < ntok ? tc : 0;
         const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tcc] / a.k) : (size_t)(i0 + tcc);
         return scale ? a.as + (arow * NT + t) * (size_t)(K / 32) : a.aq + (arow * NT + t) * (size_t)K;
     };
-    const uint8_t* srcA[2];
-    int dstA[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int q = i * 256 + tid, r = q >> 2, part = q & 3;
-        srcA[i] = a_row_ptr(r, false) + part * 16;
-        dstA[i] = r * 64 + part * 16;
-    }
+    // this wave's direct loads: weight rows 64 w .. 64 w + 63 (4 instructions of 16 rows, a
+    // lane quad per row), activation columns 32 w .. 32 w + 31 (4 instructions of 8 columns, 8
+    // lanes per column); scale words of the same rows (4 instructions) and columns (2)
+    const uint8_t* srcA[4];
     const uint8_t* srcB[4];
-    int dstB[4];
+    const uint8_t* srcAs[4];
+    const uint8_t* srcBs[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = i * 256 + tid, c = q >> 3, part = q & 7;
-        srcB[i] = b_col_ptr(c, false) + part * 16;
-        dstB[i] = c * kPfBStride + part * 16;
+    for (int j = 0; j < 4; ++j) {
+        const int r = (wave * 4 + j) * 16 + (lane >> 2);
+        srcA[j] = a_row_ptr(r, false) + (((lane & 3) ^ swz_a(r & 15)) * 16);
+        const int c = (wave * 4 + j) * 8 + (lane >> 3);
+        srcB[j] = b_col_ptr(c, false) + (((lane & 7) ^ swz_b(c & 15)) * 16);
+        srcAs[j] = a_row_ptr(r, true);
     }
-    const int sr = tid & 127;
-    const uint8_t* srcS = (tid < 128) ? a_row_ptr(sr, true) : b_col_ptr(sr, true);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) srcBs[j] = b_col_ptr((wave * 2 + j) * 16 + (lane >> 2), true);
+    const int nsteps = K / 128, last = nsteps - 1;
 
-    uint4 vA[2], vB[4];
-    uint32_t vS;
-    auto load_step = [&](int st) {
+    auto issue = [&](int st, uint8_t* stg) {
+        const size_t oa = (size_t)st * 64, ob = (size_t)st * 128;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) vA[i] = gload16(srcA[i] + (size_t)st * 64);
+        for (int j = 0; j < 4; ++j) dma16(srcA[j] + oa, stg + kPfA + (wave * 4 + j) * 1024);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vB[i] = gload16(srcB[i] + (size_t)st * 128);
-        vS = gload4(srcS + (size_t)st * 4);
+        for (int j = 0; j < 4; ++j) dma16(srcB[j] + ob, stg + kPfB + (wave * 4 + j) * 1024);
     };
-    auto store_step = [&](int buf) {
+    // scale words of steps 4m .. 4m + 3 (past the last step: the last step's) into slot sc
+    auto issue_scales = [&](int m, uint8_t* sc) {
+        const size_t ow = (size_t)min(4 * m + (lane & 3), last) * 4;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) *(uint4*)(&lA[buf][0][0] + dstA[i]) = vA[i];
+        for (int j = 0; j < 4; ++j) dma4(srcAs[j] + ow, sc + kScA + (wave * 4 + j) * 256);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(uint4*)(&lB[buf][0] + dstB[i]) = vB[i];
-        if (tid < 128) lAs[buf][sr] = vS;
-        else lBs[buf][sr] = vS;
+        for (int j = 0; j < 2; ++j) dma4(srcBs[j] + ow, sc + kScB + (wave * 2 + j) * 256);
     };
 
-    v4f acc[4][4];
+    v4f acc[8][4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[f][n] = v4f{0.f, 0.f, 0.f, 0.f};
-    // this wave's A fragments (LDS rows) and B fragments (LDS columns)
-    int arow[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-        arow[f] = GATEUP ? ((f >> 1) * 64 + wm * 32 + (f & 1) * 16 + li) : (wm * 64 + f * 16 + li);
-    const int nsteps = K / 128;
-    load_step(0);
-    store_step(0);
-    __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nsteps) load_step(st + 1);
-        uint4 A[4];
-        uint32_t sa[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            A[f] = *(const uint4*)&lA[buf][arow[f]][lg * 16];
-            sa[f] = (lAs[buf][arow[f]] >> (8 * lg)) & 0xffu;
-        }
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int col = wn * 64 + n * 16 + li;
-            const uint8_t* bp = &lB[buf][col * kPfBStride + lg * 32];
-            const uint4 b0 = *(const uint4*)bp, b1 = *(const uint4*)(bp + 16);
-            const int sb = (int)((lBs[buf][col] >> (8 * lg)) & 0xffu);
-#pragma unroll
-            for (int f = 0; f < 4; ++f) acc[f][n] = mfma_fp4_fp8(A[f], b0, b1, acc[f][n], (int)sa[f], sb);
-        }
-        if (st + 1 < nsteps) store_step(buf ^ 1);
-        __syncthreads();
+        for (int n = 0; n < 4; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
+    PfFrags fr0, fr1;
+    // Every step issues one stage, clamped to the last: past the end the ring is refilled with
+    // copies of the last stage that no step reads.  The scale group of steps 4m.. rides with
+    // stage 4m.  Before step s reads stage s + 1, the loads of stages s + 2 and s + 3 (and of
+    // the one scale group among them, if any) may still be in flight.
+    issue(0, stg0);
+    issue_scales(0, scr0);
+    issue(min(1, last), stg1);
+    issue(min(2, last), stg2);
+    issue(min(3, last), stg3);
+    wait_vm<3 * kPfLoads>();                                 // stage 0 and its scales complete
+    ring_barrier();
+    pf_read<GATEUP>(stg0, scr0, 0, fr0, wm, wn, lane);
+
+    // buffers by compile-time index (distinct arrays, so the compiler sees that a direct load
+    // into one never feeds a read of another)
+    auto stage_buf = [&](auto i) -> uint8_t* {
+        constexpr int I = decltype(i)::value;
+        if constexpr (I == 0) return stg0;
+        else if constexpr (I == 1) return stg1;
+        else if constexpr (I == 2) return stg2;
+        else return stg3;
+    };
+    auto scale_buf = [&](auto i) -> uint8_t* {
+        if constexpr (decltype(i)::value == 0) return scr0;
+        else return scr1;
+    };
+    // step s (s % 8 == Q): stage s is in registers; wait for stage s + 1, refill stage s's
+    // buffer with step s + 4 (and, opening a group of four, the scale slot of the next group),
+    // read stage s + 1 into the other register set (past the end: unused values), run the
+    // MFMAs of step s
+    auto step = [&](int s, auto pos) {
+        constexpr int Q = decltype(pos)::value;
+        PfFrags& cur = (Q & 1) ? fr1 : fr0;
+        PfFrags& nxt = (Q & 1) ? fr0 : fr1;
+        wait_vm<2 * kPfLoads + (((Q & 3) == 1 || (Q & 3) == 2) ? kScLoads : 0)>();
+        ring_barrier();                                      // also: every wave has stage s in registers
+        issue(min(s + 4, last), stage_buf(StepPos<Q & 3>{}));
+        if constexpr ((Q & 3) == 0) issue_scales((s >> 2) + 1, scale_buf(StepPos<((Q >> 2) + 1) & 1>{}));
+        pf_read<GATEUP>(stage_buf(StepPos<(Q + 1) & 3>{}), scale_buf(StepPos<((Q + 1) >> 2) & 1>{}), (Q + 1) & 3,
+                        nxt, wm, wn, lane);
+        // the reads of step s + 1 are issued before the MFMAs of step s, which do not wait for
+        // them; no MFMA of step s + 1 is hoisted above the next barrier to wait for them here
+        __builtin_amdgcn_sched_barrier(0);
+        pf_mfma(cur, acc);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int s = 0;
+    for (; s + 8 <= nsteps; s += 8) {
+        step(s, StepPos<0>{});
+        step(s + 1, StepPos<1>{});
+        step(s + 2, StepPos<2>{});
+        step(s + 3, StepPos<3>{});
+        step(s + 4, StepPos<4>{});
+        step(s + 5, StepPos<5>{});
+        step(s + 6, StepPos<6>{});
+        step(s + 7, StepPos<7>{});
     }
+    if (s < nsteps) step(s, StepPos<0>{});
+    if (s + 1 < nsteps) step(s + 1, StepPos<1>{});
+    if (s + 2 < nsteps) step(s + 2, StepPos<2>{});
+    if (s + 3 < nsteps) step(s + 3, StepPos<3>{});
+    if (s + 4 < nsteps) step(s + 4, StepPos<4>{});
+    if (s + 5 < nsteps) step(s + 5, StepPos<5>{});
+    if (s + 6 < nsteps) step(s + 6, StepPos<6>{});
+    wait_vm<0>();                                            // no direct load outlives the workgroup
 
     // columns: n * 16 + li of this wave's 64 = (pick tc, term t)
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int n = 0; n < 4; ++n)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[f][n][r] = sum_adjacent<NT>(acc[f][n][r]);
+            for (int r = 0; r < 4; ++r) acc[j][n][r] = sum_adjacent<NT>(acc[j][n][r]);
     const int t = li % NT;
     if constexpr (GATEUP) {
-        // h = silu(g) u for the wave's 32 row indices (one natural block of h), split into NT
-        // terms with one exponent per term and block
-        const int rg = (mblk * 64 + wm * 32) / 32;
+        // h = silu(g) u for the wave's 64 row indices (two natural blocks of h), each split into
+        // NT terms with one exponent per term and block
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            float v[8];
+        for (int n = 0; n < 4; ++n)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                v[r] = silu(acc[0][n][r]) * acc[2][n][r];
-                v[4 + r] = silu(acc[1][n][r]) * acc[3][n][r];
+            for (int b = 0; b < 2; ++b) {
+                float v[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v[r] = silu(acc[2 * b][n][r]) * acc[4 + 2 * b][n][r];
+                    v[4 + r] = silu(acc[2 * b + 1][n][r]) * acc[5 + 2 * b][n][r];
+                }
+                uint32_t codes[NT][2];
+                int S[NT];
+                split_terms<NT>(v, codes, S, [](float mm) { return max_xor32(max_xor16(mm)); });
+                const int rg = (mblk * 128 + wm * 64) / 32 + b;
+                const int tc = (wn * 64 + n * 16 + li) / NT;
+                if (tc < ntok) {
+                    const size_t pos = (size_t)i0 + tc;
+                    uint32_t w0 = codes[0][0], w1 = codes[0][1];
+                    int Sme = S[0];
+#pragma unroll
+                    for (int q = 1; q < NT; ++q)
+                        if (q == t) { w0 = codes[q][0]; w1 = codes[q][1]; Sme = S[q]; }
+                    uint8_t* dst = a.hq + (pos * NT + t) * (size_t)a.f;
+                    *(uint32_t*)(dst + act_half_offset(ss2, rg, 0) + 4 * lg) = w0;
+                    *(uint32_t*)(dst + act_half_offset(ss2, rg, 1) + 4 * lg) = w1;
+                    if (lg == 0) a.hs[(pos * NT + t) * (size_t)(a.f / 32) + rg] = (uint8_t)(Sme + 127);
+                }
             }
-            uint32_t codes[NT][2];
-            int S[NT];
-            split_terms<NT>(v, codes, S, [](float mm) { return max_xor32(max_xor16(mm)); });
-            const int tc = (wn * 64 + n * 16 + li) / NT;
-            if (tc < ntok) {
-                const size_t pos = (size_t)i0 + tc;
-                uint32_t w0 = codes[0][0], w1 = codes[0][1];
-                int Sme = S[0];
-#pragma unroll
-                for (int q = 1; q < NT; ++q)
-                    if (q == t) { w0 = codes[q][0]; w1 = codes[q][1]; Sme = S[q]; }
-                uint8_t* dst = a.hq + (pos * NT + t) * (size_t)a.f;
-                *(uint32_t*)(dst + act_half_offset(ss2, rg, 0) + 4 * lg) = w0;
-                *(uint32_t*)(dst + act_half_offset(ss2, rg, 1) + 4 * lg) = w1;
-                if (lg == 0) a.hs[(pos * NT + t) * (size_t)(a.f / 32) + rg] = (uint8_t)(Sme + 127);
-            }
-        }
     } else {
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const int tc = (wn * 64 + n * 16 + li) / NT;
             if (tc < ntok && t == 0) {
-                float* dst = a.o + ((size_t)i0 + tc) * a.d + mblk * 128 + wm * 64 + 4 * lg;
+                float* dst = a.o + ((size_t)i0 + tc) * a.d;
 #pragma unroll
-                for (int f = 0; f < 4; ++f)
-                    *(float4*)(dst + 16 * f) = make_float4(acc[f][n][0], acc[f][n][1], acc[f][n][2], acc[f][n][3]);
+                for (int j = 0; j < 8; ++j) {
+                    const int row = mblk * kPfRows + wm * 128 + 16 * j + 4 * lg;
+                    if (row < rows)
+                        *(float4*)(dst + row) = make_float4(acc[j][n][0], acc[j][n][1], acc[j][n][2], acc[j][n][3]);
+                }
             }
         }
     }
@@ -955,7 +1082,7 @@ __global__ __launch_bounds__(256) void k_mx_pf(GemmArgs a, int ss2, int tiles_pe
 
 template <bool GATEUP>
 static hipError_t launch_pf(const GemmArgs& a, int NT, int max_tiles, hipStream_t st) {
-    const int MT = GATEUP ? a.f / 64 : a.d / 128;
+    const int MT = GATEUP ? a.f / 128 : (a.d + kPfRows - 1) / kPfRows;
     const int cap = (max_tiles + 7) / 8;
     dim3 grid((unsigned)(8 * cap * MT));
     if (NT == 2) MOE_LAUNCH((k_mx_pf<2, GATEUP>), grid, dim3(256), 0, st, a, 1, cap);

@@ -89,6 +89,12 @@ SMALL_CASES = [
     ("tiny", dict(d_model=512, d_ff=256, n_experts=32, top_k=4, act_dtype=synth.BF16), 37),
     ("tiny", dict(d_model=1024, d_ff=512, n_experts=64, top_k=8, act_dtype=synth.BF16), 300),
     ("tiny", dict(d_model=1024, d_ff=2048, n_experts=8, top_k=2), 11),
+    # many picks per expert (LDS-tiled GEMM): fp32 activations in four terms
+    ("tiny", dict(n_experts=4, top_k=2), 200),
+    # 3 K steps of gate/up, 5 of down; the second block of 256 down rows runs past d_model
+    ("tiny", dict(d_model=384, d_ff=640, n_experts=8, top_k=2, act_dtype=synth.BF16), 150),
+    # 7 K steps: one full group of four plus a tail of three
+    ("tiny", dict(d_model=896, d_ff=256, n_experts=12, top_k=3, act_dtype=synth.BF16), 100),
 ]
 
 
