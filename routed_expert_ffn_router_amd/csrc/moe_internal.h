@@ -50,32 +50,6 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return readlane_f64(v, 63);
 }
 
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ void argmax_step(unsigned long long& key, int& idx) {
-    const uint32_t lo = dpp_u32<CTRL, ROWMASK>((uint32_t)key, (uint32_t)key);
-    const uint32_t hi = dpp_u32<CTRL, ROWMASK>((uint32_t)(key >> 32), (uint32_t)(key >> 32));
-    const int oi = (int)dpp_u32<CTRL, ROWMASK>((uint32_t)idx, (uint32_t)idx);
-    const unsigned long long ok = ((unsigned long long)hi << 32) | lo;
-    // bitwise, not short-circuit: selects instead of branches
-    const bool better = (ok > key) | ((ok == key) & (oi < idx));
-    key = better ? ok : key;
-    idx = better ? oi : idx;
-}
-
-// the (largest key, then smallest idx) pair of the wave, returned in every lane
-__device__ __forceinline__ void wave_argmax(unsigned long long& key, int& idx) {
-    argmax_step<kDppXor1, 0xF>(key, idx);
-    argmax_step<kDppXor2, 0xF>(key, idx);
-    argmax_step<kDppHalfMirror, 0xF>(key, idx);
-    argmax_step<kDppMirror, 0xF>(key, idx);
-    argmax_step<kDppBcast15, 0xA>(key, idx);
-    argmax_step<kDppBcast31, 0xC>(key, idx);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
-    key = ((unsigned long long)hi << 32) | lo;
-    idx = __builtin_amdgcn_readlane(idx, 63);
-}
-
 // maximum over each 16-lane row, returned in every lane of the row
 __device__ __forceinline__ float row16_max(float m) {
     m = fmaxf(m, __uint_as_float(dpp_u32<kDppXor1, 0xF>(__float_as_uint(m), __float_as_uint(m))));

@@ -155,35 +155,55 @@ hipError_t launch_router_logits(const moe_shape* s, const void* x, int T, const 
 }
 
 // ---------------------------------------------------------------------------------------------
-// top-k: one wave per token.  Each lane holds up to 16 logits (E <= 1024); k rounds of a
-// wave arg-max under the order (logit descending, index ascending, NaN last).
+// top-k: one wave per token.  Each lane holds up to 16 logits (E <= 1024), sorted; k rounds each
+// take the wave's best head under the order (logit descending, index ascending, NaN last).
 // ---------------------------------------------------------------------------------------------
+// Does (la, a) rank before (lb, b)?  Larger logit first, then lower index; a NaN ranks after
+// every number (NaNs among themselves by index); -0 and +0 are equal.  Branch-free.
 __device__ __forceinline__ bool ranks_before(double la, int a, double lb, int b) {
-    const bool na = isnan(la), nb = isnan(lb);
-    if (na || nb) return (na && nb) ? (a < b) : nb;
-    if (la != lb) return la > lb;
-    return a < b;
+    const bool na = __builtin_isnan(la), nb = __builtin_isnan(lb);
+    const bool num = (la > lb) | ((la == lb) & (a < b));
+    const bool nan = nb & (!na | (a < b));
+    return (na | nb) ? nan : num;
 }
 
-// Order-preserving 64-bit key of a logit: a larger logit has a larger key, -0 and +0 share a
-// key, and a NaN gets key 0 (below every number).
-__device__ __forceinline__ unsigned long long logit_key(double v) {
-    if (isnan(v)) return 0ull;
-    unsigned long long b = (unsigned long long)__double_as_longlong(v);
-    if (b == 0x8000000000000000ull) b = 0ull;
-    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_max_f64(double v) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = dpp_u32<CTRL, ROWMASK>((uint32_t)b, (uint32_t)b);
+    const uint32_t hi = dpp_u32<CTRL, ROWMASK>((uint32_t)(b >> 32), (uint32_t)(b >> 32));
+    return fmax(v, __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo)));
 }
-
-__device__ __forceinline__ double key_to_logit(unsigned long long key) {
-    const unsigned long long b = (key >> 63) ? (key & 0x7fffffffffffffffull) : ~key;
-    return __longlong_as_double((long long)b);
+// largest value of the wave, a NaN lane ignored unless every lane is NaN (in every lane)
+__device__ __forceinline__ double wave_max_f64(double v) {
+    v = dpp_max_f64<kDppXor1, 0xF>(v);
+    v = dpp_max_f64<kDppXor2, 0xF>(v);
+    v = dpp_max_f64<kDppHalfMirror, 0xF>(v);
+    v = dpp_max_f64<kDppMirror, 0xF>(v);
+    v = dpp_max_f64<kDppBcast15, 0xA>(v);
+    v = dpp_max_f64<kDppBcast31, 0xC>(v);
+    return readlane_f64(v, 63);
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_min_i32(int v) {
+    return min(v, (int)dpp_u32<CTRL, ROWMASK>((uint32_t)v, (uint32_t)v));
+}
+// smallest value of the wave (in every lane)
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = dpp_min_i32<kDppXor1, 0xF>(v);
+    v = dpp_min_i32<kDppXor2, 0xF>(v);
+    v = dpp_min_i32<kDppHalfMirror, 0xF>(v);
+    v = dpp_min_i32<kDppMirror, 0xF>(v);
+    v = dpp_min_i32<kDppBcast15, 0xA>(v);
+    v = dpp_min_i32<kDppBcast31, 0xC>(v);
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Top-k of one token's E logits by one wave (E <= 64 * S, k <= E), written in rank order to
-// idx[0..k): rank order is (logit descending, expert index ascending), a NaN ranks after every
-// number.  w[j] = sigmoid(l_j) / sum_j' sigmoid(l_j'), the sum taken in rank order.  Each lane
-// keeps its S logits as order-preserving keys, sorted; a round takes the best of the lanes'
-// heads by a DPP arg-max across the wave.  All 64 lanes must call it; lane j%64 stores entry j.
+// idx[0..k).  w[j] = sigmoid(l_j) / sum_j' sigmoid(l_j'), the sum taken in rank order.  Each lane
+// keeps its S logits sorted; a round takes the largest head (NaN only if every head is NaN) and
+// then the lowest expert index among the heads equal to it.  All 64 lanes must call it; lane
+// j%64 stores entry j.
 template <int S>
 __device__ __forceinline__ void topk_load(const double* __restrict__ l, int E, double (&lv)[S]) {
     const int lane = threadIdx.x & 63;
@@ -194,60 +214,56 @@ __device__ __forceinline__ void topk_load(const double* __restrict__ l, int E, d
     }
 }
 
-// rank order of (key, index) pairs: larger key first, then lower index
-__device__ __forceinline__ bool ranks_before(unsigned long long ka, int ia, unsigned long long kb, int ib) {
-    return (ka > kb) | ((ka == kb) & (ia < ib));
-}
-
 template <int S>
 __device__ void topk_select(const double (&lv)[S], const double* __restrict__ l, int E, int k, int32_t* idx,
                             float* w) {
     const int lane = threadIdx.x & 63;
     // this lane's entries in rank order (odd-even transposition sort, S passes); slots past E
-    // hold key 0 and index INT_MAX, which rank after every expert (a NaN logit has key 0 too,
-    // but a real index), and k <= E keeps them from being taken
-    unsigned long long key[S];
+    // hold NaN and index INT_MAX, which rank after every expert, and k <= E keeps them from
+    // being taken
+    double v[S];
     int ei[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int e = lane + 64 * s;
-        key[s] = (e < E) ? logit_key(lv[s]) : 0ull;
+        v[s] = (e < E) ? lv[s] : __builtin_nan("");
         ei[s] = (e < E) ? e : 0x7fffffff;
     }
 #pragma unroll
     for (int pass = 0; pass < S; ++pass) {
 #pragma unroll
         for (int s = pass & 1; s + 1 < S; s += 2) {
-            const bool sw = ranks_before(key[s + 1], ei[s + 1], key[s], ei[s]);
-            const unsigned long long k0 = key[s], k1 = key[s + 1];
+            const bool sw = ranks_before(v[s + 1], ei[s + 1], v[s], ei[s]);
+            const double v0 = v[s], v1 = v[s + 1];
             const int i0 = ei[s], i1 = ei[s + 1];
-            key[s] = sw ? k1 : k0;
-            key[s + 1] = sw ? k0 : k1;
+            v[s] = sw ? v1 : v0;
+            v[s + 1] = sw ? v0 : v1;
             ei[s] = sw ? i1 : i0;
             ei[s + 1] = sw ? i0 : i1;
         }
     }
-    // k rounds: the wave's best head entry is taken, and its lane's list shifts up by one
-    unsigned long long my_key = 0ull;
+    // k rounds: the winner's lane (its expert index mod 64) shifts its list up by one
+    double my_l = 0.0;
     for (int j = 0; j < k; ++j) {
-        unsigned long long bk = key[0];
-        int be = ei[0];
-        wave_argmax(bk, be);
-        const bool win = (be & 63) == lane;
+        const double m = wave_max_f64(v[0]);
+        const bool tied = __builtin_isnan(m) ? __builtin_isnan(v[0]) : (v[0] == m);
+        const int c = wave_min_i32(tied ? ei[0] : 0x7fffffff);
+        const bool win = (c & 63) == lane;
 #pragma unroll
         for (int s = 0; s + 1 < S; ++s) {
-            key[s] = win ? key[s + 1] : key[s];
+            v[s] = win ? v[s + 1] : v[s];
             ei[s] = win ? ei[s + 1] : ei[s];
         }
-        key[S - 1] = win ? 0ull : key[S - 1];
+        v[S - 1] = win ? __builtin_nan("") : v[S - 1];
         ei[S - 1] = win ? 0x7fffffff : ei[S - 1];
         if ((j & 63) == lane) {
-            idx[j] = be;
-            if (j < 64) my_key = bk;
+            idx[j] = c;
+            if (j < 64) my_l = m;
         }
     }
-    // weights: every lane's sigmoid in parallel (from the selected key), the sum in rank order
-    const double sg = (lane < k) ? 1.0 / (1.0 + exp(-key_to_logit(my_key))) : 0.0;
+    // weights: every lane's sigmoid in parallel (of the selected logit: equal to m, or +0 for
+    // -0, which has the same sigmoid), the sum in rank order
+    const double sg = (lane < k) ? 1.0 / (1.0 + exp(-my_l)) : 0.0;
     double ssum = 0.0;
     for (int j = 0; j < k && j < 64; ++j) ssum += readlane_f64(sg, j);
     for (int j = 64; j < k; ++j) ssum += 1.0 / (1.0 + exp(-l[idx[j]]));   // k > 64 only
@@ -425,7 +441,6 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     // Grouping without atomics or scans (P <= 512, two picks per thread): a pick's sorted
     // position is the number of picks of lower experts plus its rank among the picks of its own
     // expert; it starts a tile when that rank is a multiple of tt.
-    moe_expert ex[2];
     int pos[2], rank[2], cnt[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -433,8 +448,6 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         pos[u] = -1;
         if (p < P) {
             const int e = s_idx[p];
-            if constexpr (tab_lds) ex[u] = *(const moe_expert*)&s_tab[4 * e];
-            else ex[u] = a.table[e];
             int lower = 0, before = 0, same = 0;
             for (int q = 0; q < P; ++q) {
                 const int eq = s_idx[q];
@@ -459,6 +472,14 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         a.offsets[e] = lower;
     }
     __syncthreads();
+    // the expert-table entry of expert e into a tile record: four 16-byte moves, from the LDS copy
+    // of the table when there is one
+    auto put_expert = [&](TileDesc* D, int e) {
+        const uint4* src = tab_lds ? &s_tab[4 * e] : (const uint4*)(a.table + e);
+        uint4* dst = (uint4*)&D->ex;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = src[i];
+    };
     // tiles: numbered by sorted position of their first pick
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -467,7 +488,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             for (int q = 0; q < pos[u]; ++q) id += s_start[q];
             const int ntok = min(tt, cnt[u] - rank[u]);
             TileDesc* D = a.desc + id;
-            D->ex = ex[u];
+            put_expert(D, s_idx[tid + 256 * u]);
             D->i0 = pos[u];
             D->ntok = ntok;
             D->e = s_idx[s_sorted[pos[u]]];
@@ -484,8 +505,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         // an empty record still names a real expert (the first pick's), so that a stray read of
         // its pointers stays inside the weights
         TileDesc* D = a.desc + id;
-        if constexpr (tab_lds) D->ex = *(const moe_expert*)&s_tab[4 * s_idx[0]];
-        else D->ex = a.table[s_idx[0]];
+        put_expert(D, s_idx[0]);
         D->i0 = 0;
         D->ntok = 0;
         D->e = s_idx[0];

@@ -61,6 +61,28 @@ def test_route_ties_go_to_lower_index():
     np.testing.assert_array_equal(idx.cpu().numpy(), oidx)
 
 
+@pytest.mark.parametrize("T", [1, 5, 40])
+def test_route_nan_rows_and_zero_tokens(T):
+    """NaN logits rank after every number (experts 3 and 9 have NaN router rows); a token of
+    zeros gives every expert logit 0, so the lowest indices win, with equal weights."""
+    wl = small("tiny", top_k=4)
+    router = synth.make_router(wl, 0, 0, "cpu")
+    router[3] = float("nan")
+    router[9] = float("nan")
+    x = _x(wl, T)
+    x[0] = 0.0
+    shape = m.make_shape(wl.d_model, wl.d_ff, wl.n_experts, wl.top_k, wl.wformat, wl.act_dtype)
+    idx = torch.empty(T, 4, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, 4, dtype=torch.float32, device="cuda")
+    m.moe_route(shape, x, T, router.cuda(), None, idx, w, m.workspace(shape, T))
+    torch.cuda.synchronize()
+    _, oidx, ow = oracle.route(oracle.to_f64(x), router.numpy(), None, 4)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oidx)
+    np.testing.assert_array_equal(oidx[0], [0, 1, 2, 4])       # 3 is NaN: after every number
+    assert not np.isin(oidx[1:], [3, 9]).any()
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=2e-7, atol=1e-8)
+
+
 @pytest.mark.parametrize("T,k,E", [(1, 8, 288), (5, 2, 16), (64, 8, 288), (4096, 8, 288), (1000, 8, 1024)])
 def test_permute_bit_exact(T, k, E):
     g = torch.Generator().manual_seed(T + E)
