@@ -140,13 +140,14 @@ static GemmArgs gemm_args(const moe_shape* s, const moe_expert* table, int32_t T
 // NVFP4: plan tiles of kNvTilePicks picks, bf16 terms of an fp32 x, then gate/up and down on the
 // bf16 matrix cores; with staging, the distinct experts are first copied into the staging buffer
 // kStageGroup at a time and each group's tiles run from the staged copies
+// planned: the tile plan is already in the workspace (the fused router wrote it)
 static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const void* x, int32_t T,
                              const int32_t* offsets, const int32_t* sorted_pick, float* o, uint8_t* ws,
-                             const WsLayout& L, void* staging, hipStream_t st) {
+                             const WsLayout& L, void* staging, hipStream_t st, bool planned = false) {
     const int tt = nv_tile_picks(s, T);
     int32_t* tiles = (int32_t*)(ws + L.tiles);
     int32_t* ntiles = (int32_t*)(ws + L.ntiles);
-    MOE_HIP(launch_plan(s, offsets, tt, tiles, ntiles, st));
+    if (!planned) MOE_HIP(launch_plan(s, offsets, tt, tiles, ntiles, st));
     const bool bf = s->act_dtype == MOE_DT_BF16;
     const int NT = bf ? 1 : 2;
     if (!bf) MOE_HIP(launch_bf16_terms((const float*)x, T, s->d_model, (uint16_t*)(ws + L.xq), st));
@@ -336,10 +337,11 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
     int32_t* sorted_pick = (int32_t*)(w8 + L.sorted_pick);
     int32_t* pick_pos = (int32_t*)(w8 + L.pick_pos);
     float* o = (float*)(w8 + L.o);
-    if (!nv && T <= kSmallTokens && s->top_k <= 64 && (long long)T * s->top_k <= kMaxFusedPicks &&
+    if ((!nv || !staging) && T <= kSmallTokens && s->top_k <= 64 && (long long)T * s->top_k <= kMaxFusedPicks &&
         s->d_model <= 8192) {
         // few tokens: fused router (logits, top-k, permute, plan, activation split), the gate/up
         // GEMM, and the down GEMM fused with the weighted combine: three launches per layer
+        // (NVFP4: the fused router, its two GEMMs and the combine)
         const int NT = L.nt;
         const int variant = 0;
         RouteSmallArgs r;
@@ -366,6 +368,14 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
         r.xq = w8 + L.xq;
         r.xs = w8 + L.xs;
         r.ss1 = super_step(s->d_model, ksplit_for(s->d_model, variant));
+        r.split = nv ? 0 : 1;
+        if (nv) {
+            r.tt = nv_tile_picks(s, T);
+            MOE_HIP(launch_route_small(s, r, stream));
+            MOE_TRY(run_ffn_nv(s, d_table, x, T, offsets, sorted_pick, o, w8, L, nullptr, stream, true));
+            MOE_HIP(launch_combine(s, o, w, pick_pos, T, residual, y, stream));
+            return MOE_OK;
+        }
         const bool dec = decode_gemm_ok(s);
         if (dec) r.ss1 = 4;   // x terms in chunks of 512: the layout k_mx_gateup_dec reads
         MOE_HIP(launch_route_small(s, r, stream));

@@ -332,7 +332,7 @@ hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t*
 // fused router for few tokens (T <= 16), one launch per layer: every workgroup computes the fp64
 // logits of 4 experts (one wave each); the last workgroup to finish (device-scope counter) does
 // the top-k, the grouping and the tile records, then resets the counter to zero for the next
-// launch, while the others split x into fp8 terms.
+// launch, while the others split x into fp8 terms (when the GEMMs read them).
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallT = 16;
 
@@ -386,11 +386,11 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     __syncthreads();
     const int G = (int)gridDim.x, ticket = s_ticket;
     if (ticket != G - 1) {
-        split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, ticket, G - 1);
+        if (a.split) split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, ticket, G - 1);
         return;
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (G == 1) split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, 0, 1);
+    if (G == 1 && a.split) split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, 0, 1);
 
     __shared__ int32_t s_idx[kMaxFusedPicks];
     __shared__ float s_w[kMaxFusedPicks];
