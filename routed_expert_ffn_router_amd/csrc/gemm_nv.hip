@@ -386,6 +386,133 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
     }
 }
 
+// Few picks per expert ("decode"): a workgroup of 8 waves owns one tile (up to kNvTilePicks
+// picks) and one block of output rows: the same 16 row indices of gate and of up, or 32 down
+// rows.  Wave w takes the 16-row fragment w / 4 over the K quarter w % 4 and requests all of its
+// code and scale loads at once (NSW super-steps of 128 K at most); the tile's activation columns
+// are staged in LDS meanwhile (their first chunks requested before the weights), so the bf16
+// operand costs no registers.  Two workgroups share a CU, so one's MFMAs overlap the other's
+// loads.  The K quarters are summed through LDS in quarter order by wave 0, which also runs the
+// epilogue.  K is at most 512 NSW (so that a quarter has at most NSW super-steps) and a tile
+// has at most NCOL / NT picks (the launch guarantees it: a tile holds at most one pick per
+// token).
+constexpr int kNvDecMaxK = 8192;
+
+template <int NT, bool GATEUP, int NSW, int NCOL>
+__global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
+    constexpr int KMAX = 512 * NSW;
+    constexpr int CST = KMAX * 2 + 16;               // column stride in LDS (bf16, padded)
+    __shared__ __align__(16) uint8_t b_lds[NCOL * CST];
+    __shared__ v4f_nv part[8][64];
+    const int tile = blockIdx.x;
+    int t0 = 0, t1 = *a.ntiles;
+    if (a.tile_range) {
+        t0 = a.tile_range[0];
+        t1 = a.tile_range[1];
+    }
+    if (tile < t0 || tile >= t1) return;
+    const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
+    const int ntok = min(min(kNvTilePicks, NCOL / NT), a.offsets[e + 1] - i0);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int f = wave >> 2, kq = wave & 3;
+    const int K = GATEUP ? a.d : a.f;
+    const int cst = K * 2 + 16;
+    const moe_expert ex = a.table[e];
+    const int T0 = (GATEUP ? 16 : 32) * blockIdx.y;
+    const int NS = K / 128, s0 = (kq * NS) / 4, nss = ((kq + 1) * NS) / 4 - s0;
+    // 1. activation columns c = (pick c / NT, term c % NT), K bf16 each, as 16-byte chunks; the
+    // first round is requested before the weights
+    const int ncol = ntok * NT, cpc = K / 8, nchunk = ncol * cpc;
+    auto chunk_src = [&](int g) -> const uint8_t* {
+        const int c = g / cpc, tc = c / NT, t = c % NT;
+        const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tc] / a.k) : (size_t)(i0 + tc);
+        return a.aq + ((arow * NT + t) * (size_t)K + (size_t)(g % cpc) * 8) * 2;
+    };
+    const int g0 = tid < nchunk ? tid : nchunk - 1;
+    const uint4 v0 = gload16(chunk_src(g0));
+    // 2. this wave's weights: row of fragment f (gate: f = 0, up: f = 1; down: rows 16 f ..),
+    // super-steps s0 .. s0 + nss (past nss: re-read; a quarter without steps, K < 512, re-reads
+    // step s0, which is inside the row)
+    const int row = GATEUP ? T0 + li : T0 + 16 * f + li;
+    const uint8_t* mq = GATEUP ? (f == 0 ? ex.gate_q : ex.up_q) : ex.down_q;
+    const uint8_t* ms = GATEUP ? (f == 0 ? ex.gate_s : ex.up_s) : ex.down_s;
+    const uint8_t* aq = mq + (size_t)row * (K / 2) + (size_t)s0 * 64 + lg * 16;
+    const uint8_t* as = ms + (size_t)row * (K / 16) + (size_t)s0 * 8 + lg * 2;
+    uint4 A[NSW];
+    uint32_t sc[NSW];
+#pragma unroll
+    for (int q = 0; q < NSW; ++q) {
+        const int qq = q < nss ? q : (nss > 0 ? nss - 1 : 0);
+        A[q] = gload16(aq + (size_t)qq * 64);
+        sc[q] = *(const uint16_t*)(as + (size_t)qq * 8);
+    }
+    // 3. the columns into LDS (further rounds, for many columns, after the weights)
+    asm volatile("" ::"v"(v0.x), "v"(v0.y), "v"(v0.z), "v"(v0.w));
+    if (tid < nchunk) *(uint4*)(b_lds + (size_t)(g0 / cpc) * cst + (size_t)(g0 % cpc) * 16) = v0;
+    for (int g = tid + 512; g < nchunk; g += 512)
+        *(uint4*)(b_lds + (size_t)(g / cpc) * cst + (size_t)(g % cpc) * 16) = gload16(chunk_src(g));
+    __syncthreads();
+    // 4. MFMAs: lane group lg takes K [32 lg, 32 lg + 32) of a super-step, MFMA h its [8h, 8h + 8);
+    // columns past the tile read its last column (their results are not used)
+    const int col = li < ncol ? li : ncol - 1;
+    const uint8_t* bl = b_lds + (size_t)col * cst + (size_t)s0 * 256 + lg * 64;
+    v4f_nv acc = v4f_nv{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NSW; ++q) {
+        if (q < nss) {
+            const v2f_t bs = e4m3x2_to_f32(sc[q]);
+            const uint32_t w[4] = {A[q].x, A[q].y, A[q].z, A[q].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const bf16x8_t af = nv_dequant8(w[h], h < 2 ? bs[0] : bs[1]);
+                const uint4 b = *(const uint4*)(bl + (size_t)q * 256 + 16 * h);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, as_bf16x8(b), acc, 0, 0, 0);
+            }
+        }
+    }
+    // 5. K quarters summed in quarter order by wave 0, then the epilogue
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    v4f_nv r4[2];
+#pragma unroll
+    for (int ff = 0; ff < 2; ++ff) {
+        r4[ff] = part[4 * ff][lane];
+#pragma unroll
+        for (int k2 = 1; k2 < 4; ++k2) r4[ff] += part[4 * ff + k2][lane];
+        if constexpr (NT == 2) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) r4[ff][r] = sum_adjacent<2>(r4[ff][r]);
+        }
+    }
+    const int tc = li / NT, t = li % NT;
+    if (tc >= ntok || t != 0) return;
+    const size_t pos = (size_t)i0 + tc;
+    if constexpr (GATEUP) {
+        // h = silu(g) u for rows T0 + 4 lg + r, as two bf16 terms [P][2][f]
+        uint16_t* hb = (uint16_t*)a.hq + pos * 2 * (size_t)a.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float g = r4[0][r] * ex.gate_ts, u = r4[1][r] * ex.up_ts;
+            const float hv = g / (1.0f + __expf(-g)) * u;
+            const uint16_t hi = bf16_rne(hv);
+            const uint16_t lo = bf16_rne(hv - bf16_bits_to_f32(hi));
+            const int rr = T0 + 4 * lg + r;
+            hb[rr] = hi;
+            hb[a.f + rr] = lo;
+        }
+    } else {
+#pragma unroll
+        for (int ff = 0; ff < 2; ++ff) {
+            float* dst = a.o + pos * (size_t)a.d + T0 + 16 * ff + 4 * lg;
+            *(float4*)dst = make_float4(r4[ff][0] * ex.down_ts, r4[ff][1] * ex.down_ts, r4[ff][2] * ex.down_ts,
+                                        r4[ff][3] * ex.down_ts);
+        }
+    }
+}
+
 int nv_tile_picks(const moe_shape* s, int T) {
     return (long long)T * s->top_k > 8LL * s->n_experts ? kNvTilePicksMany : kNvTilePicks;
 }
@@ -403,6 +530,32 @@ hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int tile_picks
         if (!gateup) MOE_LAUNCH((k_nv_pf<2, false>), g2, dim3(256), 0, st, a, cap);
         else if (NT == 1) MOE_LAUNCH((k_nv_pf<1, true>), g2, dim3(256), 0, st, a, cap);
         else MOE_LAUNCH((k_nv_pf<2, true>), g2, dim3(256), 0, st, a, cap);
+    } else if ((gateup ? a.d : a.f) <= kNvDecMaxK) {
+        // LDS columns: a tile holds at most one pick per token, so min(tile picks, T) * NT;
+        // super-steps per K quarter: 4 (K <= 2048), 12 (K <= 6144) or 16
+        const int K = gateup ? a.d : a.f;
+        const int NTk = gateup ? NT : 2;
+        const bool narrow = (long long)(a.P / a.k < kNvTilePicks ? a.P / a.k : kNvTilePicks) * NTk <= 2;
+        const int nsw = K <= 2048 ? 4 : (K <= 6144 ? 12 : 16);
+        dim3 g3(max_tiles, rows / (gateup ? 16 : 32));
+#define MOE_NVD(N, G, S, NC) MOE_LAUNCH((k_nv_dec<N, G, S, NC>), g3, dim3(512), 0, st, a)
+#define MOE_NVD_S(N, G, NC)                                                                 \
+        do {                                                                                \
+            if (nsw == 4) MOE_NVD(N, G, 4, NC);                                             \
+            else if (nsw == 12) MOE_NVD(N, G, 12, NC);                                      \
+            else MOE_NVD(N, G, 16, NC);                                                     \
+        } while (0)
+#define MOE_NVD2(N, G)                                                                      \
+        do {                                                                                \
+            if (narrow) MOE_NVD_S(N, G, 2);                                                 \
+            else MOE_NVD_S(N, G, 2 * kNvTilePicks);                                         \
+        } while (0)
+        if (!gateup) MOE_NVD2(2, false);
+        else if (NT == 1) MOE_NVD2(1, true);
+        else MOE_NVD2(2, true);
+#undef MOE_NVD2
+#undef MOE_NVD_S
+#undef MOE_NVD
     } else {
         if (!gateup) MOE_NV(2, false, kNvTilePicks);
         else if (NT == 1) MOE_NV(1, true, kNvTilePicks);

@@ -403,7 +403,7 @@ hipError_t launch_gateup_dec(const GemmArgs& a, int NT, int max_tiles, hipStream
 hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineArgs& c, int NT, hipStream_t st);
 
 // NVFP4 (gemm_nv.hip): bf16 terms of fp32 activations, and the grouped GEMMs
-constexpr int kNvTilePicks = 8;          // few picks per expert
+constexpr int kNvTilePicks = 4;          // few picks per expert
 constexpr int kNvTilePicksMany = 64;     // many picks per expert: the LDS-tiled GEMM's tile
 int nv_tile_picks(const moe_shape* s, int T);
 constexpr int kStageGroup = 64;           // experts staged per group (NVFP4 layer with staging)
