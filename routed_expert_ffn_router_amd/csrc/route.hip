@@ -158,52 +158,52 @@ hipError_t launch_router_logits(const moe_shape* s, const void* x, int T, const 
 // top-k: one wave per token.  Each lane holds up to 16 logits (E <= 1024), sorted; k rounds each
 // take the wave's best head under the order (logit descending, index ascending, NaN last).
 // ---------------------------------------------------------------------------------------------
-// Does (la, a) rank before (lb, b)?  Larger logit first, then lower index; a NaN ranks after
-// every number (NaNs among themselves by index); -0 and +0 are equal.  Branch-free.
-__device__ __forceinline__ bool ranks_before(double la, int a, double lb, int b) {
-    const bool na = __builtin_isnan(la), nb = __builtin_isnan(lb);
-    const bool num = (la > lb) | ((la == lb) & (a < b));
-    const bool nan = nb & (!na | (a < b));
-    return (na | nb) ? nan : num;
+// The order is carried by an integer key per logit: larger logit, larger key; -0 and +0 share
+// one; a NaN has key 0, below every number.  Keys are compared as (key, expert index): equal
+// keys mean equal logits, and then the lower index ranks first.
+__device__ __forceinline__ unsigned long long logit_key(double v) {
+    unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    b = (b == 0x8000000000000000ull) ? 0ull : b;
+    const unsigned long long k = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+    return __builtin_isnan(v) ? 0ull : k;
+}
+// the logit of a key (keys of numbers; key 0 gives a NaN)
+__device__ __forceinline__ double key_logit(unsigned long long k) {
+    const unsigned long long b = (k >> 63) ? (k & 0x7fffffffffffffffull) : ~k;
+    return __longlong_as_double((long long)b);
 }
 
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ double dpp_max_f64(double v) {
-    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
-    const uint32_t lo = dpp_u32<CTRL, ROWMASK>((uint32_t)b, (uint32_t)b);
-    const uint32_t hi = dpp_u32<CTRL, ROWMASK>((uint32_t)(b >> 32), (uint32_t)(b >> 32));
-    return fmax(v, __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo)));
-}
-// largest value of the wave, a NaN lane ignored unless every lane is NaN (in every lane)
-__device__ __forceinline__ double wave_max_f64(double v) {
-    v = dpp_max_f64<kDppXor1, 0xF>(v);
-    v = dpp_max_f64<kDppXor2, 0xF>(v);
-    v = dpp_max_f64<kDppHalfMirror, 0xF>(v);
-    v = dpp_max_f64<kDppMirror, 0xF>(v);
-    v = dpp_max_f64<kDppBcast15, 0xA>(v);
-    v = dpp_max_f64<kDppBcast31, 0xC>(v);
-    return readlane_f64(v, 63);
-}
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ int dpp_min_i32(int v) {
-    return min(v, (int)dpp_u32<CTRL, ROWMASK>((uint32_t)v, (uint32_t)v));
+// Wave reductions of the top-k rounds, latency-bound: each of the six steps (xor 1, xor 2,
+// half-row mirror, row mirror, then row broadcasts 15 and 31 into the upper rows) is one VALU
+// op reading its permuted operand through DPP, after which lane 63 holds the result of the whole
+// wave.  The s_nop 1 before each step covers the DPP read of a VGPR written just before.  All
+// 64 lanes must be active.
+#define MOE_WAVE_REDUCE_DPP(op)                                                             \
+    "s_nop 1\n\t" op " %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"     \
+    "s_nop 1\n\t" op " %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"     \
+    "s_nop 1\n\t" op " %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"          \
+    "s_nop 1\n\t" op " %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"               \
+    "s_nop 1\n\t" op " %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"             \
+    "s_nop 1\n\t" op " %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"             \
+    "s_nop 1"
+// largest value of the wave (in every lane)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    asm volatile(MOE_WAVE_REDUCE_DPP("v_max_u32_dpp") : "+v"(v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 // smallest value of the wave (in every lane)
 __device__ __forceinline__ int wave_min_i32(int v) {
-    v = dpp_min_i32<kDppXor1, 0xF>(v);
-    v = dpp_min_i32<kDppXor2, 0xF>(v);
-    v = dpp_min_i32<kDppHalfMirror, 0xF>(v);
-    v = dpp_min_i32<kDppMirror, 0xF>(v);
-    v = dpp_min_i32<kDppBcast15, 0xA>(v);
-    v = dpp_min_i32<kDppBcast31, 0xC>(v);
+    asm volatile(MOE_WAVE_REDUCE_DPP("v_min_i32_dpp") : "+v"(v));
     return __builtin_amdgcn_readlane(v, 63);
 }
+#undef MOE_WAVE_REDUCE_DPP
 
 // Top-k of one token's E logits by one wave (E <= 64 * S, k <= E), written in rank order to
-// idx[0..k).  w[j] = sigmoid(l_j) / sum_j' sigmoid(l_j'), the sum taken in rank order.  Each lane
-// keeps its S logits sorted; a round takes the largest head (NaN only if every head is NaN) and
-// then the lowest expert index among the heads equal to it.  All 64 lanes must call it; lane
-// j%64 stores entry j.
+// idx[0..k).  w[j] = sigmoid(l_j) / sum_j' sigmoid(l_j'), the sum taken in rank order.  Lane l
+// holds experts l + 64 s, sorted by (key, index).  A round takes the lanes whose head has the
+// largest upper key half (a 32-bit wave max); when that is one lane, its head is the best.
+// Otherwise the lower key half decides among them, and for equal keys (equal logits) the lower
+// expert index.  All 64 lanes must call it; lane j%64 stores entry j.
 template <int S>
 __device__ __forceinline__ void topk_load(const double* __restrict__ l, int E, double (&lv)[S]) {
     const int lane = threadIdx.x & 63;
@@ -214,61 +214,98 @@ __device__ __forceinline__ void topk_load(const double* __restrict__ l, int E, d
     }
 }
 
+// The k rounds; lane j (j < min(k, 64)) returns the key of pick j.
 template <int S>
-__device__ void topk_select(const double (&lv)[S], const double* __restrict__ l, int E, int k, int32_t* idx,
-                            float* w) {
+__device__ __forceinline__ unsigned long long topk_rounds(const double (&lv)[S], int E, int k, int32_t* idx) {
     const int lane = threadIdx.x & 63;
-    // this lane's entries in rank order (odd-even transposition sort, S passes); slots past E
-    // hold NaN and index INT_MAX, which rank after every expert, and k <= E keeps them from
-    // being taken
-    double v[S];
-    int ei[S];
+    constexpr int kNone = 0x7fff;          // slot of an exhausted entry: index past every expert
+    // keys and slots (expert = lane + 64 * slot) of this lane's entries; slots past E hold key 0
+    // and rank after every expert, and k <= E keeps them from being taken
+    unsigned long long key[S];
+    int slot[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const int e = lane + 64 * s;
-        v[s] = (e < E) ? lv[s] : __builtin_nan("");
-        ei[s] = (e < E) ? e : 0x7fffffff;
+        const bool ok = lane + 64 * s < E;
+        key[s] = ok ? logit_key(lv[s]) : 0ull;
+        slot[s] = ok ? s : kNone;
     }
+    // rank order within the lane (odd-even transposition sort, S passes)
 #pragma unroll
     for (int pass = 0; pass < S; ++pass) {
 #pragma unroll
         for (int s = pass & 1; s + 1 < S; s += 2) {
-            const bool sw = ranks_before(v[s + 1], ei[s + 1], v[s], ei[s]);
-            const double v0 = v[s], v1 = v[s + 1];
-            const int i0 = ei[s], i1 = ei[s + 1];
-            v[s] = sw ? v1 : v0;
-            v[s + 1] = sw ? v0 : v1;
-            ei[s] = sw ? i1 : i0;
-            ei[s + 1] = sw ? i0 : i1;
+            const bool sw = (key[s + 1] > key[s]) | ((key[s + 1] == key[s]) & (slot[s + 1] < slot[s]));
+            const unsigned long long k0 = key[s], k1 = key[s + 1];
+            const int s0 = slot[s], s1 = slot[s + 1];
+            key[s] = sw ? k1 : k0;
+            key[s + 1] = sw ? k0 : k1;
+            slot[s] = sw ? s1 : s0;
+            slot[s + 1] = sw ? s0 : s1;
         }
     }
-    // k rounds: the winner's lane (its expert index mod 64) shifts its list up by one
-    double my_l = 0.0;
+    // k rounds: the winning lane shifts its list up by one
+    unsigned long long my_key = 0ull;
     for (int j = 0; j < k; ++j) {
-        const double m = wave_max_f64(v[0]);
-        const bool tied = __builtin_isnan(m) ? __builtin_isnan(v[0]) : (v[0] == m);
-        const int c = wave_min_i32(tied ? ei[0] : 0x7fffffff);
-        const bool win = (c & 63) == lane;
+        const uint32_t hk = (uint32_t)(key[0] >> 32);
+        const uint32_t mh = wave_max_u32(hk);
+        const unsigned long long c1 = __ballot(hk == mh);
+        int wl;
+        if (__popcll(c1) == 1) {
+            wl = __builtin_ctzll(c1);
+        } else {                            // equal upper halves: the lower half, then the index
+            const bool in1 = (c1 >> lane) & 1ull;
+            const uint32_t lk = (uint32_t)key[0];
+            const uint32_t ml = wave_max_u32(in1 ? lk : 0u);
+            const unsigned long long c2 = c1 & __ballot(lk == ml);
+            if (__popcll(c2) == 1) {
+                wl = __builtin_ctzll(c2);
+            } else {
+                const bool in2 = (c2 >> lane) & 1ull;
+                wl = wave_min_i32(in2 ? lane + 64 * slot[0] : 0x7fffffff) & 63;
+            }
+        }
+        const int c = wl + 64 * __builtin_amdgcn_readlane(slot[0], wl);
+        const uint32_t wlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[0], wl);
+        const uint32_t whi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key[0] >> 32), wl);
+        const bool win = wl == lane;
 #pragma unroll
         for (int s = 0; s + 1 < S; ++s) {
-            v[s] = win ? v[s + 1] : v[s];
-            ei[s] = win ? ei[s + 1] : ei[s];
+            key[s] = win ? key[s + 1] : key[s];
+            slot[s] = win ? slot[s + 1] : slot[s];
         }
-        v[S - 1] = win ? __builtin_nan("") : v[S - 1];
-        ei[S - 1] = win ? 0x7fffffff : ei[S - 1];
+        key[S - 1] = win ? 0ull : key[S - 1];
+        slot[S - 1] = win ? kNone : slot[S - 1];
         if ((j & 63) == lane) {
             idx[j] = c;
-            if (j < 64) my_l = m;
+            my_key = ((unsigned long long)whi << 32) | wlo;
         }
     }
-    // weights: every lane's sigmoid in parallel (of the selected logit: equal to m, or +0 for
-    // -0, which has the same sigmoid), the sum in rank order
-    const double sg = (lane < k) ? 1.0 / (1.0 + exp(-my_l)) : 0.0;
+    return my_key;
+}
+
+__device__ __forceinline__ double sigmoid64(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+// The weights of the k picks idx[0..k) (rank order) of one token, by one wave: lane j holds
+// pick j's key (from topk_rounds).  sig: the sigmoid of every expert's logit, computed
+// beforehand, or null (each lane computes its pick's: of the selected logit, where a -0 comes
+// back as +0, with the same sigmoid).  The sum is taken in rank order.
+__device__ __forceinline__ void topk_weights(unsigned long long my_key, const double* __restrict__ l,
+                                             const int32_t* idx, int k, float* w, const double* sig) {
+    const int lane = threadIdx.x & 63;
+    double sg = 0.0;
+    if (lane < k) sg = sig ? sig[idx[lane]] : sigmoid64(key_logit(my_key));
     double ssum = 0.0;
     for (int j = 0; j < k && j < 64; ++j) ssum += readlane_f64(sg, j);
-    for (int j = 64; j < k; ++j) ssum += 1.0 / (1.0 + exp(-l[idx[j]]));   // k > 64 only
+    for (int j = 64; j < k; ++j) ssum += sig ? sig[idx[j]] : sigmoid64(l[idx[j]]);   // k > 64 only
     if (lane < k) w[lane] = (float)(sg / ssum);
-    for (int j = lane + 64; j < k; j += 64) w[j] = (float)((1.0 / (1.0 + exp(-l[idx[j]]))) / ssum);
+    for (int j = lane + 64; j < k; j += 64) w[j] = (float)((sig ? sig[idx[j]] : sigmoid64(l[idx[j]])) / ssum);
+}
+
+template <int S>
+__device__ void topk_select(const double (&lv)[S], const double* __restrict__ l, int E, int k, int32_t* idx,
+                            float* w) {
+    const unsigned long long my_key = topk_rounds<S>(lv, E, k, idx);
+    topk_weights(my_key, l, idx, k, w, nullptr);
 }
 
 template <int S>
@@ -374,22 +411,26 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         }
     }
 
-    // the last workgroup to arrive finishes the routing: every thread makes its stores visible
-    // device-wide (release), one atomic per workgroup counts arrivals, and only the last one
-    // acquires, so the other workgroups leave without invalidating their cache
-    // acquires, so the other workgroups leave without invalidating their cache.  Those others, in
-    // arrival order, then split x into fp8 terms for the gate/up GEMM while the last one routes.
+    // the last workgroup to arrive finishes the routing.  The barrier orders every wave's logit
+    // stores before thread 0's device-scope release, which writes back the L2 once per workgroup
+    // (a fence in every thread would write it back once per wave, and a few hundred write-backs
+    // per launch cost microseconds); one atomic per workgroup counts arrivals, and only the last
+    // workgroup's thread 0 acquires (one L2 invalidate).  The others, in arrival order, then
+    // split x into fp8 terms for the gate/up GEMM while the last one routes.
     __shared__ int s_ticket;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int G = (int)gridDim.x;
     __syncthreads();
-    if (tid == 0) s_ticket = (int)__hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        s_ticket = (int)__hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (s_ticket == G - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
     __syncthreads();
-    const int G = (int)gridDim.x, ticket = s_ticket;
+    const int ticket = s_ticket;
     if (ticket != G - 1) {
         if (a.split) split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, ticket, G - 1);
         return;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (G == 1 && a.split) split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, 0, 1);
 
     __shared__ int32_t s_idx[kMaxFusedPicks];
@@ -398,18 +439,11 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     __shared__ uint8_t s_start[kMaxFusedPicks];     // sorted position starts a tile
     const int P = T * k, tt = a.tt;
     // the routed tokens' logits (up to four per wave) and, for E <= kTabLds, the whole expert
-    // table are requested in one round; the table goes to LDS while the top-k runs
+    // table are requested in one round, the logits first; the table goes to LDS while the
+    // top-k runs
     constexpr int kTabLds = 320, kTabRounds = (kTabLds * 4 + 255) / 256;
     constexpr bool tab_lds = S <= 5;
     __shared__ uint4 s_tab[tab_lds ? kTabLds * 4 : 1];
-    uint4 tab[tab_lds ? kTabRounds : 1];
-    if constexpr (tab_lds) {
-#pragma unroll
-        for (int r = 0; r < kTabRounds; ++r) {
-            const int g = r * 256 + tid;
-            tab[r] = ((const uint4*)a.table)[g < 4 * E ? g : 4 * E - 1];
-        }
-    }
     constexpr int J = tab_lds ? kSmallT / 4 : 1;     // tokens whose logits are preloaded per wave
     double lv[J][S];
     if (wave < T) {
@@ -417,6 +451,14 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         for (int j = 0; j < J; ++j) {
             const int t = wave + 4 * j;
             topk_load<S>(a.logits + (size_t)(t < T ? t : T - 1) * E, E, lv[j]);
+        }
+    }
+    uint4 tab[tab_lds ? kTabRounds : 1];
+    if constexpr (tab_lds) {
+#pragma unroll
+        for (int r = 0; r < kTabRounds; ++r) {
+            const int g = r * 256 + tid;
+            tab[r] = ((const uint4*)a.table)[g < 4 * E ? g : 4 * E - 1];
         }
     }
     if constexpr (tab_lds) {
@@ -428,7 +470,19 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             if (g < 4 * E) s_tab[g] = tab[r];
         }
     }
-    if (wave < T) {
+    if (T == 1 && tab_lds) {
+        // one token: wave 0 runs the rounds while the other three waves take the sigmoid of every
+        // expert's logit, so that the weights need only the sum and the divisions
+        __shared__ double s_sig[kTabLds];
+        unsigned long long my_key = 0ull;
+        if (wave == 0) {
+            my_key = topk_rounds<S>(lv[0], E, k, s_idx);
+        } else {
+            for (int e = tid - 64; e < E; e += 192) s_sig[e] = sigmoid64(a.logits[e]);
+        }
+        __syncthreads();
+        if (wave == 0) topk_weights(my_key, a.logits, s_idx, k, s_w, s_sig);
+    } else if (wave < T) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int t = wave + 4 * j;
@@ -438,6 +492,64 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             wave_topk<S>(a.logits + (size_t)t * E, E, k, s_idx + t * k, s_w + t * k);
     }
     __syncthreads();
+    // the expert-table entry of expert e into a tile record: four 16-byte moves, from the LDS copy
+    // of the table when there is one
+    auto put_expert = [&](TileDesc* D, int e) {
+        const uint4* src = tab_lds ? &s_tab[4 * e] : (const uint4*)(a.table + e);
+        uint4* dst = (uint4*)&D->ex;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = src[i];
+    };
+    // an empty record still names a real expert (the first pick's), so that a stray read of its
+    // pointers stays inside the weights
+    auto put_empty = [&](int id) {
+        TileDesc* D = a.desc + id;
+        put_expert(D, s_idx[0]);
+        D->i0 = 0;
+        D->ntok = 0;
+        D->e = s_idx[0];
+    };
+    // the expert offsets: the number of picks of lower experts
+    auto put_offsets = [&]() {
+        for (int e = tid; e <= E; e += 256) {
+            int lower = 0;
+#pragma unroll 8
+            for (int q = 0; q < P; ++q) lower += s_idx[q] < e;
+            a.offsets[e] = lower;
+        }
+    };
+    if (T == 1) {
+        // one token: its k experts are distinct, so each pick is a tile of its own, and its
+        // sorted position is the number of picks of lower experts (what the grouping below
+        // gives in this case, without its scans)
+        for (int p = tid; p < k; p += 256) {
+            const int e = s_idx[p];
+            int pos = 0;
+#pragma unroll 8
+            for (int q = 0; q < k; ++q) pos += s_idx[q] < e;
+            TileDesc* D = a.desc + pos;
+            put_expert(D, e);
+            D->i0 = pos;
+            D->ntok = 1;
+            D->e = e;
+            D->pad0 = 0;
+#pragma unroll
+            for (int c = 0; c < kDescTokens; ++c) D->tok[c] = 0;
+            a.tiles[2 * pos] = e;
+            a.tiles[2 * pos + 1] = pos;
+            a.idx[p] = e;
+            a.w[p] = s_w[p];
+            a.pick_pos[p] = pos;
+            a.sorted_pick[pos] = p;
+        }
+        put_offsets();
+        for (int id = k + tid; id < a.max_tiles; id += 256) put_empty(id);
+        if (tid == 0) {
+            *a.ntiles = k;
+            *a.counter = 0u;
+        }
+        return;
+    }
     // Grouping without atomics or scans (P <= 512, two picks per thread): a pick's sorted
     // position is the number of picks of lower experts plus its rank among the picks of its own
     // expert; it starts a tile when that rank is a multiple of tt.
@@ -449,6 +561,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         if (p < P) {
             const int e = s_idx[p];
             int lower = 0, before = 0, same = 0;
+#pragma unroll 8
             for (int q = 0; q < P; ++q) {
                 const int eq = s_idx[q];
                 lower += eq < e;
@@ -466,25 +579,14 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             a.sorted_pick[pos[u]] = p;
         }
     }
-    for (int e = tid; e <= E; e += 256) {
-        int lower = 0;
-        for (int q = 0; q < P; ++q) lower += s_idx[q] < e;
-        a.offsets[e] = lower;
-    }
+    put_offsets();
     __syncthreads();
-    // the expert-table entry of expert e into a tile record: four 16-byte moves, from the LDS copy
-    // of the table when there is one
-    auto put_expert = [&](TileDesc* D, int e) {
-        const uint4* src = tab_lds ? &s_tab[4 * e] : (const uint4*)(a.table + e);
-        uint4* dst = (uint4*)&D->ex;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = src[i];
-    };
     // tiles: numbered by sorted position of their first pick
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         if (pos[u] >= 0 && s_start[pos[u]]) {
             int id = 0;
+#pragma unroll 8
             for (int q = 0; q < pos[u]; ++q) id += s_start[q];
             const int ntok = min(tt, cnt[u] - rank[u]);
             TileDesc* D = a.desc + id;
@@ -500,16 +602,9 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     }
     // the tile count, and empty records up to max_tiles
     int nt = 0;
+#pragma unroll 8
     for (int q = 0; q < P; ++q) nt += s_start[q];
-    for (int id = nt + tid; id < a.max_tiles; id += 256) {
-        // an empty record still names a real expert (the first pick's), so that a stray read of
-        // its pointers stays inside the weights
-        TileDesc* D = a.desc + id;
-        put_expert(D, s_idx[0]);
-        D->i0 = 0;
-        D->ntok = 0;
-        D->e = s_idx[0];
-    }
+    for (int id = nt + tid; id < a.max_tiles; id += 256) put_empty(id);
     if (tid == 0) {
         *a.ntiles = nt;
         *a.counter = 0u;
