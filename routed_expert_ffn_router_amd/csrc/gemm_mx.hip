@@ -320,26 +320,25 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
     const int nrg = a.f / 32;
     for (int pair = blockIdx.x;; pair += nwg) {          // nwg = grid size, passed as an argument
     const int tile = __builtin_amdgcn_readfirstlane(pair / nrg), rg = __builtin_amdgcn_readfirstlane(pair % nrg);
-    // one round trip: the 128-byte tile record (lane l holds bytes 16(l%8)..+16) and the tile count
-    const uint8_t* rec_base = (const uint8_t*)(a.desc + tile);
-    const uint4 rec = gload16(rec_base + 16 * (lane & 7));
-    const int nt = gload_i32(a.ntiles);
-    asm volatile("" ::"v"(rec.x), "v"(rec.y), "v"(rec.z), "v"(rec.w), "v"(nt));
-    auto field64 = [&](int byte) -> const uint8_t* {
-        const uint32_t comp[4] = {rec.x, rec.y, rec.z, rec.w};
-        const int l = byte / 16, c = (byte % 16) / 4;
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)comp[c], l);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)comp[c + 1], l);
-        return (const uint8_t*)(((uint64_t)hi << 32) | lo);
-    };
-    const int ntile_count = __builtin_amdgcn_readfirstlane(nt);
+    // one round trip on the scalar path: the tile count and the tile record's fields (the vector
+    // path would queue them behind the weight loads of the other workgroup on this CU)
+    const TileDesc* D = a.desc + tile;
+    const int32_t* ntp = a.ntiles;
+    asm volatile("" : "+s"(ntp));     // read with the record in one round trip, not hoisted ahead of it
+    const int ntile_count = sload(ntp);
+    const uint8_t* const gq = sload(&D->ex.gate_q);
+    const uint8_t* const uq = sload(&D->ex.up_q);
+    const uint8_t* const gs = sload(&D->ex.gate_s);
+    const uint8_t* const us = sload(&D->ex.up_s);
+    const int i0 = sload(&D->i0);
+    const int ntok = sload(&D->ntok);
+    static_assert(kDescTokens == 8, "token fields of a tile record");
+    const int tk0 = sload(&D->tok[0]), tk1 = sload(&D->tok[1]), tk2 = sload(&D->tok[2]), tk3 = sload(&D->tok[3]);
+    const int tk4 = sload(&D->tok[4]), tk5 = sload(&D->tok[5]), tk6 = sload(&D->tok[6]), tk7 = sload(&D->tok[7]);
+    // all of them requested before the first wait
+    asm volatile("" ::"s"(ntile_count), "s"(gq), "s"(uq), "s"(gs), "s"(us), "s"(i0), "s"(ntok), "s"(tk0), "s"(tk1),
+                 "s"(tk2), "s"(tk3), "s"(tk4), "s"(tk5), "s"(tk6), "s"(tk7));
     if (tile >= ntile_count) break;
-    const uint8_t* const gq = field64(offsetof(moe_expert, gate_q));
-    const uint8_t* const uq = field64(offsetof(moe_expert, up_q));
-    const uint8_t* const gs = field64(offsetof(moe_expert, gate_s));
-    const uint8_t* const us = field64(offsetof(moe_expert, up_s));
-    const int i0 = __builtin_amdgcn_readlane((int)rec.x, offsetof(TileDesc, i0) / 16);
-    const int ntok = __builtin_amdgcn_readlane((int)rec.y, offsetof(TileDesc, i0) / 16);
     const int row = 32 * rg + 16 * (f & 1) + li;
     const int kss0 = ks * nss;
     // 1. the tile's x terms (ncol columns of K code bytes and K/32 scale bytes) are staged in LDS,
@@ -361,15 +360,13 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
     auto chunk_dst = [&](int g, int c, int off) -> uint4* {
         return g < nchunk ? (uint4*)&b_lds[c][off] : (uint4*)&bs_lds[c][off];
     };
-    // token of a chunk's column: tok[c / NT] of the record, fetched from lanes 5-6 of `rec`
+    // token of a chunk's column: tok[c / NT] of the record
     auto chunk_tok = [&](int c) {
-        const int ti = c / NT, src = (5 + (ti >> 2)) << 2;
-        const int cx = __builtin_amdgcn_ds_bpermute(src, (int)rec.x);
-        const int cy = __builtin_amdgcn_ds_bpermute(src, (int)rec.y);
-        const int cz = __builtin_amdgcn_ds_bpermute(src, (int)rec.z);
-        const int cw = __builtin_amdgcn_ds_bpermute(src, (int)rec.w);
-        const int sel = ti & 3;
-        return sel == 0 ? cx : (sel == 1 ? cy : (sel == 2 ? cz : cw));
+        const int ti = c / NT;
+        const int a01 = (ti & 1) ? tk1 : tk0, a23 = (ti & 1) ? tk3 : tk2;
+        const int a45 = (ti & 1) ? tk5 : tk4, a67 = (ti & 1) ? tk7 : tk6;
+        const int a03 = (ti & 2) ? a23 : a01, a47 = (ti & 2) ? a67 : a45;
+        return (ti & 4) ? a47 : a03;
     };
     const int g0 = tid < ntotal ? tid : ntotal - 1;
     int off0;
@@ -397,7 +394,7 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
     for (int g = tid + 512; g < ntotal; g += 512) {      // more than 512 chunks: tiles of many picks
         int off;
         const int c = chunk_col(g, off);
-        const int tok = gload_i32(&(a.desc + tile)->tok[c / NT]);   // divergent: no lane permute here
+        const int tok = chunk_tok(c);
         const uint4 v = gload16(chunk_src(g, tok, c, off));
         *chunk_dst(g, c, off) = v;
     }
@@ -566,17 +563,20 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
     }
     __syncthreads();
     // 2. every pick's h codes and scales (first P*NT rows of the h terms) for LDS: requested
-    // before the weights, so that waiting for them does not wait for the weights
+    // before the weights, so that waiting for them does not wait for the weights; only the rounds
+    // that hold chunks (the round count is uniform)
     const int nb = ncols * (K / 16), ntot = nb + ncols * (K / 512);
     uint4 v[kDownFillRounds];
 #pragma unroll
     for (int r = 0; r < kDownFillRounds; ++r) {
-        int g = r * 512 + tid;
-        g = g < ntot ? g : ntot - 1;
-        // one address by selects, one load: no branch between the loads of the round
-        const uintptr_t base = g < nb ? (uintptr_t)a.aq : (uintptr_t)a.as;
-        const int gi = g < nb ? g : g - nb;
-        v[r] = gload16((const void*)(base + (size_t)gi * 16));
+        if (r * 512 < ntot) {
+            int g = r * 512 + tid;
+            g = g < ntot ? g : ntot - 1;
+            // one address by selects, one load: no branch between the loads of the round
+            const uintptr_t base = g < nb ? (uintptr_t)a.aq : (uintptr_t)a.as;
+            const int gi = g < nb ? g : g - nb;
+            v[r] = gload16((const void*)(base + (size_t)gi * 16));
+        }
     }
     // 3. the weights of this wave's first two units (tile, K slice): u0 = wave, u1 = wave + 8
     const int units = a.max_tiles * nsl;
@@ -648,9 +648,10 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
     int us[2];
     load_units(wave, A, sa, ok0, ok1, us);
     __builtin_amdgcn_sched_barrier(0);
-    // 4. h terms into LDS (their loads were issued first), then the MFMAs of the first units
+    // 4. h terms into LDS, then the MFMAs of the first units
 #pragma unroll
-    for (int r = 0; r < kDownFillRounds; ++r) asm volatile("" ::"v"(v[r].x), "v"(v[r].y), "v"(v[r].z), "v"(v[r].w));
+    for (int r = 0; r < kDownFillRounds; ++r)
+        if (r * 512 < ntot) asm volatile("" ::"v"(v[r].x), "v"(v[r].y), "v"(v[r].z), "v"(v[r].w));
 #pragma unroll
     for (int r = 0; r < kDownFillRounds; ++r) {
         const int g = r * 512 + tid;

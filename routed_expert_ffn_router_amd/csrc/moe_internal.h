@@ -90,6 +90,13 @@ __device__ __forceinline__ uint32_t gload4(const void* p) {
 __device__ __forceinline__ int32_t gload_i32(const void* p) {
     return *(__attribute__((address_space(1))) const int32_t*)p;
 }
+// A load of wave-uniform data through the scalar path (s_load into SGPRs): it does not queue
+// behind the vector memory requests of the CU.  Only for data that no wave writes during the
+// kernel (the scalar cache is invalidated when a kernel starts), at a wave-uniform address.
+template <typename T>
+__device__ __forceinline__ T sload(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
 
 // ---------------------------------------------------------------------------------------------
 // element formats (device side)
