@@ -373,21 +373,23 @@ hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t*
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallT = 16;
 
-// NC = float4 chunks per lane of a router row (d <= 256 * NC).  Every load is issued without a
-// condition (chunks past the row re-read its last chunk and are not used), so that no branch
-// separates them and all of a wave's loads are in flight together.
+// NC = float4 chunks per lane of a router row (d <= 256 * NC, d a multiple of 4).  Every load is
+// issued without a condition (reads past the row re-read its last four elements and are not
+// used), so that no branch separates them and all of a wave's loads are in flight together.
 template <typename XT, int NT, int S, int NC>
 __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     const XT* __restrict__ x = (const XT*)a.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
     const int T = a.T, d = a.d, E = a.E, k = a.k;
-    // 1. issue the loads of this wave's whole router row
+    // 1. issue the loads of this wave's whole router row.  Lane l reads elements 256 u + 4 l ..
+    // +3; reads past the row are clamped to its last four and not used.
     const int e = blockIdx.x * 4 + wave;
-    const int nw = d / 256;
+    auto at = [&](int u) { return min(u * 256 + lane * 4, d - 4); };
+    auto used = [&](int u) { return u * 256 + lane * 4 < d; };
     float4 w4[NC];
     const float* row = a.wr + (size_t)(e < E ? e : 0) * d;
 #pragma unroll
-    for (int u = 0; u < NC; ++u) w4[u] = *(const float4*)(row + (u < nw ? u : nw - 1) * 256 + lane * 4);
+    for (int u = 0; u < NC; ++u) w4[u] = *(const float4*)(row + at(u));
     // 2. logits, fp64 accumulation of exact products
     if (e < E) {
 #pragma unroll 1
@@ -395,16 +397,15 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             const XT* xt = x + (size_t)t * d;
             float4 x4[NC];
 #pragma unroll
-            for (int u = 0; u < NC; ++u) x4[u] = load_act4(xt, (u < nw ? u : nw - 1) * 256 + lane * 4);
+            for (int u = 0; u < NC; ++u) x4[u] = load_act4(xt, at(u));
             double acc = 0.0;
 #pragma unroll
             for (int u = 0; u < NC; ++u) {
-                if (u < nw) {
-                    acc = fma((double)x4[u].x, (double)w4[u].x, acc);
-                    acc = fma((double)x4[u].y, (double)w4[u].y, acc);
-                    acc = fma((double)x4[u].z, (double)w4[u].z, acc);
-                    acc = fma((double)x4[u].w, (double)w4[u].w, acc);
-                }
+                double p = fma((double)x4[u].x, (double)w4[u].x, acc);
+                p = fma((double)x4[u].y, (double)w4[u].y, p);
+                p = fma((double)x4[u].z, (double)w4[u].z, p);
+                p = fma((double)x4[u].w, (double)w4[u].w, p);
+                acc = used(u) ? p : acc;
             }
             acc = wave_sum_f64(acc);
             if (lane == 0) a.logits[(size_t)t * E + e] = a.bias ? acc + (double)a.bias[e] : acc;

@@ -117,6 +117,9 @@ SMALL_CASES = [
     ("tiny", dict(d_model=384, d_ff=640, n_experts=8, top_k=2, act_dtype=synth.BF16), 150),
     # 7 K steps: one full group of four plus a tail of three
     ("tiny", dict(d_model=896, d_ff=256, n_experts=12, top_k=3, act_dtype=synth.BF16), 100),
+    # few tokens, router rows not a whole number of 256-element chunks per half (fused router)
+    ("tiny", dict(d_model=384, d_ff=256, n_experts=16, top_k=2, act_dtype=synth.BF16), 4),
+    ("tiny", dict(d_model=640, d_ff=256, n_experts=9, top_k=3), 2),
 ]
 
 
