@@ -404,6 +404,8 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
     constexpr int CST = KMAX * 2 + 16;               // column stride in LDS (bf16, padded)
     __shared__ __align__(16) uint8_t b_lds[NCOL * CST];
     __shared__ v4f_nv part[8][64];
+    __shared__ __align__(16) uint8_t s_sc[8][16][128];   // per wave: its rows' scale bytes of its K quarter
+    static_assert(NSW * 8 <= 128 && NSW % 4 == 0, "a K quarter's scale bytes: 8 per super-step and row");
     const int tile = blockIdx.x;
     int t0 = 0, t1 = *a.ntiles;
     if (a.tile_range) {
@@ -439,18 +441,27 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
     const uint8_t* mq = GATEUP ? (f == 0 ? ex.gate_q : ex.up_q) : ex.down_q;
     const uint8_t* ms = GATEUP ? (f == 0 ? ex.gate_s : ex.up_s) : ex.down_s;
     const uint8_t* aq = mq + (size_t)row * (K / 2) + (size_t)s0 * 64 + lg * 16;
-    const uint8_t* as = ms + (size_t)row * (K / 16) + (size_t)s0 * 8 + lg * 2;
     uint4 A[NSW];
-    uint32_t sc[NSW];
 #pragma unroll
     for (int q = 0; q < NSW; ++q) {
         const int qq = q < nss ? q : (nss > 0 ? nss - 1 : 0);
         A[q] = gload16(aq + (size_t)qq * 64);
-        sc[q] = *(const uint16_t*)(as + (size_t)qq * 8);
+    }
+    // the scale bytes of this wave's quarter, 8 per super-step and row: lane (li, lg) loads those
+    // of super-steps lg, lg + 4, .. of row li (past nss: super-step nss - 1 again, not used), one
+    // 8-byte load each, for LDS with the columns
+    const uint8_t* srow = ms + (size_t)row * (K / 16) + (size_t)s0 * 8;
+    uint2 S2[NSW / 4];
+#pragma unroll
+    for (int i = 0; i < NSW / 4; ++i) {
+        const int q = 4 * i + lg, qq = q < nss ? q : (nss > 0 ? nss - 1 : 0);
+        S2[i] = *(const uint2*)(srow + (size_t)qq * 8);
     }
     // 3. the columns into LDS (further rounds, for many columns, after the weights)
     asm volatile("" ::"v"(v0.x), "v"(v0.y), "v"(v0.z), "v"(v0.w));
     if (tid < nchunk) *(uint4*)(b_lds + (size_t)(g0 / cpc) * cst + (size_t)(g0 % cpc) * 16) = v0;
+#pragma unroll
+    for (int i = 0; i < NSW / 4; ++i) *(uint2*)&s_sc[wave][li][8 * (4 * i + lg)] = S2[i];
     for (int g = tid + 512; g < nchunk; g += 512)
         *(uint4*)(b_lds + (size_t)(g / cpc) * cst + (size_t)(g % cpc) * 16) = gload16(chunk_src(g));
     __syncthreads();
@@ -462,7 +473,7 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
 #pragma unroll
     for (int q = 0; q < NSW; ++q) {
         if (q < nss) {
-            const v2f_t bs = e4m3x2_to_f32(sc[q]);
+            const v2f_t bs = e4m3x2_to_f32(*(const uint16_t*)&s_sc[wave][li][8 * q + 2 * lg]);
             const uint32_t w[4] = {A[q].x, A[q].y, A[q].z, A[q].w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
