@@ -367,34 +367,41 @@ hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t*
 
 // ---------------------------------------------------------------------------------------------
 // fused router for few tokens (T <= 16), one launch per layer: every workgroup computes the fp64
-// logits of 4 experts (one wave each); the last workgroup to finish (device-scope counter) does
-// the top-k, the grouping and the tile records, then resets the counter to zero for the next
-// launch, while the others split x into fp8 terms (when the GEMMs read them).
+// logits of 4 experts (a wave each; rows longer than 4096: 2 experts, two waves each); the last
+// workgroup to finish (device-scope counter) does the top-k, the grouping and the tile records,
+// then resets the counter to zero for the next launch, while the others split x into fp8 terms
+// (when the GEMMs read them).
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallT = 16;
 
-// NC = float4 chunks per lane of a router row (d <= 256 * NC, d a multiple of 4).  Every load is
-// issued without a condition (reads past the row re-read its last four elements and are not
-// used), so that no branch separates them and all of a wave's loads are in flight together.
-template <typename XT, int NT, int S, int NC>
+// RW router rows per workgroup: 4 (a wave per row) or 2 (two waves per row, each with half of
+// it, for long rows).  NC = float4 chunks per lane of a wave's part of a row (d / (4 / RW) <= 256
+// NC, d a multiple of 8).  Every load is issued without a condition (reads past the part re-read
+// its last four elements and are not used), so that no branch separates them and all of a
+// wave's loads are in flight together.
+template <typename XT, int NT, int S, int NC, int RW>
 __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     const XT* __restrict__ x = (const XT*)a.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
     const int T = a.T, d = a.d, E = a.E, k = a.k;
-    // 1. issue the loads of this wave's whole router row.  Lane l reads elements 256 u + 4 l ..
-    // +3; reads past the row are clamped to its last four and not used.
-    const int e = blockIdx.x * 4 + wave;
-    auto at = [&](int u) { return min(u * 256 + lane * 4, d - 4); };
-    auto used = [&](int u) { return u * 256 + lane * 4 < d; };
+    // 1. issue the loads of this wave's part of its router row.  Lane l reads elements 256 u +
+    // 4 l .. +3 of the part; reads past it are clamped to its last four and not used.
+    constexpr int WPR = 4 / RW;
+    static_assert(RW * WPR == 4, "four waves per workgroup");
+    const int e = blockIdx.x * RW + wave / WPR, part = wave % WPR;
+    const int pl = d / WPR;
+    auto at = [&](int u) { return min(u * 256 + lane * 4, pl - 4); };
+    auto used = [&](int u) { return u * 256 + lane * 4 < pl; };
     float4 w4[NC];
-    const float* row = a.wr + (size_t)(e < E ? e : 0) * d;
+    const float* row = a.wr + (size_t)(e < E ? e : 0) * d + (size_t)part * pl;
 #pragma unroll
     for (int u = 0; u < NC; ++u) w4[u] = *(const float4*)(row + at(u));
-    // 2. logits, fp64 accumulation of exact products
+    // 2. logits, fp64 accumulation of exact products (the parts of a row added in order)
+    __shared__ double s_part[4][kSmallT];
     if (e < E) {
 #pragma unroll 1
         for (int t = 0; t < T; ++t) {
-            const XT* xt = x + (size_t)t * d;
+            const XT* xt = x + (size_t)t * d + (size_t)part * pl;
             float4 x4[NC];
 #pragma unroll
             for (int u = 0; u < NC; ++u) x4[u] = load_act4(xt, at(u));
@@ -408,7 +415,21 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 acc = used(u) ? p : acc;
             }
             acc = wave_sum_f64(acc);
-            if (lane == 0) a.logits[(size_t)t * E + e] = a.bias ? acc + (double)a.bias[e] : acc;
+            if constexpr (WPR == 1) {
+                if (lane == 0) a.logits[(size_t)t * E + e] = a.bias ? acc + (double)a.bias[e] : acc;
+            } else {
+                if (lane == 0) s_part[wave][t] = acc;
+            }
+        }
+    }
+    if constexpr (WPR == 2) {
+        __syncthreads();
+        if (tid < RW * T) {
+            const int j = tid % RW, t = tid / RW, ej = blockIdx.x * RW + j;
+            if (ej < E) {
+                const double v = s_part[2 * j][t] + s_part[2 * j + 1][t];
+                a.logits[(size_t)t * E + ej] = a.bias ? v + (double)a.bias[ej] : v;
+            }
         }
     }
 
@@ -614,20 +635,22 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
 
 hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipStream_t st) {
     trace("route_small", 0, st);
-    dim3 grid((s->n_experts + 3) / 4);
+    // rows up to 4096: a wave per row; longer (up to 8192): two waves per row
+    const int RW = s->d_model <= 4096 ? 4 : 2;
+    dim3 grid((s->n_experts + RW - 1) / RW);
     const bool bf = s->act_dtype == MOE_DT_BF16;
-#define MOE_RS(XT, N, NC)                                                                            \
-    do {                                                                                             \
-        if (s->n_experts <= 320) MOE_LAUNCH((k_route_small<XT, N, 5, NC>), grid, dim3(256), 0, st, a); \
-        else MOE_LAUNCH((k_route_small<XT, N, 16, NC>), grid, dim3(256), 0, st, a);              \
+#define MOE_RS(XT, N, R)                                                                                \
+    do {                                                                                                \
+        if (s->n_experts <= 320) MOE_LAUNCH((k_route_small<XT, N, 5, 16, R>), grid, dim3(256), 0, st, a); \
+        else MOE_LAUNCH((k_route_small<XT, N, 16, 16, R>), grid, dim3(256), 0, st, a);              \
     } while (0)
     // activation terms: 2 for bf16 activations, 4 for fp32 (act_terms)
     if (bf) {
-        if (s->d_model <= 4096) MOE_RS(uint16_t, 2, 16);
-        else MOE_RS(uint16_t, 2, 32);
+        if (RW == 4) MOE_RS(uint16_t, 2, 4);
+        else MOE_RS(uint16_t, 2, 2);
     } else {
-        if (s->d_model <= 4096) MOE_RS(float, 4, 16);
-        else MOE_RS(float, 4, 32);
+        if (RW == 4) MOE_RS(float, 4, 4);
+        else MOE_RS(float, 4, 2);
     }
 #undef MOE_RS
     trace("route_small", 1, st);
