@@ -995,14 +995,30 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
         PfFrags& nxt = (Q & 1) ? fr0 : fr1;
         wait_vm<2 * kPfLoads + (((Q & 3) == 1 || (Q & 3) == 2) ? kScLoads : 0)>();
         ring_barrier();                                      // also: every wave has stage s in registers
+        __builtin_amdgcn_sched_barrier(0);
         issue(min(s + 4, last), stage_buf(StepPos<Q & 3>{}));
         if constexpr ((Q & 3) == 0) issue_scales((s >> 2) + 1, scale_buf(StepPos<((Q >> 2) + 1) & 1>{}));
         pf_read<GATEUP>(stage_buf(StepPos<(Q + 1) & 3>{}), scale_buf(StepPos<((Q + 1) >> 2) & 1>{}), (Q + 1) & 3,
                         nxt, wm, wn, lane);
-        // the reads of step s + 1 are issued before the MFMAs of step s, which do not wait for
-        // them; no MFMA of step s + 1 is hoisted above the next barrier to wait for them here
-        __builtin_amdgcn_sched_barrier(0);
         pf_mfma(cur, acc);
+        // schedule: the step's direct loads (NV) and its 28 LDS reads of step s + 1 go between the
+        // 32 MFMAs of step s, one MFMA, one direct load and one LDS read at a time, so that their
+        // issue hides under the matrix core's work (with one wave per SIMD nothing else would);
+        // the MFMAs do not wait for those reads, and no MFMA of step s + 1 is hoisted above the
+        // next barrier
+        constexpr int NV = kPfLoads + ((Q & 3) == 0 ? kScLoads : 0);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 28 - NV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     int s = 0;
