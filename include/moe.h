@@ -106,9 +106,9 @@ size_t moe_blob_stride(const moe_shape *shape);
 
 /* Bytes of workspace the entry points need for T tokens (moe_layer needs the most; every
  * other call needs no more).  Returns 0 for a bad shape or T.  A workspace must be zero-filled
- * once before its first use (a memset at allocation): moe_layer keeps a completion counter in
- * it that every call leaves at zero again.  Calls that overlap in time need distinct
- * workspaces. */
+ * once before its first use (a memset at allocation): for T <= 16, moe_layer hands the router
+ * logits over through slots in it that every call leaves at zero again.  Calls that overlap in
+ * time need distinct workspaces. */
 size_t moe_workspace_bytes(const moe_shape *shape, int32_t T);
 
 /* Fill a DEVICE expert table from n_experts blobs laid out at base + e * stride (stride >=

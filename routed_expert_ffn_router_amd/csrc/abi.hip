@@ -46,7 +46,12 @@ WsLayout ws_layout(const moe_shape* s, int32_t T) {
     L.max_tiles = (int)((E < P ? E : P) + P / tt + 1);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
-    L.counter = take(4);
+    // the fused router's logit hand-over: the same bytes in the layout of every T, used by nothing
+    // else, so that calls with different T on one workspace keep it zero
+    L.slots = take(8 * (size_t)kSmallTokens * E);
+    // write-only scratch of the one-token router's warm-up pass
+    const size_t sink_rec = sizeof(TileDesc) * (size_t)L.max_tiles, sink_slots = 8 * (E + 1);
+    L.sink = take(sink_rec > sink_slots ? sink_rec : sink_slots);
     L.logits = take(8 * (size_t)T * E * (size_t)logits_splits(s, T));   // partial slices of the tiled router
     L.idx = take(4 * P);
     L.w = take(4 * P);
@@ -353,7 +358,8 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
         r.wr = w_router;
         r.bias = logit_bias;
         r.logits = logits;
-        r.counter = (uint32_t*)(w8 + L.counter);
+        r.slots = (unsigned long long*)(w8 + L.slots);
+        r.sink = w8 + L.sink;
         r.idx = idx;
         r.w = w;
         r.offsets = offsets;

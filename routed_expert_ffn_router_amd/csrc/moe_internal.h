@@ -314,7 +314,7 @@ struct TileDesc {
 static_assert(sizeof(TileDesc) == 128, "tile record is 128 bytes");
 
 struct WsLayout {
-    size_t counter, logits, idx, w, offsets, sorted_pick, pick_pos, tiles, ntiles, desc, xq, xs, hq, hs, o;
+    size_t slots, sink, logits, idx, w, offsets, sorted_pick, pick_pos, tiles, ntiles, desc, xq, xs, hq, hs, o;
     size_t stage_table, stage_list, stage_n, stage_ranges;   // NVFP4 staging (moe_layer)
     size_t total;
     int nt;        // activation terms
@@ -345,7 +345,9 @@ struct RouteSmallArgs {
     const float* wr;
     const float* bias;
     double* logits;
-    uint32_t* counter;        // zero before the launch; the launch leaves it zero
+    unsigned long long* slots;  // [T][E] logit hand-over, zero before the launch; the launch leaves it zero
+    void* sink;               // write-only scratch for the one-token warm-up pass: >= 8 (E + 1) bytes and
+                              // >= max_tiles records
     int32_t* idx;
     float* w;
     int32_t* offsets;

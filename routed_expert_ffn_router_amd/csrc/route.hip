@@ -197,6 +197,17 @@ __device__ __forceinline__ int wave_min_i32(int v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 #undef MOE_WAVE_REDUCE_DPP
+// largest value of each 16-lane row, in every lane of the row (the first four steps above: the
+// mirrors leave the row's maximum in all of its lanes)
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+    asm volatile("s_nop 1\n\tv_max_u32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1\n\tv_max_u32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1\n\tv_max_u32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1\n\tv_max_u32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1"
+                 : "+v"(v));
+    return v;
+}
 
 // Top-k of one token's E logits by one wave (E <= 64 * S, k <= E), written in rank order to
 // idx[0..k).  w[j] = sigmoid(l_j) / sum_j' sigmoid(l_j'), the sum taken in rank order.  Lane l
@@ -214,9 +225,11 @@ __device__ __forceinline__ void topk_load(const double* __restrict__ l, int E, d
     }
 }
 
-// The k rounds; lane j (j < min(k, 64)) returns the key of pick j.
+// The k rounds over the keys kv (lane l: experts l + 64 s; entries past E are ignored); lane j
+// (j < min(k, 64)) returns the key of pick j.
 template <int S>
-__device__ __forceinline__ unsigned long long topk_rounds(const double (&lv)[S], int E, int k, int32_t* idx) {
+__device__ __forceinline__ unsigned long long topk_rounds(const unsigned long long (&kv)[S], int E, int k,
+                                                          int32_t* idx) {
     const int lane = threadIdx.x & 63;
     constexpr int kNone = 0x7fff;          // slot of an exhausted entry: index past every expert
     // keys and slots (expert = lane + 64 * slot) of this lane's entries; slots past E hold key 0
@@ -226,7 +239,7 @@ __device__ __forceinline__ unsigned long long topk_rounds(const double (&lv)[S],
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const bool ok = lane + 64 * s < E;
-        key[s] = ok ? logit_key(lv[s]) : 0ull;
+        key[s] = ok ? kv[s] : 0ull;
         slot[s] = ok ? s : kNone;
     }
     // rank order within the lane (odd-even transposition sort, S passes)
@@ -283,6 +296,68 @@ __device__ __forceinline__ unsigned long long topk_rounds(const double (&lv)[S],
     return my_key;
 }
 
+// The same top-k (k <= 8) in one pass instead of k dependent rounds.  Lane l holds experts l + 64 s
+// (unsorted).  Every 16-lane row offers its two best entries by upper key half (the lane with the
+// row's best, the lowest such lane, offers its second); t, the least of these eight offers, has at
+// least k distinct entries at or above it, so every pick has upper half >= t.  (When a row offers
+// padding, t is 0 and every expert qualifies.)  The qualifying entries (usually a dozen) are packed
+// into cand (64 entries of LDS owned by this wave), and candidate c's rank is the number of
+// candidates ahead of it under (key descending, index ascending): a total order, so ranks 0..k-1
+// are the picks.  Writes idx[0..k) and returns, in lane j < k, the key of pick j; returns false
+// (writing nothing) when more than 64 entries qualify.  kv: the keys (entries past E are ignored).
+template <int S>
+__device__ __forceinline__ bool topk_pass(const unsigned long long (&kv)[S], int E, int k, int32_t* idx, uint4* cand,
+                                          unsigned long long* rk, unsigned long long& my_key) {
+    const int lane = threadIdx.x & 63;
+    unsigned long long key[S];
+    uint32_t b1 = 0u, b2 = 0u;              // the lane's two largest upper halves
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        key[s] = lane + 64 * s < E ? kv[s] : 0ull;
+        const uint32_t h = (uint32_t)(key[s] >> 32);
+        b2 = max(b2, min(b1, h));
+        b1 = max(b1, h);
+    }
+    const uint32_t m1 = row_max_u32(b1);
+    const uint32_t rowbits = (uint32_t)(__ballot(b1 == m1) >> (lane & 48)) & 0xffffu;
+    const bool first = b1 == m1 && (rowbits & ((1u << (lane & 15)) - 1u)) == 0u;
+    const uint32_t m2 = row_max_u32(first ? b2 : b1);
+    const uint32_t t = min(min((uint32_t)__builtin_amdgcn_readlane((int)m2, 0), (uint32_t)__builtin_amdgcn_readlane((int)m2, 16)),
+                           min((uint32_t)__builtin_amdgcn_readlane((int)m2, 32), (uint32_t)__builtin_amdgcn_readlane((int)m2, 48)));
+    unsigned long long cm[S];
+    int base[S], C = 0;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        cm[s] = __ballot(lane + 64 * s < E && (uint32_t)(key[s] >> 32) >= t);
+        base[s] = C;
+        C += __popcll(cm[s]);
+    }
+    if (C > 64) return false;
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        if ((cm[s] >> lane) & 1ull)
+            cand[base[s] + __popcll(cm[s] & below)] =
+                make_uint4((uint32_t)key[s], (uint32_t)(key[s] >> 32), (uint32_t)(lane + 64 * s), 0u);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // the wave's LDS writes land in order
+    const uint4 me = cand[lane < C ? lane : 0];
+    const unsigned long long mk = ((unsigned long long)me.y << 32) | me.x;
+    int rank = 0;
+#pragma unroll 4
+    for (int j = 0; j < C; ++j) {
+        const uint4 o = cand[j];
+        const unsigned long long ok_ = ((unsigned long long)o.y << 32) | o.x;
+        rank += (ok_ > mk) | ((ok_ == mk) & (o.z < me.z));
+    }
+    if (lane < C && rank < k) {
+        idx[rank] = (int32_t)me.z;
+        rk[rank] = mk;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    my_key = lane < k ? rk[lane] : 0ull;
+    return true;
+}
+
 __device__ __forceinline__ double sigmoid64(double z) { return 1.0 / (1.0 + exp(-z)); }
 
 // The weights of the k picks idx[0..k) (rank order) of one token, by one wave: lane j holds
@@ -304,7 +379,10 @@ __device__ __forceinline__ void topk_weights(unsigned long long my_key, const do
 template <int S>
 __device__ void topk_select(const double (&lv)[S], const double* __restrict__ l, int E, int k, int32_t* idx,
                             float* w) {
-    const unsigned long long my_key = topk_rounds<S>(lv, E, k, idx);
+    unsigned long long kv[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) kv[s] = logit_key(lv[s]);
+    const unsigned long long my_key = topk_rounds<S>(kv, E, k, idx);
     topk_weights(my_key, l, idx, k, w, nullptr);
 }
 
@@ -366,154 +444,121 @@ hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t*
 }
 
 // ---------------------------------------------------------------------------------------------
-// fused router for few tokens (T <= 16), one launch per layer: every workgroup computes the fp64
-// logits of 4 experts (a wave each; rows longer than 4096: 2 experts, two waves each); the last
-// workgroup to finish (device-scope counter) does the top-k, the grouping and the tile records,
-// then resets the counter to zero for the next launch, while the others split x into fp8 terms
-// (when the GEMMs read them).
+// fused router for few tokens (T <= 16), one launch per layer.  Every workgroup but the last
+// computes the fp64 logits of RW experts and then splits its share of x into fp8 terms (when the
+// GEMMs read them); the last workgroup waits for the logits and does the top-k, the grouping and
+// the tile records.
+//
+// Hand-over without a counter: each logit goes to its own 8-byte slot as the complement of its
+// order key (logit_key), written with a device-scope store (through to the coherent level, no
+// fence).  No key is all ones (that would be a NaN's natural key, and NaNs take key 0), so a slot
+// reads zero exactly until its logit is there.  The routing workgroup polls its tokens' slots with
+// device-scope loads until none is zero, and zeroes them again for the next launch.  Workgroups
+// start in index order, so every row workgroup has started before the routing workgroup waits;
+// the wait is bounded all the same.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallT = 16;
+constexpr int kPollLimit = 1 << 20;       // polls of one token group (under a microsecond each)
 
-// RW router rows per workgroup: 4 (a wave per row) or 2 (two waves per row, each with half of
-// it, for long rows).  NC = float4 chunks per lane of a wave's part of a row (d / (4 / RW) <= 256
-// NC, d a multiple of 8).  Every load is issued without a condition (reads past the part re-read
-// its last four elements and are not used), so that no branch separates them and all of a
-// wave's loads are in flight together.
+__device__ __forceinline__ void put_slot(unsigned long long* p, double v) {
+    __hip_atomic_store(p, ~logit_key(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long get_slot(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void clear_slot(unsigned long long* p) {
+    __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// LDS hand-over between the waves of a workgroup: the LDS writes done, then the barrier (no wait
+// for global loads in flight, which __syncthreads would add)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// a stand-in key for expert e (distinct, scattered like real logits), for the warm-up pass
+__device__ __forceinline__ unsigned long long dummy_key(int e) {
+    return ((unsigned long long)(uint32_t)(e + 1) * 0x9e3779b97f4a7c15ull) | 0x8000000000000000ull;
+}
+
+// RW router rows per workgroup, 4 / RW waves per row, each with an equal part of it.  NC = float4
+// chunks per lane of a wave's part (d / (4 / RW) <= 256 NC, d a multiple of 8).  Every load is
+// issued without a condition (reads past the part re-read its last four elements and are not
+// used), so that no branch separates them and all of a wave's loads are in flight together.
 template <typename XT, int NT, int S, int NC, int RW>
 __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     const XT* __restrict__ x = (const XT*)a.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
     const int T = a.T, d = a.d, E = a.E, k = a.k;
-    // 1. issue the loads of this wave's part of its router row.  Lane l reads elements 256 u +
-    // 4 l .. +3 of the part; reads past it are clamped to its last four and not used.
-    constexpr int WPR = 4 / RW;
-    static_assert(RW * WPR == 4, "four waves per workgroup");
-    const int e = blockIdx.x * RW + wave / WPR, part = wave % WPR;
-    const int pl = d / WPR;
-    auto at = [&](int u) { return min(u * 256 + lane * 4, pl - 4); };
-    auto used = [&](int u) { return u * 256 + lane * 4 < pl; };
-    float4 w4[NC];
-    const float* row = a.wr + (size_t)(e < E ? e : 0) * d + (size_t)part * pl;
+    const int Gr = (int)gridDim.x - 1;          // row workgroups; the last workgroup routes
+    if ((int)blockIdx.x < Gr) {
+        // 1. issue the loads of this wave's part of its router row.  Lane l reads elements 256 u +
+        // 4 l .. +3 of the part; reads past it are clamped to its last four and not used.
+        constexpr int WPR = 4 / RW;
+        static_assert(RW * WPR == 4, "four waves per workgroup");
+        const int e = blockIdx.x * RW + wave / WPR, part = wave % WPR;
+        const int pl = d / WPR;
+        auto at = [&](int u) { return min(u * 256 + lane * 4, pl - 4); };
+        auto used = [&](int u) { return u * 256 + lane * 4 < pl; };
+        float4 w4[NC];
+        const float* row = a.wr + (size_t)(e < E ? e : 0) * d + (size_t)part * pl;
 #pragma unroll
-    for (int u = 0; u < NC; ++u) w4[u] = *(const float4*)(row + at(u));
-    // 2. logits, fp64 accumulation of exact products (the parts of a row added in order)
-    __shared__ double s_part[4][kSmallT];
-    if (e < E) {
+        for (int u = 0; u < NC; ++u) w4[u] = *(const float4*)(row + at(u));
+        // 2. logits, fp64 accumulation of exact products (the parts of a row added in order)
+        __shared__ double s_part[4][kSmallT];
+        if (e < E) {
 #pragma unroll 1
-        for (int t = 0; t < T; ++t) {
-            const XT* xt = x + (size_t)t * d + (size_t)part * pl;
-            float4 x4[NC];
+            for (int t = 0; t < T; ++t) {
+                const XT* xt = x + (size_t)t * d + (size_t)part * pl;
+                float4 x4[NC];
 #pragma unroll
-            for (int u = 0; u < NC; ++u) x4[u] = load_act4(xt, at(u));
-            double acc = 0.0;
+                for (int u = 0; u < NC; ++u) x4[u] = load_act4(xt, at(u));
+                double acc = 0.0;
 #pragma unroll
-            for (int u = 0; u < NC; ++u) {
-                double p = fma((double)x4[u].x, (double)w4[u].x, acc);
-                p = fma((double)x4[u].y, (double)w4[u].y, p);
-                p = fma((double)x4[u].z, (double)w4[u].z, p);
-                p = fma((double)x4[u].w, (double)w4[u].w, p);
-                acc = used(u) ? p : acc;
-            }
-            acc = wave_sum_f64(acc);
-            if constexpr (WPR == 1) {
-                if (lane == 0) a.logits[(size_t)t * E + e] = a.bias ? acc + (double)a.bias[e] : acc;
-            } else {
-                if (lane == 0) s_part[wave][t] = acc;
+                for (int u = 0; u < NC; ++u) {
+                    double p = fma((double)x4[u].x, (double)w4[u].x, acc);
+                    p = fma((double)x4[u].y, (double)w4[u].y, p);
+                    p = fma((double)x4[u].z, (double)w4[u].z, p);
+                    p = fma((double)x4[u].w, (double)w4[u].w, p);
+                    acc = used(u) ? p : acc;
+                }
+                acc = wave_sum_f64(acc);
+                if constexpr (WPR == 1) {
+                    if (lane == 0) put_slot(a.slots + (size_t)t * E + e, a.bias ? acc + (double)a.bias[e] : acc);
+                } else {
+                    if (lane == 0) s_part[wave][t] = acc;
+                }
             }
         }
-    }
-    if constexpr (WPR == 2) {
-        __syncthreads();
-        if (tid < RW * T) {
-            const int j = tid % RW, t = tid / RW, ej = blockIdx.x * RW + j;
-            if (ej < E) {
-                const double v = s_part[2 * j][t] + s_part[2 * j + 1][t];
-                a.logits[(size_t)t * E + ej] = a.bias ? v + (double)a.bias[ej] : v;
+        if constexpr (WPR > 1) {
+            __syncthreads();
+            if (tid < RW * T) {
+                const int j = tid % RW, t = tid / RW, ej = blockIdx.x * RW + j;
+                if (ej < E) {
+                    double v = s_part[WPR * j][t];
+#pragma unroll
+                    for (int q = 1; q < WPR; ++q) v += s_part[WPR * j + q][t];
+                    put_slot(a.slots + (size_t)t * E + ej, a.bias ? v + (double)a.bias[ej] : v);
+                }
             }
         }
-    }
-
-    // the last workgroup to arrive finishes the routing.  The barrier orders every wave's logit
-    // stores before thread 0's device-scope release, which writes back the L2 once per workgroup
-    // (a fence in every thread would write it back once per wave, and a few hundred write-backs
-    // per launch cost microseconds); one atomic per workgroup counts arrivals, and only the last
-    // workgroup's thread 0 acquires (one L2 invalidate).  The others, in arrival order, then
-    // split x into fp8 terms for the gate/up GEMM while the last one routes.
-    __shared__ int s_ticket;
-    const int G = (int)gridDim.x;
-    __syncthreads();
-    if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        s_ticket = (int)__hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (s_ticket == G - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    __syncthreads();
-    const int ticket = s_ticket;
-    if (ticket != G - 1) {
-        if (a.split) split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, ticket, G - 1);
+        // 3. this workgroup's share of the split of x into fp8 terms for the gate/up GEMM
+        if (a.split) split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, blockIdx.x, Gr);
         return;
     }
-    if (G == 1 && a.split) split_rows_lanewise<XT, NT>(x, T, d, a.ss1, a.xq, a.xs, 0, 1);
 
+    // the routing workgroup
     __shared__ int32_t s_idx[kMaxFusedPicks];
     __shared__ float s_w[kMaxFusedPicks];
     __shared__ int32_t s_sorted[kMaxFusedPicks];    // sorted position -> pick
     __shared__ uint8_t s_start[kMaxFusedPicks];     // sorted position starts a tile
+    __shared__ uint4 s_cand[4][64];                 // top-k candidates, per wave
+    __shared__ unsigned long long s_rk[4][8];       // keys of the picks in rank order, per wave
     const int P = T * k, tt = a.tt;
-    // the routed tokens' logits (up to four per wave) and, for E <= kTabLds, the whole expert
-    // table are requested in one round, the logits first; the table goes to LDS while the
-    // top-k runs
+    // for E <= kTabLds the whole expert table is kept in LDS
     constexpr int kTabLds = 320, kTabRounds = (kTabLds * 4 + 255) / 256;
     constexpr bool tab_lds = S <= 5;
     __shared__ uint4 s_tab[tab_lds ? kTabLds * 4 : 1];
-    constexpr int J = tab_lds ? kSmallT / 4 : 1;     // tokens whose logits are preloaded per wave
-    double lv[J][S];
-    if (wave < T) {
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int t = wave + 4 * j;
-            topk_load<S>(a.logits + (size_t)(t < T ? t : T - 1) * E, E, lv[j]);
-        }
-    }
-    uint4 tab[tab_lds ? kTabRounds : 1];
-    if constexpr (tab_lds) {
-#pragma unroll
-        for (int r = 0; r < kTabRounds; ++r) {
-            const int g = r * 256 + tid;
-            tab[r] = ((const uint4*)a.table)[g < 4 * E ? g : 4 * E - 1];
-        }
-    }
-    if constexpr (tab_lds) {
-#pragma unroll
-        for (int r = 0; r < kTabRounds; ++r) asm volatile("" ::"v"(tab[r].x), "v"(tab[r].y), "v"(tab[r].z), "v"(tab[r].w));
-#pragma unroll
-        for (int r = 0; r < kTabRounds; ++r) {
-            const int g = r * 256 + tid;
-            if (g < 4 * E) s_tab[g] = tab[r];
-        }
-    }
-    if (T == 1 && tab_lds) {
-        // one token: wave 0 runs the rounds while the other three waves take the sigmoid of every
-        // expert's logit, so that the weights need only the sum and the divisions
-        __shared__ double s_sig[kTabLds];
-        unsigned long long my_key = 0ull;
-        if (wave == 0) {
-            my_key = topk_rounds<S>(lv[0], E, k, s_idx);
-        } else {
-            for (int e = tid - 64; e < E; e += 192) s_sig[e] = sigmoid64(a.logits[e]);
-        }
-        __syncthreads();
-        if (wave == 0) topk_weights(my_key, a.logits, s_idx, k, s_w, s_sig);
-    } else if (wave < T) {
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int t = wave + 4 * j;
-            if (t < T) topk_select<S>(lv[j], a.logits + (size_t)t * E, E, k, s_idx + t * k, s_w + t * k);
-        }
-        for (int t = wave + 4 * J; t < T; t += 4)
-            wave_topk<S>(a.logits + (size_t)t * E, E, k, s_idx + t * k, s_w + t * k);
-    }
-    __syncthreads();
     // the expert-table entry of expert e into a tile record: four 16-byte moves, from the LDS copy
     // of the table when there is one
     auto put_expert = [&](TileDesc* D, int e) {
@@ -524,13 +569,180 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     };
     // an empty record still names a real expert (the first pick's), so that a stray read of its
     // pointers stays inside the weights
-    auto put_empty = [&](int id) {
-        TileDesc* D = a.desc + id;
+    auto put_empty = [&](TileDesc* desc, int id) {
+        TileDesc* D = desc + id;
         put_expert(D, s_idx[0]);
         D->i0 = 0;
         D->ntok = 0;
         D->e = s_idx[0];
     };
+
+    if (T == 1 && tab_lds) {
+        // One token (the decode step).  The expert table is requested first.  While the row
+        // workgroups still stream the router, the whole tail below runs once on stand-in keys with
+        // every output pointed at a.sink, so that the real pass, which starts by polling the
+        // slots, then runs from a warm instruction cache.  Wave 0 polls and picks; waves 1-3 take the
+        // sigmoid of every logit into LDS, zero the slots, and write the offsets and the empty
+        // records.
+        __shared__ unsigned long long s_key[kTabLds];
+        __shared__ double s_sig[kTabLds];
+        // the table in five named pieces (an array held across the pass loop would go to scratch)
+        static_assert(kTabRounds == 5, "five rounds of table loads");
+        const uint4* tsrc = (const uint4*)a.table;
+        auto tload = [&](int r) { const int g = r * 256 + tid; return tsrc[g < 4 * E ? g : 4 * E - 1]; };
+        auto tstore = [&](int r, const uint4& v) { const int g = r * 256 + tid; if (g < 4 * E) s_tab[g] = v; };
+        const uint4 tab0 = tload(0), tab1 = tload(1), tab2 = tload(2), tab3 = tload(3), tab4 = tload(4);
+#pragma unroll 1
+        for (int pass = 0; pass < 2; ++pass) {
+            int live = pass;
+            asm volatile("" : "+s"(live));      // opaque: one copy of the code serves both passes
+            TileDesc* const desc = live ? a.desc : (TileDesc*)a.sink;
+            int32_t* const tiles = live ? a.tiles : (int32_t*)a.sink;
+            int32_t* const idx = live ? a.idx : (int32_t*)a.sink;
+            float* const wout = live ? a.w : (float*)a.sink;
+            int32_t* const pick_pos = live ? a.pick_pos : (int32_t*)a.sink;
+            int32_t* const sorted_pick = live ? a.sorted_pick : (int32_t*)a.sink;
+            int32_t* const offsets = live ? a.offsets : (int32_t*)a.sink;
+            int32_t* const ntiles = live ? a.ntiles : (int32_t*)a.sink;
+            unsigned long long* const slots = live ? a.slots : (unsigned long long*)a.sink;
+            unsigned long long kv[S];
+            if (live) {
+                tstore(0, tab0);
+                tstore(1, tab1);
+                tstore(2, tab2);
+                tstore(3, tab3);
+                tstore(4, tab4);
+            }
+            if (wave == 0) {
+                if (live) {
+                    // poll the slots (lane l: experts l + 64 s) until none is zero
+                    for (int it = 0; it < kPollLimit; ++it) {
+                        bool miss = false;
+#pragma unroll
+                        for (int s = 0; s < S; ++s) {
+                            const unsigned long long v = get_slot(a.slots + min(lane + 64 * s, E - 1));
+                            kv[s] = ~v;
+                            miss |= (lane + 64 * s < E) & (v == 0ull);
+                        }
+                        if (__ballot(miss) == 0ull) break;
+                    }
+                } else {
+                    // a branch of its own (the asm keeps it one), so that the warm-up pass does
+                    // not wait for the poll in flight
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int s = 0; s < S; ++s) kv[s] = dummy_key(lane + 64 * s);
+                }
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                    if (lane + 64 * s < E) s_key[lane + 64 * s] = kv[s];
+            }
+            lds_barrier();
+            if (wave == 0) {
+                unsigned long long my_key = 0ull;
+                if (k > 8 || !topk_pass<S>(kv, E, k, s_idx, s_cand[0], s_rk[0], my_key))
+                    my_key = topk_rounds<S>(kv, E, k, s_idx);
+            } else {
+                for (int e = tid - 64; e < E; e += 192) {
+                    s_sig[e] = sigmoid64(key_logit(s_key[e]));
+                    clear_slot(slots + e);
+                }
+            }
+            lds_barrier();
+            if (wave == 0) {
+                // the weights (sum in rank order) and the records: the token's k experts are
+                // distinct, so pick p is a tile of its own at sorted position = the number of
+                // picks of lower experts (what the grouping below gives in this case)
+                const int p = lane;
+                const int e = p < k ? s_idx[p] : 0;
+                const double sg = p < k ? s_sig[e] : 0.0;
+                double ssum = 0.0;
+                for (int j = 0; j < k; ++j) ssum += readlane_f64(sg, j);
+                int pos = 0;
+                for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(e, q) < e;
+                if (p < k) {
+                    TileDesc* D = desc + pos;
+                    put_expert(D, e);
+                    D->i0 = pos;
+                    D->ntok = 1;
+                    D->e = e;
+                    D->pad0 = 0;
+#pragma unroll
+                    for (int c = 0; c < kDescTokens; ++c) D->tok[c] = 0;
+                    tiles[2 * pos] = e;
+                    tiles[2 * pos + 1] = pos;
+                    idx[p] = e;
+                    wout[p] = (float)(sg / ssum);
+                    pick_pos[p] = pos;
+                    sorted_pick[pos] = p;
+                }
+            } else {
+                // the expert offsets (picks of lower experts), the empty records, the tile count
+                for (int e = tid - 64; e <= E; e += 192) {
+                    int lower = 0;
+#pragma unroll 8
+                    for (int q = 0; q < k; ++q) lower += s_idx[q] < e;
+                    offsets[e] = lower;
+                }
+                for (int id = k + tid - 64; id < a.max_tiles; id += 192) put_empty(desc, id);
+                if (tid == 64) *ntiles = k;
+            }
+            lds_barrier();      // the real pass rewrites what this one read from LDS
+        }
+        return;
+    }
+
+    if constexpr (tab_lds) {
+        uint4 tab[kTabRounds];
+#pragma unroll
+        for (int r = 0; r < kTabRounds; ++r) {
+            const int g = r * 256 + tid;
+            tab[r] = ((const uint4*)a.table)[g < 4 * E ? g : 4 * E - 1];
+        }
+#pragma unroll
+        for (int r = 0; r < kTabRounds; ++r) {
+            const int g = r * 256 + tid;
+            if (g < 4 * E) s_tab[g] = tab[r];
+        }
+    }
+    // wave w routes tokens w, w + 4, ...; J of them per round of polls (lane l: experts l + 64 s).
+    // Every poll load is issued without a condition (indices past T or E re-read the last slot
+    // and are not used), so that all of them are in flight together.
+    constexpr int J = tab_lds ? kSmallT / 4 : 1;
+    for (int t0 = wave; t0 < T; t0 += 4 * J) {
+        unsigned long long kv[J][S];
+        for (int it = 0; it < kPollLimit; ++it) {
+            bool miss = false;
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const int t = t0 + 4 * j, e = lane + 64 * s;
+                    const unsigned long long v = get_slot(a.slots + (size_t)min(t, T - 1) * E + min(e, E - 1));
+                    kv[j][s] = ~v;
+                    miss |= (t < T) & (e < E) & (v == 0ull);
+                }
+            if (__ballot(miss) == 0ull) break;
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int t = t0 + 4 * j, e = lane + 64 * s;
+                if (t < T && e < E) clear_slot(a.slots + (size_t)t * E + e);
+            }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int t = t0 + 4 * j;
+            if (t < T) {
+                unsigned long long my_key = 0ull;
+                if (k > 8 || !topk_pass<S>(kv[j], E, k, s_idx + t * k, s_cand[wave], s_rk[wave], my_key))
+                    my_key = topk_rounds<S>(kv[j], E, k, s_idx + t * k);
+                topk_weights(my_key, nullptr, s_idx + t * k, k, s_w + t * k, nullptr);
+            }
+        }
+    }
+    __syncthreads();
     // the expert offsets: the number of picks of lower experts
     auto put_offsets = [&]() {
         for (int e = tid; e <= E; e += 256) {
@@ -541,9 +753,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         }
     };
     if (T == 1) {
-        // one token: its k experts are distinct, so each pick is a tile of its own, and its
-        // sorted position is the number of picks of lower experts (what the grouping below
-        // gives in this case, without its scans)
+        // one token (more than kTabLds experts): each pick is a tile of its own, as above
         for (int p = tid; p < k; p += 256) {
             const int e = s_idx[p];
             int pos = 0;
@@ -565,11 +775,8 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             a.sorted_pick[pos] = p;
         }
         put_offsets();
-        for (int id = k + tid; id < a.max_tiles; id += 256) put_empty(id);
-        if (tid == 0) {
-            *a.ntiles = k;
-            *a.counter = 0u;
-        }
+        for (int id = k + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id);
+        if (tid == 0) *a.ntiles = k;
         return;
     }
     // Grouping without atomics or scans (P <= 512, two picks per thread): a pick's sorted
@@ -626,32 +833,30 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     int nt = 0;
 #pragma unroll 8
     for (int q = 0; q < P; ++q) nt += s_start[q];
-    for (int id = nt + tid; id < a.max_tiles; id += 256) put_empty(id);
-    if (tid == 0) {
-        *a.ntiles = nt;
-        *a.counter = 0u;
-    }
+    for (int id = nt + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id);
+    if (tid == 0) *a.ntiles = nt;
 }
 
 hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipStream_t st) {
     trace("route_small", 0, st);
-    // rows up to 4096: a wave per row; longer (up to 8192): two waves per row
-    const int RW = s->d_model <= 4096 ? 4 : 2;
-    dim3 grid((s->n_experts + RW - 1) / RW);
+    // one router row per workgroup, a quarter per wave (about 4 KB per wave at d = 4096), so the
+    // rows spread over the whole chip; the routing workgroup last
+    dim3 grid(s->n_experts + 1);
     const bool bf = s->act_dtype == MOE_DT_BF16;
-#define MOE_RS(XT, N, R)                                                                                \
-    do {                                                                                                \
-        if (s->n_experts <= 320) MOE_LAUNCH((k_route_small<XT, N, 5, 16, R>), grid, dim3(256), 0, st, a); \
-        else MOE_LAUNCH((k_route_small<XT, N, 16, 16, R>), grid, dim3(256), 0, st, a);              \
+    const bool lng = s->d_model > 4096;
+#define MOE_RS(XT, N)                                                                                    \
+    do {                                                                                                 \
+        if (s->n_experts <= 320) {                                                                       \
+            if (lng) MOE_LAUNCH((k_route_small<XT, N, 5, 8, 1>), grid, dim3(256), 0, st, a);            \
+            else MOE_LAUNCH((k_route_small<XT, N, 5, 4, 1>), grid, dim3(256), 0, st, a);                \
+        } else {                                                                                         \
+            if (lng) MOE_LAUNCH((k_route_small<XT, N, 16, 8, 1>), grid, dim3(256), 0, st, a);           \
+            else MOE_LAUNCH((k_route_small<XT, N, 16, 4, 1>), grid, dim3(256), 0, st, a);               \
+        }                                                                                                \
     } while (0)
     // activation terms: 2 for bf16 activations, 4 for fp32 (act_terms)
-    if (bf) {
-        if (RW == 4) MOE_RS(uint16_t, 2, 4);
-        else MOE_RS(uint16_t, 2, 2);
-    } else {
-        if (RW == 4) MOE_RS(float, 4, 4);
-        else MOE_RS(float, 4, 2);
-    }
+    if (bf) MOE_RS(uint16_t, 2);
+    else MOE_RS(float, 4);
 #undef MOE_RS
     trace("route_small", 1, st);
     return hipGetLastError();

@@ -120,6 +120,9 @@ SMALL_CASES = [
     # few tokens, router rows not a whole number of 256-element chunks per half (fused router)
     ("tiny", dict(d_model=384, d_ff=256, n_experts=16, top_k=2, act_dtype=synth.BF16), 4),
     ("tiny", dict(d_model=640, d_ff=256, n_experts=9, top_k=3), 2),
+    # fused router: k > 8 takes the k-round top-k; E > 320 holds 16 logits per lane
+    ("tiny", dict(n_experts=64, top_k=12), 3),
+    ("tiny", dict(n_experts=400, top_k=8, act_dtype=synth.BF16), 5),
 ]
 
 
@@ -135,6 +138,47 @@ def test_layer_small(name, kw, T):
     err = rel_l2(y.float().cpu().numpy(), oy)
     print(f"  rel-L2 {err:.3e} (tol {tol(wl):.0e})")
     assert err <= tol(wl)
+
+
+@pytest.mark.parametrize("T", [1, 3, 16])
+def test_fused_route_ties_nan_and_zero_token(T):
+    """The few-token router of moe_layer: experts 2, 9 and 13 tie exactly on every token, experts
+    3 and 7 have NaN logits (after every number), and token 0 is all zeros (every finite logit 0,
+    so the lowest indices win with equal weights)."""
+    wl = small("tiny", top_k=4)
+    print(f"fused route ties/NaN T={T}", flush=True)
+    dl = DeviceLayer(m, wl)
+    dl.router[9] = dl.router[2]
+    dl.router[13] = dl.router[2]
+    dl.router[3] = float("nan")
+    dl.router[7] = float("nan")
+    x = _x(wl, T)
+    x[0] = 0.0
+    y, idx, w = run_layer(m, dl, x)
+    oy, oidx, ow, _ = oracle_layer(dl, x)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oidx)
+    np.testing.assert_array_equal(oidx[0], [0, 1, 2, 4])
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=2e-7, atol=1e-8)
+    assert rel_l2(y.float().cpu().numpy(), oy) <= tol(wl)
+
+
+def test_fused_route_workspace_shared_across_T():
+    """One workspace, sized for 64 tokens, used by the general path (T=64) and then by the
+    few-token path (T=1, 16, 1): each result equals the one from a fresh workspace."""
+    wl = small("tiny", d_model=512, d_ff=256, n_experts=32, top_k=4, act_dtype=synth.BF16)
+    dl = DeviceLayer(m, wl)
+    ws = m.workspace(dl.shape, 64)
+    for T in (64, 1, 16, 1):
+        print(f"shared workspace T={T}", flush=True)
+        x = _x(wl, T, tag=f"ws{T}")
+        y = torch.empty_like(x)
+        idx = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, wl.top_k, dtype=torch.float32, device="cuda")
+        m.moe_layer(dl.shape, x, T, dl.router, dl.bias, dl.table, None, None, y, idx, w, ws)
+        torch.cuda.synchronize()
+        y0, i0, w0 = run_layer(m, dl, x)
+        assert torch.equal(idx, i0) and torch.equal(w, w0)
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
 
 
 def test_layer_residual_and_scaling():
@@ -241,6 +285,22 @@ def test_glm_decode_layer(glm_layer, T):
     err = rel_l2(y.float().cpu().numpy(), oy)
     print(f"  rel-L2 {err:.3e}")
     assert err <= tol(wl)
+
+
+def test_glm_decode_zero_token(glm_layer):
+    """A zero token at full width: all 288 logits are 0, more candidates than the one-pass top-k
+    takes, so the k-round top-k picks experts 0..7 with weights 1/8; token 1 is ordinary."""
+    dl = glm_layer
+    wl = dl.wl
+    print("glm layer zero token", flush=True)
+    x = _x(wl, 2, tag="zero")
+    x[0] = 0.0
+    y, idx, w = run_layer(m, dl, x)
+    oy, oidx, ow, _ = oracle_layer(dl, x, idx_hint=idx.cpu().numpy())
+    np.testing.assert_array_equal(idx.cpu().numpy(), oidx)
+    np.testing.assert_array_equal(oidx[0], np.arange(8))
+    np.testing.assert_allclose(w[0].cpu().numpy(), 0.125, rtol=0, atol=0)
+    assert rel_l2(y.float().cpu().numpy(), oy) <= tol(wl)
 
 
 def test_glm_prefill_chunk_sampled(glm_layer):
