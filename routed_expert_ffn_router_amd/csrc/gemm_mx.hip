@@ -372,7 +372,10 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
     int off0;
     const int c0 = chunk_col(g0, off0);
     const int tok0 = chunk_tok(c0);
-    // 2. this wave's weights: all loads at once (super-steps past nss re-read the last one)
+    const uint4 xv0 = gload16(chunk_src(g0, tok0, c0, off0));
+    __builtin_amdgcn_sched_barrier(0);       // keep it ahead of the weight loads
+    // 2. this wave's weights: all loads at once (super-steps past nss re-read the last one), after
+    // the x-term chunk, so that storing that chunk waits only for it
     const uint8_t* mq = (f >= 2) ? uq : gq;
     const uint8_t* ms = (f >= 2) ? us : gs;
     const uint8_t* aq = (mq + (size_t)row * (K / 2) + lg * 16 * SS + (size_t)kss0 * 64 * SS);
@@ -386,11 +389,8 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
         for (int h = 0; h < SS; ++h) A[q][h] = gload16(aq + (size_t)qq * 64 * SS + 16 * h);
         sa[q] = gload4(as + (size_t)qq * 4 * SS);
     }
-    // 3. the x-term chunks (their data arrives with the weights; stored to LDS after)
-    {
-        const uint4 v = gload16(chunk_src(g0, tok0, c0, off0));
-        if (tid < ntotal) *chunk_dst(g0, c0, off0) = v;
-    }
+    // 3. the x-term chunks to LDS
+    if (tid < ntotal) *chunk_dst(g0, c0, off0) = xv0;
     for (int g = tid + 512; g < ntotal; g += 512) {      // more than 512 chunks: tiles of many picks
         int off;
         const int c = chunk_col(g, off);
@@ -398,9 +398,10 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
         const uint4 v = gload16(chunk_src(g, tok, c, off));
         *chunk_dst(g, c, off) = v;
     }
-    __syncthreads();
+    lds_barrier();
     // 4. MFMAs, FP8 operand from LDS, one super-step's operands read before its MFMAs (columns
-    // past the tile read its last column; their results are not used)
+    // past the tile read its last column; their results are not used).  The barrier above does
+    // not wait for the weights: each super-step's MFMAs start when its own weights are in.
     const int col = li < ncol ? li : ncol - 1;
     const uint8_t* bl = &b_lds[col][(size_t)kss0 * 128 * SS + lg * 32 * SS];
     const uint8_t* bsl = &bs_lds[col][kss0 * 4 * SS + lg * SS];
@@ -582,15 +583,15 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
     const int units = a.max_tiles * nsl;
     const int tc = li / NT, t = li % NT;
     auto unit_ok = [&](int u) { return u < units && d_lds[u / nsl].ntok > 0; };
-    // loads of units u0 and u0 + 8; a unit without a tile re-reads the other one's weights, and
-    // nothing is read when neither has a tile (records of absent tiles are never dereferenced)
+    // loads of units u0 and u0 + 8, issued without a condition (so that the h terms above can be
+    // waited for alone): a unit without a tile re-reads the other one's weights, or unit 0's when
+    // neither has one (every record, an empty one too, names a real expert)
     auto load_units = [&](int u0, uint4 (&A)[2][NSS][SS], uint32_t (&sa)[2][NSS], bool& ok0, bool& ok1,
                           int (&us)[2]) {
         const int u1 = u0 + 8;
         ok0 = unit_ok(u0);
         ok1 = unit_ok(u1);
-        if (!ok0 && !ok1) return;
-        us[1] = ok1 ? u1 : u0;
+        us[1] = ok1 ? u1 : (ok0 ? u0 : 0);
         us[0] = ok0 ? u0 : us[1];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -663,7 +664,7 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
             *(uint4*)&bs_lds[col][(gg % (K / 512)) * 16] = v[r];
         }
     }
-    __syncthreads();
+    lds_barrier();          // not waiting for the weights: each unit's MFMAs start when its own are in
     run_units(A, sa, ok0, ok1, us);
     for (int u0 = wave + 16; u0 < units; u0 += 16) {      // more than sixteen units: further pairs
         load_units(u0, A, sa, ok0, ok1, us);
@@ -671,17 +672,28 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
     }
     __syncthreads();
     // 5. y[t][r] = scaling * sum_j w[t,j] * (sum over K slices of o) (+ residual), rank order j
+    // (every pick's position and weight read first, then every partial, then the sums: two LDS
+    // round trips instead of two per pick)
     const int k = a.k;
     if (tid < c.T * 16) {
         const int tok = tid >> 4, r = tid & 15;
-        float accv = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const int p = tok * k + j;
-            const int pos = s_posq[p];
-            float o = 0.f;
-            for (int sl = 0; sl < nsl; ++sl) o += o_part[sl][pos][r];
-            accv = fmaf(s_wq[p], o, accv);
+        int pos[MAXP];
+        float wgt[MAXP], o[MAXP];
+#pragma unroll
+        for (int j = 0; j < MAXP; ++j) {
+            const int p = tok * k + (j < k ? j : 0);
+            pos[j] = s_posq[p];
+            wgt[j] = s_wq[p];
         }
+#pragma unroll
+        for (int j = 0; j < MAXP; ++j) {
+            o[j] = o_part[0][pos[j]][r];
+            for (int sl = 1; sl < nsl; ++sl) o[j] += o_part[sl][pos[j]][r];
+        }
+        float accv = 0.f;
+#pragma unroll
+        for (int j = 0; j < MAXP; ++j)
+            if (j < k) accv = fmaf(wgt[j], o[j], accv);
         float val = accv * c.scaling;
         if (c.residual) val += resq;
         store_act((XT*)c.y, yoff, val);
@@ -822,12 +834,7 @@ __device__ __forceinline__ void wait_vm() {
 // moves no memory access across it.  Unlike __syncthreads it does not wait for this wave's
 // direct loads still in flight (they target other stages; each is waited for with wait_vm
 // before the barrier that publishes its stage).
-__device__ __forceinline__ void ring_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0), vmcnt and expcnt unchanged
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
+__device__ __forceinline__ void ring_barrier() { lds_barrier(); }
 
 struct PfFrags {
     uint4 a[8];

@@ -98,6 +98,15 @@ __device__ __forceinline__ T sload(const T* p) {
     return *(const __attribute__((address_space(4))) T*)p;
 }
 
+// Workgroup barrier for LDS hand-over: this wave's LDS operations done, then s_barrier.  Unlike
+// __syncthreads it does not wait for global loads in flight (the workgroup-scope fence would).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0), vmcnt and expcnt unchanged
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------------------------
 // element formats (device side)
 // ---------------------------------------------------------------------------------------------

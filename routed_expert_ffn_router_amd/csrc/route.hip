@@ -300,11 +300,14 @@ __device__ __forceinline__ unsigned long long topk_rounds(const unsigned long lo
 // (unsorted).  Every 16-lane row offers its two best entries by upper key half (the lane with the
 // row's best, the lowest such lane, offers its second); t, the least of these eight offers, has at
 // least k distinct entries at or above it, so every pick has upper half >= t.  (When a row offers
-// padding, t is 0 and every expert qualifies.)  The qualifying entries (usually a dozen) are packed
-// into cand (64 entries of LDS owned by this wave), and candidate c's rank is the number of
-// candidates ahead of it under (key descending, index ascending): a total order, so ranks 0..k-1
-// are the picks.  Writes idx[0..k) and returns, in lane j < k, the key of pick j; returns false
-// (writing nothing) when more than 64 entries qualify.  kv: the keys (entries past E are ignored).
+// padding, t is 0 and every expert qualifies.)  The qualifying entries (usually a dozen or two)
+// are packed into cand (128 entries of LDS owned by this wave: 64 candidates, then a discard area
+// that the other lanes write to, so that the writes need no branch), and candidate c's rank is the
+// number of candidates ahead of it under (key descending, index ascending): a total order, so
+// ranks 0..k-1 are the picks.  Sixteen candidates are ranked at a time: lane l takes candidate
+// 16 b + l % 16 and counts a quarter of the others, and the four lanes l ^ 16 s add their counts.
+// Writes idx[0..k) and returns, in lane j < k, the key of pick j; returns false (writing nothing)
+// when more than 64 entries qualify.  kv: the keys (entries past E are ignored).
 template <int S>
 __device__ __forceinline__ bool topk_pass(const unsigned long long (&kv)[S], int E, int k, int32_t* idx, uint4* cand,
                                           unsigned long long* rk, unsigned long long& my_key) {
@@ -335,23 +338,33 @@ __device__ __forceinline__ bool topk_pass(const unsigned long long (&kv)[S], int
     if (C > 64) return false;
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int s = 0; s < S; ++s)
-        if ((cm[s] >> lane) & 1ull)
-            cand[base[s] + __popcll(cm[s] & below)] =
-                make_uint4((uint32_t)key[s], (uint32_t)(key[s] >> 32), (uint32_t)(lane + 64 * s), 0u);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // the wave's LDS writes land in order
-    const uint4 me = cand[lane < C ? lane : 0];
-    const unsigned long long mk = ((unsigned long long)me.y << 32) | me.x;
-    int rank = 0;
-#pragma unroll 4
-    for (int j = 0; j < C; ++j) {
-        const uint4 o = cand[j];
-        const unsigned long long ok_ = ((unsigned long long)o.y << 32) | o.x;
-        rank += (ok_ > mk) | ((ok_ == mk) & (o.z < me.z));
+    for (int s = 0; s < S; ++s) {
+        const bool in = (cm[s] >> lane) & 1ull;
+        cand[in ? base[s] + __popcll(cm[s] & below) : 64 + lane] =
+            make_uint4((uint32_t)key[s], (uint32_t)(key[s] >> 32), (uint32_t)(lane + 64 * s), 0u);
     }
-    if (lane < C && rank < k) {
-        idx[rank] = (int32_t)me.z;
-        rk[rank] = mk;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // the wave's LDS writes land in order
+    for (int b = 0; 16 * b < C; ++b) {
+        const int c = 16 * b + (lane & 15);
+        const int cc = c < C ? c : 0;
+        const uint4 me = cand[cc];
+        const unsigned long long mk = ((unsigned long long)me.y << 32) | me.x;
+        int part = 0;
+#pragma unroll 4
+        for (int j0 = 0; j0 < C; j0 += 4) {
+            const int j = j0 + (lane >> 4);
+            const uint4 o = cand[j < C ? j : cc];           // past C: itself, which never counts
+            const unsigned long long ok_ = ((unsigned long long)o.y << 32) | o.x;
+            part += (ok_ > mk) | ((ok_ == mk) & (o.z < me.z));
+        }
+        const auto r16 = __builtin_amdgcn_permlane16_swap((uint32_t)part, (uint32_t)part, false, false);
+        const uint32_t p2 = r16[0] + r16[1];
+        const auto r32 = __builtin_amdgcn_permlane32_swap(p2, p2, false, false);
+        const int rank = (int)(r32[0] + r32[1]);
+        if (lane < 16 && c < C && rank < k) {
+            idx[rank] = (int32_t)me.z;
+            rk[rank] = mk;
+        }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     my_key = lane < k ? rk[lane] : 0ull;
@@ -469,13 +482,6 @@ __device__ __forceinline__ unsigned long long get_slot(const unsigned long long*
 __device__ __forceinline__ void clear_slot(unsigned long long* p) {
     __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// LDS hand-over between the waves of a workgroup: the LDS writes done, then the barrier (no wait
-// for global loads in flight, which __syncthreads would add)
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 // a stand-in key for expert e (distinct, scattered like real logits), for the warm-up pass
 __device__ __forceinline__ unsigned long long dummy_key(int e) {
     return ((unsigned long long)(uint32_t)(e + 1) * 0x9e3779b97f4a7c15ull) | 0x8000000000000000ull;
@@ -552,7 +558,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     __shared__ float s_w[kMaxFusedPicks];
     __shared__ int32_t s_sorted[kMaxFusedPicks];    // sorted position -> pick
     __shared__ uint8_t s_start[kMaxFusedPicks];     // sorted position starts a tile
-    __shared__ uint4 s_cand[4][64];                 // top-k candidates, per wave
+    __shared__ uint4 s_cand[4][128];                // top-k candidates, per wave
     __shared__ unsigned long long s_rk[4][8];       // keys of the picks in rank order, per wave
     const int P = T * k, tt = a.tt;
     // for E <= kTabLds the whole expert table is kept in LDS
@@ -581,9 +587,9 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         // One token (the decode step).  The expert table is requested first.  While the row
         // workgroups still stream the router, the whole tail below runs once on stand-in keys with
         // every output pointed at a.sink, so that the real pass, which starts by polling the
-        // slots, then runs from a warm instruction cache.  Wave 0 polls and picks; waves 1-3 take the
-        // sigmoid of every logit into LDS, zero the slots, and write the offsets and the empty
-        // records.
+        // slots, then runs from a warm instruction cache.  Wave 0 polls, picks and writes the
+        // records; waves 1-3 meanwhile take the sigmoid of every logit into LDS and zero the slots;
+        // then wave 1 writes the weights and waves 2-3 the offsets and the empty records.
         __shared__ unsigned long long s_key[kTabLds];
         __shared__ double s_sig[kTabLds];
         // the table in five named pieces (an array held across the pass loop would go to scratch)
@@ -650,14 +656,11 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             }
             lds_barrier();
             if (wave == 0) {
-                // the weights (sum in rank order) and the records: the token's k experts are
-                // distinct, so pick p is a tile of its own at sorted position = the number of
-                // picks of lower experts (what the grouping below gives in this case)
+                // the records: the token's k experts are distinct, so pick p is a tile of its own
+                // at sorted position = the number of picks of lower experts (what the grouping
+                // below gives in this case)
                 const int p = lane;
                 const int e = p < k ? s_idx[p] : 0;
-                const double sg = p < k ? s_sig[e] : 0.0;
-                double ssum = 0.0;
-                for (int j = 0; j < k; ++j) ssum += readlane_f64(sg, j);
                 int pos = 0;
                 for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(e, q) < e;
                 if (p < k) {
@@ -672,20 +675,26 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                     tiles[2 * pos] = e;
                     tiles[2 * pos + 1] = pos;
                     idx[p] = e;
-                    wout[p] = (float)(sg / ssum);
                     pick_pos[p] = pos;
                     sorted_pick[pos] = p;
                 }
+            } else if (wave == 1) {
+                // the weights, the sum in rank order
+                const int p = lane;
+                const double sg = p < k ? s_sig[s_idx[p]] : 0.0;
+                double ssum = 0.0;
+                for (int j = 0; j < k; ++j) ssum += readlane_f64(sg, j);
+                if (p < k) wout[p] = (float)(sg / ssum);
             } else {
                 // the expert offsets (picks of lower experts), the empty records, the tile count
-                for (int e = tid - 64; e <= E; e += 192) {
+                for (int e = tid - 128; e <= E; e += 128) {
                     int lower = 0;
 #pragma unroll 8
                     for (int q = 0; q < k; ++q) lower += s_idx[q] < e;
                     offsets[e] = lower;
                 }
-                for (int id = k + tid - 64; id < a.max_tiles; id += 192) put_empty(desc, id);
-                if (tid == 64) *ntiles = k;
+                for (int id = k + tid - 128; id < a.max_tiles; id += 128) put_empty(desc, id);
+                if (tid == 128) *ntiles = k;
             }
             lds_barrier();      // the real pass rewrites what this one read from LDS
         }
