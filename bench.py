@@ -254,6 +254,9 @@ def main():
             ws = m.workspace(stack.shape, T)
             idx_keep = torch.empty(nl, T, wl.top_k, dtype=torch.int32, device="cuda")
             w_keep = torch.empty(nl, T, wl.top_k, dtype=torch.float32, device="cuda")
+            # the inputs and the zero-filled workspace come from torch's stream; S (a non-blocking
+            # stream) does not wait for it by itself
+            torch.cuda.synchronize()
             # eager reference step (keeps every layer's routing), then the graph
             with torch.cuda.stream(stream):
                 run_stack(T, biases, x0, bufs, ws, keep=(idx_keep, w_keep))()
@@ -309,6 +312,7 @@ def main():
         idx = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
         wts = torch.empty(T, wl.top_k, dtype=torch.float32, device="cuda")
         ws = m.workspace(stack.shape, T)
+        torch.cuda.synchronize()        # inputs and workspace ready before S uses them
         call = lambda: m.moe_layer(stack.shape, x, T, stack.router[0], None, stack.table[0], None, None, y, idx,
                                    wts, ws, stream=S)
         for _ in range(max(2, args.warmup)):
@@ -352,6 +356,7 @@ def main():
             bufs = [torch.empty_like(x0), torch.empty_like(x0)]
             ws = m.workspace(nst.shape, T)
             idx = torch.empty(nvl, T, wl.top_k, dtype=torch.int32, device="cuda")
+            torch.cuda.synchronize()    # inputs and workspace ready before S uses them
             for staged in (False, True):
                 def step(staged=staged):
                     cur = x0

@@ -177,7 +177,11 @@ def moe_workspace_bytes(shape: moe_shape, T: int) -> int:
 
 
 def workspace(shape: moe_shape, T: int, device="cuda"):
-    """A zero-filled uint8 device tensor of moe_workspace_bytes(shape, T) bytes (at least 256)."""
+    """A zero-filled uint8 device tensor of moe_workspace_bytes(shape, T) bytes (at least 256).
+
+    The zero fill runs on torch's current stream: a caller that launches on another stream makes
+    that stream wait for it first (torch.cuda.synchronize() or Stream.wait_stream), as for any input.
+    """
     import torch
     n = max(moe_workspace_bytes(shape, T), 256)
     return torch.zeros(n, dtype=torch.uint8, device=device)
