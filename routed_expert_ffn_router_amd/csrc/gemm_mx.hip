@@ -667,6 +667,7 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
     lds_barrier();          // not waiting for the weights: each unit's MFMAs start when its own are in
     run_units(A, sa, ok0, ok1, us);
     for (int u0 = wave + 16; u0 < units; u0 += 16) {      // more than sixteen units: further pairs
+        if (!unit_ok(u0) && !unit_ok(u0 + 8)) continue;       // (none of them holds a tile)
         load_units(u0, A, sa, ok0, ok1, us);
         run_units(A, sa, ok0, ok1, us);
     }
@@ -685,10 +686,11 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
             pos[j] = s_posq[p];
             wgt[j] = s_wq[p];
         }
+        static_assert(kMaxDecSlices == 2, "the K slices of a down unit are added below");
 #pragma unroll
         for (int j = 0; j < MAXP; ++j) {
-            o[j] = o_part[0][pos[j]][r];
-            for (int sl = 1; sl < nsl; ++sl) o[j] += o_part[sl][pos[j]][r];
+            const float p0 = o_part[0][pos[j]][r], p1 = o_part[1][pos[j]][r];   // slice 1 read even
+            o[j] = nsl > 1 ? p0 + p1 : p0;                                     // when unused
         }
         float accv = 0.f;
 #pragma unroll
