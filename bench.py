@@ -230,16 +230,16 @@ def main():
         log(f"# building the {nl}-layer decode stack in HBM")
         stack = Stack(m, synth, torch, wl_dec, nl, args.seed, log)
 
-    def run_stack(T, biases, x0, bufs, ws, keep=None):
-        """One step: T tokens through every layer, x_{l+1} = x_l + y_l (residual fused)."""
+    def run_stack(T, biases, xs, bufs, ws, keep=None):
+        """One step: every layer l reads its own input xs[l] and writes y_l = xs[l] + MoE_l(xs[l])
+        (residual fused).  Each input stands in for the normalised hidden state a transformer block
+        hands its MoE layer; feeding one layer's output straight into the next, with no norm
+        between them, grows the activations without bound (past bf16's range by layer 19)."""
         def fn():
-            cur = x0
             for l in range(nl):
-                nxt = bufs[l % 2]
-                m.moe_layer(stack.shape, cur, T, stack.router[l], biases[l], stack.table[l], None, cur, nxt,
-                            None if keep is None else keep[0][l], None if keep is None else keep[1][l],
-                            ws, stream=S)
-                cur = nxt
+                m.moe_layer(stack.shape, xs[l], T, stack.router[l], biases[l], stack.table[l], None, xs[l],
+                            bufs[l % 2], None if keep is None else keep[0][l],
+                            None if keep is None else keep[1][l], ws, stream=S)
         return fn
 
     result_kernels = {}
@@ -249,8 +249,8 @@ def main():
                 continue
             wl = synth.WORKLOADS[name]
             biases = [synth.make_bias(wl, l, args.seed, "cuda") for l in range(nl)]
-            x0 = synth.make_x(wl, args.seed, "cuda", tokens=T, tag=f"x_{name}")
-            bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+            xs = [synth.make_x(wl, args.seed, "cuda", tokens=T, tag=f"x_{name}_{l}") for l in range(nl)]
+            bufs = [torch.empty_like(xs[0]), torch.empty_like(xs[0])]
             ws = m.workspace(stack.shape, T)
             idx_keep = torch.empty(nl, T, wl.top_k, dtype=torch.int32, device="cuda")
             w_keep = torch.empty(nl, T, wl.top_k, dtype=torch.float32, device="cuda")
@@ -259,10 +259,10 @@ def main():
             torch.cuda.synchronize()
             # eager reference step (keeps every layer's routing), then the graph
             with torch.cuda.stream(stream):
-                run_stack(T, biases, x0, bufs, ws, keep=(idx_keep, w_keep))()
+                run_stack(T, biases, xs, bufs, ws, keep=(idx_keep, w_keep))()
             hip.sync(S)
             y_eager = bufs[(nl - 1) % 2].clone()
-            gexec, _ = hip.capture(S, run_stack(T, biases, x0, bufs, ws, keep=(idx_keep, w_keep)))
+            gexec, _ = hip.capture(S, run_stack(T, biases, xs, bufs, ws, keep=(idx_keep, w_keep)))
             for _ in range(3):      # replays reproduce the eager step bit for bit
                 hip.launch(gexec, S)
                 hip.sync(S)
@@ -280,7 +280,7 @@ def main():
             ms = hip.elapsed_ms(e0, e1) / args.steps
             torch.cuda.synchronize()
             # per-kernel durations: events recorded by each kernel's own dispatch, same step
-            per = kernel_times(hip, m, S, run_stack(T, biases, x0, bufs, ws))
+            per = kernel_times(hip, m, S, run_stack(T, biases, xs, bufs, ws))
             kern = {k: float(np.mean(v)) for k, v in per.items()}
             touched = [len(np.unique(idx_keep[l].cpu().numpy())) for l in range(nl)]
             layer_bytes = float(np.mean([algorithmic_layer_bytes(wl, u, T) for u in touched]))
@@ -298,7 +298,7 @@ def main():
                                        "bytes_per_launch": gu_bytes}
             rec["gate_up_roofline"]["frac"] = rec["gate_up_roofline"]["achieved"] / HBM_PEAK_GBS
             out[name] = rec
-            out[name + "_state"] = (idx_keep, w_keep, x0, bufs, ws)
+            out[name + "_state"] = (idx_keep, w_keep, xs, bufs, ws)
             log(f"# {name}: {ms:.3f} ms/step, {us_layer:.2f} us/layer, "
                 f"{rec['layer_tokens_per_s']:.0f} layer-tokens/s, {100 * rec['hbm_frac_layer']:.1f}% of HBM peak")
             log(f"#   kernels (us): " + ", ".join(f"{k} {v:.2f}" for k, v in kern.items()))
@@ -352,19 +352,17 @@ def main():
         staging = torch.empty(min(wl.n_experts, 64), nst.blob.shape[2], dtype=torch.uint8, device="cuda")
         rec = {}
         for T in (1, 2048):
-            x0 = synth.make_x(wl, args.seed, "cuda", tokens=T, tag=f"x_nv{T}")
-            bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+            # each layer its own input, as in the decode stack
+            xs = [synth.make_x(wl, args.seed, "cuda", tokens=T, tag=f"x_nv{T}_{l}") for l in range(nvl)]
+            bufs = [torch.empty_like(xs[0]), torch.empty_like(xs[0])]
             ws = m.workspace(nst.shape, T)
             idx = torch.empty(nvl, T, wl.top_k, dtype=torch.int32, device="cuda")
             torch.cuda.synchronize()    # inputs and workspace ready before S uses them
             for staged in (False, True):
                 def step(staged=staged):
-                    cur = x0
                     for l in range(nvl):
-                        nxt = bufs[l % 2]
-                        m.moe_layer(nst.shape, cur, T, nst.router[l], None, nst.table[l],
-                                    staging if staged else None, cur, nxt, idx[l], None, ws, stream=S)
-                        cur = nxt
+                        m.moe_layer(nst.shape, xs[l], T, nst.router[l], None, nst.table[l],
+                                    staging if staged else None, xs[l], bufs[l % 2], idx[l], None, ws, stream=S)
                 with torch.cuda.stream(stream):
                     step()
                 hip.sync(S)
@@ -403,22 +401,15 @@ def main():
     parity = None
     if want("decode") and not args.no_cpu_baseline:
         import oracle
-        idx_keep, w_keep, x0, bufs, ws = out["decode_state"]
-        # every layer's input x_l of the eager step, and its output y_l without the residual
-        xs = [x0]
+        idx_keep, w_keep, xs, bufs, ws = out["decode_state"]
+        # every layer's output y_l without the residual, on its own input x_l
         ys = []
-        cur = x0
         with torch.cuda.stream(stream):
             for l in range(nl):
-                y_l = torch.empty_like(x0)
-                m.moe_layer(stack.shape, cur, 1, stack.router[l], None, stack.table[l], None, None, y_l, None, None,
-                            ws, stream=S)
-                nxt = torch.empty_like(x0)
-                m.moe_layer(stack.shape, cur, 1, stack.router[l], None, stack.table[l], None, cur, nxt, None, None,
-                            ws, stream=S)
-                xs.append(nxt)
+                y_l = torch.empty_like(xs[l])
+                m.moe_layer(stack.shape, xs[l], 1, stack.router[l], None, stack.table[l], None, None, y_l, None,
+                            None, ws, stream=S)
                 ys.append(y_l)
-                cur = nxt
         hip.sync(S)
         t_cpu = 0.0
         n_done = 0
@@ -438,14 +429,17 @@ def main():
             n_done += 1
             exact = exact and bool(np.array_equal(oidx, idx_keep[l].cpu().numpy()))
             gy = oracle.to_f64(ys[l])
-            worst = max(worst, float(np.linalg.norm(gy - oy) / np.linalg.norm(oy)))
+            err = float(np.linalg.norm(gy - oy) / np.linalg.norm(oy))
+            worst = err if not np.isfinite(err) else max(worst, err)     # a NaN or inf fails the check
+            if not np.isfinite(worst):
+                break
             if t_cpu > args.cpu_seconds:
                 break
         cpu = {"value": n_done / t_cpu, "unit": "layer-tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
                "sample": f"decode stack, T=1, first {n_done} of {nl} layers on the GPU's own layer inputs "
                          f"({t_cpu:.1f} s of fp64 oracle time)"}
         parity = {"layers_checked": n_done, "router_indices_exact": exact, "worst_rel_l2_y": worst,
-                  "tolerance": 8e-3, "pass": bool(exact and worst <= 8e-3)}
+                  "tolerance": 8e-3, "pass": bool(exact and np.isfinite(worst) and worst <= 8e-3)}
         log(f"# oracle: {cpu['value']:.3f} layer-tokens/s on {cpu['cores']} threads; parity {parity}")
 
     # ---------------- the one JSON line ----------------
@@ -457,7 +451,9 @@ def main():
         line.update({
             "value": dec["layer_tokens_per_s"], "unit": "layer-tokens/s", "ms_per_step": dec["ms_per_step"],
             "config": {"workload": "decode: 42 stacked MoE layers, d_model 4096, d_ff 2048, 288 MXFP4 experts "
-                                   "(E2M1 + E8M0/32), top-8 sigmoid router, T=1, bf16 activations, flat routing",
+                                   "(E2M1 + E8M0/32), top-8 sigmoid router, T=1, bf16 activations, flat routing; "
+                                   "each layer reads its own unit-scale input (the normalised hidden state), "
+                                   "residual fused",
                        "layers": nl, "tokens_per_step": 1, "parallelism": "single GPU"},
             "stack_tokens_per_s": dec["stack_tokens_per_s"], "us_per_layer": dec["us_per_layer"],
             "hbm_frac_layer": dec["hbm_frac_layer"],
