@@ -20,6 +20,8 @@
 // KSPLIT = 1 they own four different row groups (many tokens per expert: prefill).  The K loop
 // issues every load of a chunk of CH super-steps before its MFMAs, so each wave keeps
 // CH * 64 * SS bytes per weight fragment in flight.
+#include <utility>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -878,8 +880,14 @@ template <int Q>
 struct StepPos {
     static constexpr int value = Q;
 };
+// f(StepPos<B>), f(StepPos<B + 1>), ... in order, for each index of the sequence
+template <int B, typename F, int... I>
+__device__ __forceinline__ void for_steps(F&& f, std::integer_sequence<int, I...>) {
+    (f(StepPos<B + I>{}), ...);
+}
 
-template <int NT, bool GATEUP>
+// FULL: 0, or the step count K / 128 that this instance runs as straight-line code
+template <int NT, bool GATEUP, int FULL>
 __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles_per_xcd_cap) {
     __shared__ __align__(16) uint8_t stg0[kPfStage];
     __shared__ __align__(16) uint8_t stg1[kPfStage];
@@ -1030,6 +1038,14 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
+    // The K extents of the workload (d_model 4096 for gate/up, d_ff 2048 for down) run as straight-
+    // line code: with a loop, the allocator moves accumulators across the back edge, and each such
+    // move waits for the MFMA that writes its source (several hundred cycles).
+    if constexpr (FULL > 0) {
+        for_steps<0>([&](auto i) { step(decltype(i)::value, StepPos<decltype(i)::value % 8>{}); },
+                     std::make_integer_sequence<int, FULL>{});
+        wait_vm<0>();
+    } else {
     int s = 0;
     for (; s + 8 <= nsteps; s += 8) {
         step(s, StepPos<0>{});
@@ -1049,6 +1065,7 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
     if (s + 5 < nsteps) step(s + 5, StepPos<5>{});
     if (s + 6 < nsteps) step(s + 6, StepPos<6>{});
     wait_vm<0>();                                            // no direct load outlives the workgroup
+    }
 
     // columns: n * 16 + li of this wave's 64 = (pick tc, term t)
 #pragma unroll
@@ -1111,8 +1128,16 @@ static hipError_t launch_pf(const GemmArgs& a, int NT, int max_tiles, hipStream_
     const int MT = GATEUP ? a.f / 128 : (a.d + kPfRows - 1) / kPfRows;
     const int cap = (max_tiles + 7) / 8;
     dim3 grid((unsigned)(8 * cap * MT));
-    if (NT == 2) MOE_LAUNCH((k_mx_pf<2, GATEUP>), grid, dim3(256), 0, st, a, 1, cap);
-    else MOE_LAUNCH((k_mx_pf<4, GATEUP>), grid, dim3(256), 0, st, a, 1, cap);
+    // the workload's K (d_model 4096 for gate/up, d_ff 2048 for down) takes the straight-line instance
+    constexpr int kFull = GATEUP ? 32 : 16;
+    const bool full = (GATEUP ? a.d : a.f) == 128 * kFull;
+    if (NT == 2) {
+        if (full) MOE_LAUNCH((k_mx_pf<2, GATEUP, kFull>), grid, dim3(256), 0, st, a, 1, cap);
+        else MOE_LAUNCH((k_mx_pf<2, GATEUP, 0>), grid, dim3(256), 0, st, a, 1, cap);
+    } else {
+        if (full) MOE_LAUNCH((k_mx_pf<4, GATEUP, kFull>), grid, dim3(256), 0, st, a, 1, cap);
+        else MOE_LAUNCH((k_mx_pf<4, GATEUP, 0>), grid, dim3(256), 0, st, a, 1, cap);
+    }
     return hipGetLastError();
 }
 
