@@ -138,7 +138,11 @@ moe_status moe_route(const moe_shape *shape, const void *x, int32_t T, const flo
  * expert_offsets: [n_experts+1], picks of expert e are sorted positions
  *   [expert_offsets[e], expert_offsets[e+1]);  sorted_pick: [T*top_k] pick id at each
  *   sorted position;  pick_pos: [T*top_k] sorted position of each pick (inverse).
- * Expert ids in topk_idx must be in [0, n_experts). */
+ * Expert ids in topk_idx must be in [0, n_experts).
+ * ws / ws_bytes: NULL, or the workspace of moe_workspace_bytes(shape, T) bytes (less is
+ *   MOE_ERR_WORKSPACE).  With it, 4096 or more picks are sorted by one workgroup per 1024 picks,
+ *   whose per-block expert counts it holds; without it one workgroup sorts them all.  The
+ *   result is the same either way. */
 moe_status moe_permute(const moe_shape *shape, const int32_t *topk_idx, int32_t T,
                        int32_t *expert_offsets, int32_t *sorted_pick, int32_t *pick_pos,
                        void *ws, size_t ws_bytes, hipStream_t stream);

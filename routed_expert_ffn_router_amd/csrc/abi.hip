@@ -58,6 +58,7 @@ WsLayout ws_layout(const moe_shape* s, int32_t T) {
     L.offsets = take(4 * (E + 1));
     L.sorted_pick = take(4 * P);
     L.pick_pos = take(4 * P);
+    L.perm_blocks = take(4 * ((P + 1023) / 1024) * E);
     L.tiles = take(8 * (size_t)L.max_tiles);
     L.ntiles = take(4);
     L.desc = take(sizeof(TileDesc) * (size_t)L.max_tiles);
@@ -277,11 +278,15 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t T, i
                        int32_t* sorted_pick, int32_t* pick_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
     MOE_TRY(check_shape(s));
     MOE_TRY(check_T(s, T));
-    (void)ws;
-    (void)ws_bytes;
     if (!topk_idx || !expert_offsets || !sorted_pick || !pick_pos) return MOE_ERR_INVALID;
     if (T == 0) return MOE_OK;
-    return hip_status(launch_permute(s, topk_idx, T, expert_offsets, sorted_pick, pick_pos, stream));
+    int32_t* bcnt = nullptr;         // with a workspace, many picks are sorted by many workgroups
+    if (ws) {
+        const WsLayout L = ws_layout(s, T);
+        if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+        bcnt = (int32_t*)((uint8_t*)ws + L.perm_blocks);
+    }
+    return hip_status(launch_permute(s, topk_idx, T, expert_offsets, sorted_pick, pick_pos, bcnt, stream));
 }
 
 moe_status moe_gather_experts(const moe_shape* s, const moe_expert* d_table, const int32_t* d_list, int32_t n,
@@ -403,7 +408,7 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
     }
     MOE_HIP(launch_router_logits(s, x, T, w_router, logit_bias, logits, stream));
     MOE_HIP(launch_topk(s, logits, T, idx, w, stream));
-    MOE_HIP(launch_permute(s, idx, T, offsets, sorted_pick, pick_pos, stream));
+    MOE_HIP(launch_permute(s, idx, T, offsets, sorted_pick, pick_pos, (int32_t*)(w8 + L.perm_blocks), stream));
     if (nv) MOE_TRY(run_ffn_nv(s, d_table, x, T, offsets, sorted_pick, o, w8, L, staging, stream));
     else MOE_TRY(run_ffn(s, d_table, x, T, offsets, sorted_pick, o, w8, L, stream));
     MOE_HIP(launch_combine(s, o, w, pick_pos, T, residual, y, stream));

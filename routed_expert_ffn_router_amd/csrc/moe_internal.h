@@ -323,7 +323,8 @@ struct TileDesc {
 static_assert(sizeof(TileDesc) == 128, "tile record is 128 bytes");
 
 struct WsLayout {
-    size_t slots, sink, logits, idx, w, offsets, sorted_pick, pick_pos, tiles, ntiles, desc, xq, xs, hq, hs, o;
+    size_t slots, sink, logits, idx, w, offsets, sorted_pick, pick_pos, perm_blocks, tiles, ntiles, desc, xq, xs,
+        hq, hs, o;
     size_t stage_table, stage_list, stage_n, stage_ranges;   // NVFP4 staging (moe_layer)
     size_t total;
     int nt;        // activation terms
@@ -342,8 +343,9 @@ hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t*
                        hipStream_t st);
 hipError_t launch_act_split(const moe_shape* s, const void* x, int rows, int K, int SS, int NT,
                             uint8_t* q, uint8_t* sc, hipStream_t st);
+// bcnt: per-block expert counts ([ceil(T * top_k / 1024)][n_experts] int32) or null (one workgroup)
 hipError_t launch_permute(const moe_shape* s, const int32_t* idx, int T, int32_t* offsets,
-                          int32_t* sorted_pick, int32_t* pick_pos, hipStream_t st);
+                          int32_t* sorted_pick, int32_t* pick_pos, int32_t* bcnt, hipStream_t st);
 hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int tile_tokens, int32_t* tiles,
                        int32_t* ntiles, hipStream_t st);
 

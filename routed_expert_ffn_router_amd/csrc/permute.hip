@@ -8,6 +8,7 @@ namespace moe {
 
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
+constexpr int kPermMultiBlocks = 4;    // blocks of picks from which the sort spreads over workgroups
 
 // Block-wide exclusive scan of one int per thread (1024 threads).  Returns the exclusive
 // prefix; *total receives the sum.  Uses `scratch` (kPermWaves ints) in LDS.
@@ -30,6 +31,21 @@ __device__ int block_excl_scan(int v, int* scratch, int* total) {
     __syncthreads();
     *total = tot;
     return wbase + incl - v;
+}
+
+// Rank of this lane's pick among the lanes of its wave holding the same expert id (ballots over
+// the id's 10 bits; ids are below 1024), and their number in *n.  Lanes with e < 0 take part in no
+// group.
+__device__ __forceinline__ int wave_peer_rank(int e, int lane, int* n) {
+    unsigned long long peers = __ballot(e >= 0);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {
+        unsigned long long m = __ballot((e >> b) & 1);
+        peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    *n = __popcll(peers);
+    return __popcll(peers & lt_mask);
 }
 
 // One workgroup of 1024 threads.  LDS: counts and running cursors per expert, and per-wave
@@ -59,20 +75,12 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
     }
     if (tid == 0) offsets[E] = total;
     __syncthreads();
-    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int base = 0; base < P; base += kPermThreads) {
         const int p = base + tid;
         int e = (p < P) ? idx[p] : -1;
         if (e >= E) e = -1;
-        // lanes of this wave holding the same expert id
-        unsigned long long peers = __ballot(e >= 0);
-#pragma unroll
-        for (int b = 0; b < 10; ++b) {
-            unsigned long long m = __ballot((e >> b) & 1);
-            peers &= ((e >> b) & 1) ? m : ~m;
-        }
-        const int rank = __popcll(peers & lt_mask);
-        const int n = __popcll(peers);
+        int n;
+        const int rank = wave_peer_rank(e, lane, &n);
         if (e >= 0 && rank == 0) wcnt[wv][e] = n;
         __syncthreads();
         if (e >= 0) {
@@ -90,12 +98,87 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
     }
 }
 
+// Many picks: the same counting sort over blocks of kPermThreads picks, one workgroup per block.
+// (1) per-block counts per expert; (2) one workgroup turns them, expert by expert, into each
+// block's first position relative to the expert's offset, and scans the totals into the offsets;
+// (3) each block places its picks at offset + block start + rank within the block, which is the
+// single-workgroup order (stable in pick order).  bcnt: [nblk][E] int32 in the workspace.
+__global__ __launch_bounds__(kPermThreads) void k_perm_count(const int32_t* __restrict__ idx, int P, int E,
+                                                             int32_t* __restrict__ bcnt) {
+    __shared__ int cnt[1024];
+    const int tid = threadIdx.x;
+    cnt[tid] = 0;
+    __syncthreads();
+    const int p = blockIdx.x * kPermThreads + tid;
+    if (p < P) {
+        const int e = idx[p];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    if (tid < E) bcnt[(size_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(kPermThreads) void k_perm_scan(int nblk, int E, int32_t* __restrict__ bcnt,
+                                                            int32_t* __restrict__ offsets) {
+    __shared__ int scratch[kPermWaves];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int b0 = 0; b0 < nblk; b0 += 8) {      // eight blocks' loads in flight at once
+            int c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = (b0 + i < nblk) ? bcnt[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (b0 + i < nblk) bcnt[(size_t)(b0 + i) * E + e] = run;
+                run += c[i];
+            }
+        }
+    }
+    int total;
+    const int excl = block_excl_scan(e < E ? run : 0, scratch, &total);
+    if (e < E) offsets[e] = excl;
+    if (e == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(kPermThreads) void k_perm_scatter(const int32_t* __restrict__ idx, int P, int E,
+                                                               const int32_t* __restrict__ bcnt,
+                                                               const int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ sorted_pick,
+                                                               int32_t* __restrict__ pick_pos) {
+    __shared__ int wcnt[kPermWaves][1024];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int p = blockIdx.x * kPermThreads + tid;
+    int e = (p < P) ? idx[p] : -1;
+    if (e >= E) e = -1;
+    for (int i = tid; i < kPermWaves * 1024; i += kPermThreads) (&wcnt[0][0])[i] = 0;
+    int n;
+    const int rank = wave_peer_rank(e, lane, &n);
+    __syncthreads();
+    if (e >= 0 && rank == 0) wcnt[wv][e] = n;
+    __syncthreads();
+    if (e >= 0) {
+        int pos = offsets[e] + bcnt[(size_t)blockIdx.x * E + e] + rank;
+        for (int w = 0; w < wv; ++w) pos += wcnt[w][e];
+        sorted_pick[pos] = p;
+        pick_pos[p] = pos;
+    }
+}
+
 hipError_t launch_permute(const moe_shape* s, const int32_t* idx, int T, int32_t* offsets,
-                          int32_t* sorted_pick, int32_t* pick_pos, hipStream_t st) {
+                          int32_t* sorted_pick, int32_t* pick_pos, int32_t* bcnt, hipStream_t st) {
     trace("permute", 0, st);
     const int P = T * s->top_k;
-    MOE_LAUNCH(k_permute, dim3(1), dim3(kPermThreads), 0, st, idx, P, s->n_experts, offsets,
-                       sorted_pick, pick_pos);
+    const int nblk = (P + kPermThreads - 1) / kPermThreads;
+    if (bcnt && nblk >= kPermMultiBlocks) {
+        MOE_LAUNCH(k_perm_count, dim3(nblk), dim3(kPermThreads), 0, st, idx, P, s->n_experts, bcnt);
+        MOE_LAUNCH(k_perm_scan, dim3(1), dim3(kPermThreads), 0, st, nblk, s->n_experts, bcnt, offsets);
+        MOE_LAUNCH(k_perm_scatter, dim3(nblk), dim3(kPermThreads), 0, st, idx, P, s->n_experts, bcnt, offsets,
+                   sorted_pick, pick_pos);
+    } else {
+        MOE_LAUNCH(k_permute, dim3(1), dim3(kPermThreads), 0, st, idx, P, s->n_experts, offsets,
+                   sorted_pick, pick_pos);
+    }
     trace("permute", 1, st);
     return hipGetLastError();
 }

@@ -83,15 +83,24 @@ def test_route_nan_rows_and_zero_tokens(T):
     np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=2e-7, atol=1e-8)
 
 
-@pytest.mark.parametrize("T,k,E", [(1, 8, 288), (5, 2, 16), (64, 8, 288), (4096, 8, 288), (1000, 8, 1024)])
-def test_permute_bit_exact(T, k, E):
+# with a workspace, 4+ blocks of 1024 picks are sorted by one workgroup per block; (3000, 2, 4) puts
+# runs of one expert across every block boundary, (1000, 8, 1024) ends in a ragged block
+@pytest.mark.parametrize("with_ws", [False, True])
+@pytest.mark.parametrize("T,k,E", [(1, 8, 288), (5, 2, 16), (64, 8, 288), (4096, 8, 288), (1000, 8, 1024),
+                                   (3000, 2, 4)])
+def test_permute_bit_exact(T, k, E, with_ws):
     g = torch.Generator().manual_seed(T + E)
     idx = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).to(torch.int32)
     shape = m.make_shape(256, 128, E, k)
     off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
     pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
-    m.moe_permute(shape, idx.cuda(), T, off, sp, pp)
+    if with_ws:
+        ws = m.workspace(shape, T)
+        torch.cuda.synchronize()
+        m.moe_permute(shape, idx.cuda(), T, off, sp, pp, ws, ws.numel() * ws.element_size())
+    else:
+        m.moe_permute(shape, idx.cuda(), T, off, sp, pp)
     torch.cuda.synchronize()
     ooff, osp, opp = oracle.permute(idx.numpy(), E)
     np.testing.assert_array_equal(off.cpu().numpy(), ooff)
