@@ -37,7 +37,9 @@ __global__ __launch_bounds__(256) void k_logits_gemv(const XT* __restrict__ x, i
 // tokens x 64 experts and one K slice of the split; wave w computes tokens 16 (w & 1) + [0, 16)
 // against experts 32 (w >> 1) + [0, 32) as two 16x16 blocks.  Operand layout (measured): lane l
 // supplies row or column l % 16 at K = l / 16; result register r of lane l is row 4 r + l / 16,
-// column l % 16.  The K slice is staged through LDS 64 columns at a time as fp32.  Slice z's
+// column l % 16.  Within each group of 16 K values, the four MFMAs j = 0..3 take K = 4 (l / 16) + j
+// (each K once), so a lane reads its four values with one 16-byte LDS load.  The K slice is staged
+// through LDS 64 columns at a time as fp32, rows padded to 68 floats (16-byte aligned).  Slice z's
 // partial sums go to part[z][t][e]; slice 0 also adds the bias.  The top-k sums the slices in
 // order z = 0, 1, ...
 constexpr int kLgTok = 32, kLgExp = 64, kLgK = 64;
@@ -46,8 +48,8 @@ template <typename XT>
 __global__ __launch_bounds__(256) void k_logits_mfma(const XT* __restrict__ x, int T, int d,
                                                       const float* __restrict__ wr, const float* __restrict__ bias,
                                                       int E, int kslice, double* __restrict__ part) {
-    __shared__ float xs[2][kLgTok][kLgK + 1];
-    __shared__ float ws[2][kLgExp][kLgK + 1];
+    __shared__ __align__(16) float xs[2][kLgTok][kLgK + 4];
+    __shared__ __align__(16) float ws[2][kLgExp][kLgK + 4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t0 = blockIdx.x * kLgTok, e0 = blockIdx.y * kLgExp, z = blockIdx.z;
     const int kb = z * kslice;
@@ -93,13 +95,18 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const XT* __restrict__ x, i
     for (int ch = 0; ch < nch; ++ch) {
         const int buf = ch & 1;
         if (ch + 1 < nch) load_chunk((ch + 1) * kLgK);
-#pragma unroll 4
-        for (int kk = 0; kk < kLgK; kk += 4) {
-            const double a = (double)xs[buf][tr][kk + kl];
-            const double b0 = (double)ws[buf][ec][kk + kl];
-            const double b1 = (double)ws[buf][ec + 16][kk + kl];
-            acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b0, acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b1, acc[1], 0, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < kLgK; kk += 16) {
+            const float4 a4 = *(const float4*)&xs[buf][tr][kk + 4 * kl];
+            const float4 b4 = *(const float4*)&ws[buf][ec][kk + 4 * kl];
+            const float4 c4 = *(const float4*)&ws[buf][ec + 16][kk + 4 * kl];
+            const float av[4] = {a4.x, a4.y, a4.z, a4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w},
+                        cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[j], (double)bv[j], acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[j], (double)cv[j], acc[1], 0, 0, 0);
+            }
         }
         if (ch + 1 < nch) store_chunk(buf ^ 1);
         __syncthreads();
