@@ -69,6 +69,8 @@ def test_validation_other_entry_points():
     nv = m.make_shape(256, 128, 16, 2, 1, 0)
     b = ctypes.byref
     assert L.moe_permute(b(sh), None, 4, FAKE, FAKE, FAKE, None, 0, 0) == m.MOE_ERR_INVALID
+    # a workspace, when given, must hold the layout for (shape, T)
+    assert L.moe_permute(b(sh), FAKE, 4, FAKE, FAKE, FAKE, FAKE, 16, 0) == m.MOE_ERR_WORKSPACE
     assert L.moe_expert_ffn(b(sh), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 16, 0) == m.MOE_ERR_WORKSPACE
     assert L.moe_expert_ffn(b(nv), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 16, 0) == m.MOE_ERR_WORKSPACE
     # staging belongs to the NVFP4 gather path; it must be 16-byte aligned
