@@ -22,6 +22,9 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_WF_MXFP4, MOE_WF_NVFP4 = 0, 1
+MOE_AQ_EXACT, MOE_AQ_MXFP8 = 0, 1
+MOE_WS_STATUS_OFFSET = 0
+MOE_WS_ROUTE_TIMEOUT, MOE_WS_BAD_EXPERT_ID = 0x1, 0x2
 
 
 class MoeError(RuntimeError):
@@ -33,7 +36,8 @@ class MoeError(RuntimeError):
 class moe_shape(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("wformat", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("routed_scaling", ctypes.c_float)]
+                ("routed_scaling", ctypes.c_float), ("renorm_skip", ctypes.c_float), ("n_shared", ctypes.c_int32),
+                ("act_quant", ctypes.c_int32)]
 
 
 class moe_expert(ctypes.Structure):
@@ -54,11 +58,22 @@ _P = ctypes.c_void_p
 _SP = ctypes.POINTER(moe_shape)
 _i32 = ctypes.c_int32
 _sz = ctypes.c_size_t
+TRACE_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int, ctypes.c_void_p)
+EVENT_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p),
+                              ctypes.POINTER(ctypes.c_void_p))
+
+
+class moe_observer(ctypes.Structure):
+    _fields_ = [("trace_hook", ctypes.c_void_p), ("trace_user", ctypes.c_void_p),
+                ("event_hook", ctypes.c_void_p), ("event_user", ctypes.c_void_p)]
+
+
 _SIGS = {
     "moe_abi_version": (ctypes.c_int, []),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_blob_stride": (_sz, [_SP]),
     "moe_workspace_bytes": (_sz, [_SP, _i32]),
+    "moe_workspace_init": (ctypes.c_int, [_SP, _i32, _P, _sz, _i32, _P]),
     "moe_fill_table": (ctypes.c_int, [_SP, _P, _sz, _P, _P]),
     "moe_route": (ctypes.c_int, [_SP, _P, _i32, _P, _P, _P, _P, _P, _sz, _P]),
     "moe_permute": (ctypes.c_int, [_SP, _P, _i32, _P, _P, _P, _P, _sz, _P]),
@@ -66,8 +81,8 @@ _SIGS = {
     "moe_expert_ffn": (ctypes.c_int, [_SP, _P, _P, _i32, _P, _P, _P, _P, _sz, _P]),
     "moe_combine": (ctypes.c_int, [_SP, _P, _P, _P, _i32, _P, _P, _P]),
     "moe_layer": (ctypes.c_int, [_SP, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
-    "moe_set_trace_hook": (None, [_P, _P]),
-    "moe_set_event_hook": (None, [_P, _P]),
+    "moe_layer_observed": (ctypes.c_int, [_SP, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P,
+                                          ctypes.POINTER(moe_observer)]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -75,44 +90,27 @@ for _name, (_res, _args) in _SIGS.items():
     _fn.argtypes = _args
 
 
-TRACE_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int, ctypes.c_void_p)
-_hook_ref = None
-
-
-def moe_set_trace_hook(hook):
-    """Install a Python callable hook(kernel: str, phase: int, stream: int), or None to clear.
-
-    The library calls it right before (phase 0) and after (phase 1) enqueuing each kernel."""
-    global _hook_ref
-    if hook is None:
-        _hook_ref = None
-        _lib.moe_set_trace_hook(None, None)
-        return
-    _hook_ref = TRACE_HOOK(lambda user, name, phase, stream: hook(name.decode(), phase, stream or 0))
-    _lib.moe_set_trace_hook(ctypes.cast(_hook_ref, ctypes.c_void_p), None)
-
-
-EVENT_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p),
-                              ctypes.POINTER(ctypes.c_void_p))
-_ev_hook_ref = None
-
-
-def moe_set_event_hook(hook):
-    """Install hook(kernel: str) -> (start_event, stop_event) or None (raw hipEvent_t handles as
-    ints), or None to clear.  A returned pair is recorded at the kernel's own start and end."""
-    global _ev_hook_ref
-    if hook is None:
-        _ev_hook_ref = None
-        _lib.moe_set_event_hook(None, None)
-        return
-
-    def _cb(user, name, start, stop):
-        pair = hook(name.decode())
-        if pair is not None:
-            start[0], stop[0] = pair
-
-    _ev_hook_ref = EVENT_HOOK(_cb)
-    _lib.moe_set_event_hook(ctypes.cast(_ev_hook_ref, ctypes.c_void_p), None)
+def make_observer(trace=None, events=None):
+    """An observer for moe_layer_observed: trace(kernel: str, phase: int, stream: int) is called
+    before (phase 0) and after (phase 1) each kernel is enqueued; events(kernel: str) may return a
+    pair of raw hipEvent_t handles (ints) that the kernel's own dispatch records at its start and
+    end, or None.  Returns the structure; keep it alive for the duration of the call."""
+    obs = moe_observer()
+    refs = []
+    if trace is not None:
+        cb = TRACE_HOOK(lambda user, name, phase, stream: trace(name.decode(), phase, stream or 0))
+        refs.append(cb)
+        obs.trace_hook = ctypes.cast(cb, ctypes.c_void_p)
+    if events is not None:
+        def _ev(user, name, start, stop):
+            pair = events(name.decode())
+            if pair is not None:
+                start[0], stop[0] = pair
+        cb = EVENT_HOOK(_ev)
+        refs.append(cb)
+        obs.event_hook = ctypes.cast(cb, ctypes.c_void_p)
+    obs._refs = refs         # the callbacks live as long as the structure
+    return obs
 
 
 def header_functions() -> list:
@@ -156,8 +154,10 @@ def _check(fn: str, status: int):
 
 
 def make_shape(d_model: int, d_ff: int, n_experts: int, top_k: int, wformat: int = MOE_WF_MXFP4,
-               act_dtype: int = MOE_DT_BF16, routed_scaling: float = 1.0) -> moe_shape:
-    return moe_shape(d_model, d_ff, n_experts, top_k, wformat, act_dtype, routed_scaling)
+               act_dtype: int = MOE_DT_BF16, routed_scaling: float = 1.0, renorm_skip: float = 0.0,
+               n_shared: int = 0, act_quant: int = MOE_AQ_EXACT) -> moe_shape:
+    return moe_shape(d_model, d_ff, n_experts, top_k, wformat, act_dtype, routed_scaling, renorm_skip, n_shared,
+                     act_quant)
 
 
 def abi_version() -> int:
@@ -177,7 +177,8 @@ def moe_workspace_bytes(shape: moe_shape, T: int) -> int:
 
 
 def workspace(shape: moe_shape, T: int, device="cuda"):
-    """A zero-filled uint8 device tensor of moe_workspace_bytes(shape, T) bytes (at least 256).
+    """A zero-filled uint8 device tensor of moe_workspace_bytes(shape, T) bytes (at least 256): a
+    prepared workspace (status 0, default poll limit).
 
     The zero fill runs on torch's current stream: a caller that launches on another stream makes
     that stream wait for it first (torch.cuda.synchronize() or Stream.wait_stream), as for any input.
@@ -185,6 +186,18 @@ def workspace(shape: moe_shape, T: int, device="cuda"):
     import torch
     n = max(moe_workspace_bytes(shape, T), 256)
     return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_workspace_init(shape, T: int, ws, poll_limit: int = 0, ws_bytes=None, stream=None):
+    ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check("moe_workspace_init", _lib.moe_workspace_init(ctypes.byref(shape), T, _ptr(ws), ws_bytes, poll_limit,
+                                                         _stream(stream)))
+
+
+def workspace_status(ws) -> int:
+    """The workspace's status word (MOE_WS_* bits); reads 4 bytes back, so it synchronises."""
+    import torch
+    return int(ws[MOE_WS_STATUS_OFFSET:MOE_WS_STATUS_OFFSET + 4].cpu().view(torch.int32)[0]) & 0xFFFFFFFF
 
 
 def moe_fill_table(shape, base, stride: int, table, stream=None):
@@ -223,9 +236,12 @@ def moe_combine(shape, o, topk_w, pick_pos, T: int, residual, y, stream=None):
 
 
 def moe_layer(shape, x, T: int, w_router, logit_bias, d_table, staging, residual, y, topk_idx_out=None,
-              topk_w_out=None, ws=None, ws_bytes=None, stream=None):
+              topk_w_out=None, ws=None, ws_bytes=None, stream=None, observer=None):
+    """moe_layer, or moe_layer_observed when an observer (make_observer) is given."""
     ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
-    _check("moe_layer", _lib.moe_layer(ctypes.byref(shape), _ptr(x), T, _ptr(w_router), _ptr(logit_bias),
-                                       _ptr(d_table), _ptr(staging), _ptr(residual), _ptr(y),
-                                       _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), ws_bytes,
-                                       _stream(stream)))
+    args = (ctypes.byref(shape), _ptr(x), T, _ptr(w_router), _ptr(logit_bias), _ptr(d_table), _ptr(staging),
+            _ptr(residual), _ptr(y), _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), ws_bytes, _stream(stream))
+    if observer is None:
+        _check("moe_layer", _lib.moe_layer(*args))
+    else:
+        _check("moe_layer_observed", _lib.moe_layer_observed(*args, ctypes.byref(observer)))

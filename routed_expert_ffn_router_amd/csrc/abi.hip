@@ -9,18 +9,25 @@ namespace moe {
 
 constexpr int kSmallTokens = 16;   // moe_layer's fused three-launch path
 
-static moe_trace_hook g_hook = nullptr;
-static void* g_hook_user = nullptr;
-
-static moe_event_hook g_ev_hook = nullptr;
-static void* g_ev_user = nullptr;
+// The observer of the call in progress on this thread (moe_layer_observed), null otherwise: it
+// lives only for the duration of that call, so the library keeps no state between calls.
+static thread_local const moe_observer* t_obs = nullptr;
 static thread_local hipEvent_t t_launch_ev[2] = {nullptr, nullptr};
 
+struct ObserverScope {
+    explicit ObserverScope(const moe_observer* o) { t_obs = o; }
+    ~ObserverScope() {
+        t_obs = nullptr;
+        t_launch_ev[0] = t_launch_ev[1] = nullptr;
+    }
+};
+
 void trace(const char* kernel, int phase, hipStream_t st) {
-    if (g_hook) g_hook(g_hook_user, kernel, phase, st);
     t_launch_ev[0] = t_launch_ev[1] = nullptr;
-    if (phase == 0 && g_ev_hook) {
-        g_ev_hook(g_ev_user, kernel, &t_launch_ev[0], &t_launch_ev[1]);
+    if (!t_obs) return;
+    if (t_obs->trace_hook) t_obs->trace_hook(t_obs->trace_user, kernel, phase, st);
+    if (phase == 0 && t_obs->event_hook) {
+        t_obs->event_hook(t_obs->event_user, kernel, &t_launch_ev[0], &t_launch_ev[1]);
         if (!t_launch_ev[0] || !t_launch_ev[1]) t_launch_ev[0] = t_launch_ev[1] = nullptr;
     }
 }
@@ -46,8 +53,10 @@ WsLayout ws_layout(const moe_shape* s, int32_t T) {
     L.max_tiles = (int)((E < P ? E : P) + P / tt + 1);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
-    // the fused router's logit hand-over: the same bytes in the layout of every T, used by nothing
-    // else, so that calls with different T on one workspace keep it zero
+    // status word and poll limit (MOE_WS_STATUS_OFFSET = 0), then the fused router's logit
+    // hand-over: the same bytes in the layout of every T, used by nothing else, so that calls with
+    // different T on one workspace keep them
+    L.hdr = take(kWsHeaderBytes);
     L.slots = take(8 * (size_t)kSmallTokens * E);
     // write-only scratch of the one-token router's warm-up pass
     const size_t sink_rec = sizeof(TileDesc) * (size_t)L.max_tiles, sink_slots = 8 * (E + 1);
@@ -94,6 +103,11 @@ static moe_status check_shape(const moe_shape* s) {
     if (s->wformat != MOE_WF_MXFP4 && s->wformat != MOE_WF_NVFP4) return MOE_ERR_INVALID;
     if (s->act_dtype != MOE_DT_F32 && s->act_dtype != MOE_DT_BF16) return MOE_ERR_INVALID;
     if (!isfinite(s->routed_scaling)) return MOE_ERR_INVALID;
+    if (!isfinite(s->renorm_skip) || s->renorm_skip < 0.0f || s->renorm_skip >= 1.0f) return MOE_ERR_INVALID;
+    if (s->n_shared != 0 && s->n_shared != 1) return MOE_ERR_INVALID;
+    if (s->act_quant != MOE_AQ_EXACT && s->act_quant != MOE_AQ_MXFP8) return MOE_ERR_INVALID;
+    if (s->act_quant == MOE_AQ_MXFP8 && s->wformat != MOE_WF_MXFP4) return MOE_ERR_UNSUPPORTED;
+    if (s->n_shared != 0 || s->renorm_skip != 0.0f || s->act_quant != MOE_AQ_EXACT) return MOE_ERR_UNSUPPORTED;
     if (s->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
     if (s->d_model % 128 != 0 || s->d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
     if ((long long)s->d_model * s->d_ff > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
@@ -214,16 +228,6 @@ extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-void moe_set_trace_hook(moe_trace_hook hook, void* user) {
-    g_hook = hook;
-    g_hook_user = user;
-}
-
-void moe_set_event_hook(moe_event_hook hook, void* user) {
-    g_ev_hook = hook;
-    g_ev_user = user;
-}
-
 const char* moe_status_string(moe_status status) {
     switch (status) {
         case MOE_OK: return "ok";
@@ -247,6 +251,19 @@ size_t moe_blob_stride(const moe_shape* s) {
 size_t moe_workspace_bytes(const moe_shape* s, int32_t T) {
     if (check_shape(s) != MOE_OK || check_T(s, T) != MOE_OK) return 0;
     return ws_layout(s, T).total;
+}
+
+moe_status moe_workspace_init(const moe_shape* s, int32_t T, void* ws, size_t ws_bytes, int32_t poll_limit,
+                              hipStream_t stream) {
+    MOE_TRY(check_shape(s));
+    MOE_TRY(check_T(s, T));
+    if (!ws) return MOE_ERR_INVALID;
+    if (!aligned(ws, 256)) return MOE_ERR_INVALID;
+    const WsLayout L = ws_layout(s, T);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    // the header and the hand-over slots are the workspace's first bytes (one range)
+    const size_t end = L.slots + 8 * (size_t)kSmallTokens * s->n_experts;
+    return hip_status(launch_ws_init((uint32_t*)ws, end / 4, poll_limit, stream));
 }
 
 moe_status moe_fill_table(const moe_shape* s, const void* base, size_t stride, moe_expert* table,
@@ -281,12 +298,15 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t T, i
     if (!topk_idx || !expert_offsets || !sorted_pick || !pick_pos) return MOE_ERR_INVALID;
     if (T == 0) return MOE_OK;
     int32_t* bcnt = nullptr;         // with a workspace, many picks are sorted by many workgroups
+    uint32_t* status = nullptr;
     if (ws) {
+        if (!aligned(ws, 256)) return MOE_ERR_INVALID;
         const WsLayout L = ws_layout(s, T);
         if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
         bcnt = (int32_t*)((uint8_t*)ws + L.perm_blocks);
+        status = (uint32_t*)((uint8_t*)ws + L.hdr);
     }
-    return hip_status(launch_permute(s, topk_idx, T, expert_offsets, sorted_pick, pick_pos, bcnt, stream));
+    return hip_status(launch_permute(s, topk_idx, T, expert_offsets, sorted_pick, pick_pos, bcnt, status, stream));
 }
 
 moe_status moe_gather_experts(const moe_shape* s, const moe_expert* d_table, const int32_t* d_list, int32_t n,
@@ -327,6 +347,15 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
                      const float* logit_bias, const moe_expert* d_table, void* staging, const void* residual,
                      void* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
+    return moe_layer_observed(s, x, T, w_router, logit_bias, d_table, staging, residual, y, topk_idx_out,
+                              topk_w_out, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_observed(const moe_shape* s, const void* x, int32_t T, const float* w_router,
+                              const float* logit_bias, const moe_expert* d_table, void* staging,
+                              const void* residual, void* y, int32_t* topk_idx_out, float* topk_w_out, void* ws,
+                              size_t ws_bytes, hipStream_t stream, const moe_observer* observer) {
+    ObserverScope scope(observer);
     MOE_TRY(check_shape(s));
     MOE_TRY(check_T(s, T));
     if (T == 0) return MOE_OK;
@@ -363,6 +392,7 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
         r.wr = w_router;
         r.bias = logit_bias;
         r.logits = logits;
+        r.hdr = (uint32_t*)(w8 + L.hdr);
         r.slots = (unsigned long long*)(w8 + L.slots);
         r.sink = w8 + L.sink;
         r.idx = idx;
@@ -408,7 +438,8 @@ moe_status moe_layer(const moe_shape* s, const void* x, int32_t T, const float* 
     }
     MOE_HIP(launch_router_logits(s, x, T, w_router, logit_bias, logits, stream));
     MOE_HIP(launch_topk(s, logits, T, idx, w, stream));
-    MOE_HIP(launch_permute(s, idx, T, offsets, sorted_pick, pick_pos, (int32_t*)(w8 + L.perm_blocks), stream));
+    MOE_HIP(launch_permute(s, idx, T, offsets, sorted_pick, pick_pos, (int32_t*)(w8 + L.perm_blocks),
+                           (uint32_t*)(w8 + L.hdr), stream));
     if (nv) MOE_TRY(run_ffn_nv(s, d_table, x, T, offsets, sorted_pick, o, w8, L, staging, stream));
     else MOE_TRY(run_ffn(s, d_table, x, T, offsets, sorted_pick, o, w8, L, stream));
     MOE_HIP(launch_combine(s, o, w, pick_pos, T, residual, y, stream));

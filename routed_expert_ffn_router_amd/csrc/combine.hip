@@ -4,7 +4,8 @@
 namespace moe {
 
 // y[t] = s * sum_j w[t,j] * o[pick_pos[t*k+j]] (+ residual[t]); one thread per 4 columns,
-// the k terms summed in rank order in fp32, rounded once to the output dtype.
+// the k terms summed in rank order in fp32 (picks with pick_pos -1 left out), rounded once to the
+// output dtype.
 template <typename XT>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, const float* __restrict__ w,
                                                  const int32_t* __restrict__ pick_pos, int T, int k, int d,
@@ -16,7 +17,9 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, co
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
         const float wj = w[(size_t)t * k + j];
-        const float4 v = *(const float4*)(o + (size_t)pick_pos[(size_t)t * k + j] * d + c);
+        const int pos = pick_pos[(size_t)t * k + j];
+        if (pos < 0) continue;                  // a pick without an expert (dropped or refused)
+        const float4 v = *(const float4*)(o + (size_t)pos * d + c);
         acc.x = fmaf(wj, v.x, acc.x);
         acc.y = fmaf(wj, v.y, acc.y);
         acc.z = fmaf(wj, v.z, acc.z);

@@ -300,11 +300,12 @@ __device__ __forceinline__ void split_rows_lanewise(const XT* __restrict__ x, in
 // launchers (one per kernel family); all return hipGetLastError() of their launch
 // ---------------------------------------------------------------------------------------------
 
-// tracing hook (set through moe_set_trace_hook); every launcher brackets its launch with these
+// every launcher brackets its launch with these: they call the hooks of the observer of the call in
+// progress (moe_layer_observed), if any
 void trace(const char* kernel, int phase, hipStream_t st);
 
-// timing events for the launch being enqueued (from the event hook, at trace phase 0; null when
-// there is none): every launch goes through MOE_LAUNCH, which hands them to hipExtLaunchKernel
+// timing events for the launch being enqueued (from the observer's event hook, at trace phase 0;
+// null when there is none): every launch goes through MOE_LAUNCH, which hands them to hipExtLaunchKernel
 hipEvent_t launch_event(int which);
 #define MOE_LAUNCH(kernel, grid, block, shm, st, ...)                                                  \
     hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)(shm), st, ::moe::launch_event(0),            \
@@ -322,8 +323,13 @@ struct TileDesc {
 };
 static_assert(sizeof(TileDesc) == 128, "tile record is 128 bytes");
 
+// workspace header: word 0 = status (MOE_WS_* error bits, sticky), word 1 = poll limit of the
+// few-token router (0: kPollLimitDefault; < 0: no polls)
+constexpr size_t kWsHeaderBytes = 256;
+constexpr int kPollLimitDefault = 1 << 20;
+
 struct WsLayout {
-    size_t slots, sink, logits, idx, w, offsets, sorted_pick, pick_pos, perm_blocks, tiles, ntiles, desc, xq, xs,
+    size_t hdr, slots, sink, logits, idx, w, offsets, sorted_pick, pick_pos, perm_blocks, tiles, ntiles, desc, xq, xs,
         hq, hs, o;
     size_t stage_table, stage_list, stage_n, stage_ranges;   // NVFP4 staging (moe_layer)
     size_t total;
@@ -343,14 +349,19 @@ hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t*
                        hipStream_t st);
 hipError_t launch_act_split(const moe_shape* s, const void* x, int rows, int K, int SS, int NT,
                             uint8_t* q, uint8_t* sc, hipStream_t st);
-// bcnt: per-block expert counts ([ceil(T * top_k / 1024)][n_experts] int32) or null (one workgroup)
+// bcnt: per-block expert counts ([ceil(T * top_k / 1024)][n_experts] int32) or null (one workgroup);
+// status: the workspace's status word (MOE_WS_BAD_EXPERT_ID) or null
 hipError_t launch_permute(const moe_shape* s, const int32_t* idx, int T, int32_t* offsets,
-                          int32_t* sorted_pick, int32_t* pick_pos, int32_t* bcnt, hipStream_t st);
+                          int32_t* sorted_pick, int32_t* pick_pos, int32_t* bcnt, uint32_t* status,
+                          hipStream_t st);
+// zero words [0, nwords) of a workspace, except word 1 := poll_limit
+hipError_t launch_ws_init(uint32_t* ws, size_t nwords, int32_t poll_limit, hipStream_t st);
 hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int tile_tokens, int32_t* tiles,
                        int32_t* ntiles, hipStream_t st);
 
 // fused few-token router (route + permute + plan + activation split); T <= 16, P <= 1024
 struct RouteSmallArgs {
+    uint32_t* hdr;            // workspace header: status word, poll limit
     const void* x;
     int T, d, E, k;
     const float* wr;

@@ -48,24 +48,40 @@ __device__ __forceinline__ int wave_peer_rank(int e, int lane, int* n) {
     return __popcll(peers & lt_mask);
 }
 
+// An expert id outside [0, E): -1 is a dropped pick (renorm_skip), anything else an error that
+// sets MOE_WS_BAD_EXPERT_ID in the status word (when there is one).  Either way the pick takes no
+// sorted position: pick_pos -1, and the positions past offsets[E] hold -1.
+__device__ __forceinline__ bool bad_expert_id(int e, int E) { return e < -1 || e >= E; }
+
+__device__ __forceinline__ void report_bad_ids(bool any_bad, uint32_t* status) {
+    if (any_bad && status) __hip_atomic_fetch_or(status, MOE_WS_BAD_EXPERT_ID, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One workgroup of 1024 threads.  LDS: counts and running cursors per expert, and per-wave
 // counts of the current chunk (for the stable rank across waves).
 __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restrict__ idx, int P, int E,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_pick,
-                                                          int32_t* __restrict__ pick_pos) {
+                                                          int32_t* __restrict__ pick_pos,
+                                                          uint32_t* __restrict__ status) {
     __shared__ int cnt[1024];
     __shared__ int run[1024];
     __shared__ int wcnt[kPermWaves][1024];
     __shared__ int scratch[kPermWaves];
+    __shared__ int s_bad;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     for (int e = tid; e < 1024; e += kPermThreads) cnt[e] = 0;
     for (int i = tid; i < kPermWaves * 1024; i += kPermThreads) (&wcnt[0][0])[i] = 0;
+    if (tid == 0) s_bad = 0;
     __syncthreads();
+    bool bad = false;
     for (int p = tid; p < P; p += kPermThreads) {
         int e = idx[p];
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+        bad |= bad_expert_id(e, E);
     }
+    if (bad) s_bad = 1;
     __syncthreads();
     int total;
     int excl = block_excl_scan(tid < E ? cnt[tid] : 0, scratch, &total);
@@ -73,12 +89,19 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
         offsets[tid] = excl;
         run[tid] = excl;
     }
-    if (tid == 0) offsets[E] = total;
+    if (tid == 0) {
+        offsets[E] = total;
+        report_bad_ids(s_bad != 0, status);
+    }
+    for (int i = total + tid; i < P; i += kPermThreads) sorted_pick[i] = -1;
     __syncthreads();
     for (int base = 0; base < P; base += kPermThreads) {
         const int p = base + tid;
         int e = (p < P) ? idx[p] : -1;
-        if (e >= E) e = -1;
+        if (e >= E || e < 0) {
+            if (p < P) pick_pos[p] = -1;
+            e = -1;
+        }
         int n;
         const int rank = wave_peer_rank(e, lane, &n);
         if (e >= 0 && rank == 0) wcnt[wv][e] = n;
@@ -104,22 +127,25 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
 // (3) each block places its picks at offset + block start + rank within the block, which is the
 // single-workgroup order (stable in pick order).  bcnt: [nblk][E] int32 in the workspace.
 __global__ __launch_bounds__(kPermThreads) void k_perm_count(const int32_t* __restrict__ idx, int P, int E,
-                                                             int32_t* __restrict__ bcnt) {
+                                                             int32_t* __restrict__ bcnt, uint32_t* __restrict__ status) {
     __shared__ int cnt[1024];
     const int tid = threadIdx.x;
     cnt[tid] = 0;
     __syncthreads();
     const int p = blockIdx.x * kPermThreads + tid;
+    bool bad = false;
     if (p < P) {
         const int e = idx[p];
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+        bad = bad_expert_id(e, E);
     }
-    __syncthreads();
+    report_bad_ids(__syncthreads_or(bad) && tid == 0, status);
     if (tid < E) bcnt[(size_t)blockIdx.x * E + tid] = cnt[tid];
 }
 
-__global__ __launch_bounds__(kPermThreads) void k_perm_scan(int nblk, int E, int32_t* __restrict__ bcnt,
-                                                            int32_t* __restrict__ offsets) {
+__global__ __launch_bounds__(kPermThreads) void k_perm_scan(int nblk, int E, int P, int32_t* __restrict__ bcnt,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ sorted_pick) {
     __shared__ int scratch[kPermWaves];
     const int e = threadIdx.x;
     int run = 0;
@@ -139,6 +165,7 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_scan(int nblk, int E, int
     const int excl = block_excl_scan(e < E ? run : 0, scratch, &total);
     if (e < E) offsets[e] = excl;
     if (e == 0) offsets[E] = total;
+    for (int i = total + e; i < P; i += kPermThreads) sorted_pick[i] = -1;   // positions of no pick
 }
 
 __global__ __launch_bounds__(kPermThreads) void k_perm_scatter(const int32_t* __restrict__ idx, int P, int E,
@@ -150,7 +177,10 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_scatter(const int32_t* __
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int p = blockIdx.x * kPermThreads + tid;
     int e = (p < P) ? idx[p] : -1;
-    if (e >= E) e = -1;
+    if (e >= E || e < 0) {
+        if (p < P) pick_pos[p] = -1;
+        e = -1;
+    }
     for (int i = tid; i < kPermWaves * 1024; i += kPermThreads) (&wcnt[0][0])[i] = 0;
     int n;
     const int rank = wave_peer_rank(e, lane, &n);
@@ -166,18 +196,19 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_scatter(const int32_t* __
 }
 
 hipError_t launch_permute(const moe_shape* s, const int32_t* idx, int T, int32_t* offsets,
-                          int32_t* sorted_pick, int32_t* pick_pos, int32_t* bcnt, hipStream_t st) {
+                          int32_t* sorted_pick, int32_t* pick_pos, int32_t* bcnt, uint32_t* status, hipStream_t st) {
     trace("permute", 0, st);
     const int P = T * s->top_k;
     const int nblk = (P + kPermThreads - 1) / kPermThreads;
     if (bcnt && nblk >= kPermMultiBlocks) {
-        MOE_LAUNCH(k_perm_count, dim3(nblk), dim3(kPermThreads), 0, st, idx, P, s->n_experts, bcnt);
-        MOE_LAUNCH(k_perm_scan, dim3(1), dim3(kPermThreads), 0, st, nblk, s->n_experts, bcnt, offsets);
+        MOE_LAUNCH(k_perm_count, dim3(nblk), dim3(kPermThreads), 0, st, idx, P, s->n_experts, bcnt, status);
+        MOE_LAUNCH(k_perm_scan, dim3(1), dim3(kPermThreads), 0, st, nblk, s->n_experts, P, bcnt, offsets,
+                   sorted_pick);
         MOE_LAUNCH(k_perm_scatter, dim3(nblk), dim3(kPermThreads), 0, st, idx, P, s->n_experts, bcnt, offsets,
                    sorted_pick, pick_pos);
     } else {
         MOE_LAUNCH(k_permute, dim3(1), dim3(kPermThreads), 0, st, idx, P, s->n_experts, offsets,
-                   sorted_pick, pick_pos);
+                   sorted_pick, pick_pos, status);
     }
     trace("permute", 1, st);
     return hipGetLastError();
@@ -202,6 +233,20 @@ __global__ __launch_bounds__(kPermThreads) void k_plan(const int32_t* __restrict
         tiles[2 * (first + j) + 1] = o0 + j * tt;
     }
     if (e == 0) *ntiles = total;
+}
+
+// workspace preparation: the header (status 0, poll limit) and the hand-over slots (0)
+__global__ __launch_bounds__(256) void k_ws_init(uint32_t* __restrict__ ws, size_t nwords, int32_t poll_limit) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nwords; i += (size_t)gridDim.x * 256)
+        ws[i] = i == 1 ? (uint32_t)poll_limit : 0u;
+}
+
+hipError_t launch_ws_init(uint32_t* ws, size_t nwords, int32_t poll_limit, hipStream_t st) {
+    trace("ws_init", 0, st);
+    const size_t blocks = (nwords + 255) / 256;
+    MOE_LAUNCH(k_ws_init, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, ws, nwords, poll_limit);
+    trace("ws_init", 1, st);
+    return hipGetLastError();
 }
 
 hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int tile_tokens, int32_t* tiles,

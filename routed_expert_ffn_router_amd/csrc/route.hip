@@ -478,7 +478,13 @@ hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t*
 // the wait is bounded all the same.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallT = 16;
-constexpr int kPollLimit = 1 << 20;       // polls of one token group (under a microsecond each)
+
+// Routing refused (the status word was already nonzero, or the wait for the logits gave up):
+// record a timeout in the status word (only if it was clean), and leave outputs that fail loudly
+// downstream - no tile, idx -1, w NaN (so y is NaN), positions 0 (in bounds for every reader).
+__device__ __forceinline__ void report_timeout(uint32_t* status) {
+    __hip_atomic_fetch_or(status, MOE_WS_ROUTE_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ void put_slot(unsigned long long* p, double v) {
     __hip_atomic_store(p, ~logit_key(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -580,15 +586,33 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[i] = src[i];
     };
-    // an empty record still names a real expert (the first pick's), so that a stray read of its
-    // pointers stays inside the weights
-    auto put_empty = [&](TileDesc* desc, int id) {
+    // an empty record still names a real expert (the first pick's, or expert 0), so that a stray
+    // read of its pointers stays inside the weights
+    auto put_empty = [&](TileDesc* desc, int id, int e) {
         TileDesc* D = desc + id;
-        put_expert(D, s_idx[0]);
+        put_expert(D, e);
         D->i0 = 0;
         D->ntok = 0;
-        D->e = s_idx[0];
+        D->e = e;
     };
+    // the outputs of a refused routing (see report_timeout), by all 256 threads
+    auto put_refused = [&](TileDesc* desc, int32_t* idx, float* wout, int32_t* pick_pos, int32_t* sorted_pick,
+                           int32_t* offsets, int32_t* ntiles) {
+        for (int p = tid; p < P; p += 256) {
+            idx[p] = -1;
+            wout[p] = __builtin_nan("");
+            pick_pos[p] = 0;
+            sorted_pick[p] = 0;
+        }
+        for (int e = tid; e <= E; e += 256) offsets[e] = 0;
+        for (int id = tid; id < a.max_tiles; id += 256) put_empty(desc, id, 0);
+        if (tid == 0) *ntiles = 0;
+    };
+    // status word and poll limit, written only by earlier launches
+    const uint32_t st0 = sload(&a.hdr[0]);
+    const int plim = (int)sload(&a.hdr[1]);
+    const int poll_limit = plim == 0 ? kPollLimitDefault : plim;     // < 0: no polls
+    __shared__ int s_fail[4];                                           // per wave: its wait gave up
 
     if (T == 1 && tab_lds) {
         // One token (the decode step).  The expert table is requested first.  While the row
@@ -619,6 +643,8 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             int32_t* const ntiles = live ? a.ntiles : (int32_t*)a.sink;
             unsigned long long* const slots = live ? a.slots : (unsigned long long*)a.sink;
             unsigned long long kv[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s) kv[s] = 0ull;
             if (live) {
                 tstore(0, tab0);
                 tstore(1, tab1);
@@ -628,16 +654,27 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             }
             if (wave == 0) {
                 if (live) {
-                    // poll the slots (lane l: experts l + 64 s) until none is zero
-                    for (int it = 0; it < kPollLimit; ++it) {
-                        bool miss = false;
+                    // poll the slots (lane l: experts l + 64 s) until none is zero, at most
+                    // poll_limit times; none at all on a workspace whose status is already set
+                    bool got = false;
+                    if (st0 == 0u) {
+                        for (int it = 0; it < poll_limit; ++it) {
+                            bool miss = false;
 #pragma unroll
-                        for (int s = 0; s < S; ++s) {
-                            const unsigned long long v = get_slot(a.slots + min(lane + 64 * s, E - 1));
-                            kv[s] = ~v;
-                            miss |= (lane + 64 * s < E) & (v == 0ull);
+                            for (int s = 0; s < S; ++s) {
+                                const unsigned long long v = get_slot(a.slots + min(lane + 64 * s, E - 1));
+                                kv[s] = ~v;
+                                miss |= (lane + 64 * s < E) & (v == 0ull);
+                            }
+                            if (__ballot(miss) == 0ull) {
+                                got = true;
+                                break;
+                            }
                         }
-                        if (__ballot(miss) == 0ull) break;
+                    }
+                    if (lane == 0) {
+                        s_fail[0] = got ? 0 : 1;
+                        if (!got && st0 == 0u) report_timeout(a.hdr);
                     }
                 } else {
                     // a branch of its own (the asm keeps it one), so that the warm-up pass does
@@ -645,12 +682,17 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                     asm volatile("" ::: "memory");
 #pragma unroll
                     for (int s = 0; s < S; ++s) kv[s] = dummy_key(lane + 64 * s);
+                    if (lane == 0) s_fail[0] = 0;
                 }
 #pragma unroll
                 for (int s = 0; s < S; ++s)
                     if (lane + 64 * s < E) s_key[lane + 64 * s] = kv[s];
             }
             lds_barrier();
+            if (s_fail[0]) {               // live pass only: nothing was routed
+                put_refused(desc, idx, wout, pick_pos, sorted_pick, offsets, ntiles);
+                return;
+            }
             if (wave == 0) {
                 unsigned long long my_key = 0ull;
                 if (k > 8 || !topk_pass<S>(kv, E, k, s_idx, s_cand[0], s_rk[0], my_key))
@@ -700,7 +742,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                     for (int q = 0; q < k; ++q) lower += s_idx[q] < e;
                     offsets[e] = lower;
                 }
-                for (int id = k + tid - 128; id < a.max_tiles; id += 128) put_empty(desc, id);
+                for (int id = k + tid - 128; id < a.max_tiles; id += 128) put_empty(desc, id, s_idx[0]);
                 if (tid == 128) *ntiles = k;
             }
             lds_barrier();      // the real pass rewrites what this one read from LDS
@@ -725,9 +767,11 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     // Every poll load is issued without a condition (indices past T or E re-read the last slot
     // and are not used), so that all of them are in flight together.
     constexpr int J = tab_lds ? kSmallT / 4 : 1;
-    for (int t0 = wave; t0 < T; t0 += 4 * J) {
+    bool gave_up = st0 != 0u;      // a workspace whose status is set is not routed on
+    for (int t0 = wave; t0 < T && !gave_up; t0 += 4 * J) {
         unsigned long long kv[J][S];
-        for (int it = 0; it < kPollLimit; ++it) {
+        bool got = false;
+        for (int it = 0; it < poll_limit; ++it) {
             bool miss = false;
 #pragma unroll
             for (int j = 0; j < J; ++j)
@@ -738,7 +782,15 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                     kv[j][s] = ~v;
                     miss |= (t < T) & (e < E) & (v == 0ull);
                 }
-            if (__ballot(miss) == 0ull) break;
+            if (__ballot(miss) == 0ull) {
+                got = true;
+                break;
+            }
+        }
+        if (!got) {
+            gave_up = true;
+            if (lane == 0) report_timeout(a.hdr);
+            break;
         }
 #pragma unroll
         for (int j = 0; j < J; ++j)
@@ -758,7 +810,12 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             }
         }
     }
+    if (lane == 0) s_fail[wave] = gave_up ? 1 : 0;
     __syncthreads();
+    if (s_fail[0] | s_fail[1] | s_fail[2] | s_fail[3]) {
+        put_refused(a.desc, a.idx, a.w, a.pick_pos, a.sorted_pick, a.offsets, a.ntiles);
+        return;
+    }
     // the expert offsets: the number of picks of lower experts
     auto put_offsets = [&]() {
         for (int e = tid; e <= E; e += 256) {
@@ -791,7 +848,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             a.sorted_pick[pos] = p;
         }
         put_offsets();
-        for (int id = k + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id);
+        for (int id = k + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id, s_idx[0]);
         if (tid == 0) *a.ntiles = k;
         return;
     }
@@ -849,7 +906,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     int nt = 0;
 #pragma unroll 8
     for (int q = 0; q < P; ++q) nt += s_start[q];
-    for (int id = nt + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id);
+    for (int id = nt + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id, s_idx[0]);
     if (tid == 0) *a.ntiles = nt;
 }
 

@@ -77,3 +77,51 @@ def oracle_layer(dl, x, idx_hint=None, residual=None, scaling=None):
 
 def small(name="tiny", **kw):
     return dataclasses.replace(synth.WORKLOADS[name], **kw)
+
+
+def covering_sample(idx, E, tile_picks, n_min=64, seed=0):
+    """Tokens whose picks, between them, fill every column slot of a tile of `tile_picks` picks,
+    land in every eighth of the tile list (the many-pick GEMM hands each of the 8 XCDs one
+    contiguous eighth), and include a pick of every ragged last tile, padded with further tokens
+    to at least n_min.  idx: [T, k] routing.  Pure bookkeeping of the tile plan (expert ranges in
+    sorted order, tiles of tile_picks consecutive positions), no arithmetic of the method."""
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    first = np.concatenate([[0], np.cumsum(counts)])[:-1]
+    tiles_per = (counts + tile_picks - 1) // tile_picks
+    tile0 = np.concatenate([[0], np.cumsum(tiles_per)])[:-1]
+    ntiles = int(tiles_per.sum())
+    tpx = (ntiles + 7) // 8
+    # sorted position of each pick: stable by (expert, pick id)
+    order = np.argsort(idx.reshape(-1), kind="stable")
+    pos = np.empty(T * k, dtype=np.int64)
+    pos[order] = np.arange(T * k)
+    e = idx.reshape(-1)
+    rel = pos - first[e]
+    slot = rel % tile_picks
+    tile = tile0[e] + rel // tile_picks
+    xcd = tile // tpx
+    ragged = (rel // tile_picks == tiles_per[e] - 1) & (counts[e] % tile_picks != 0)
+    need = {("slot", s) for s in range(tile_picks)} | {("xcd", x) for x in range(min(8, ntiles))}
+    rng = np.random.default_rng(seed)
+    chosen = []
+    for t in rng.permutation(T):
+        feats = set()
+        for p in range(t * k, t * k + k):
+            feats |= {("slot", int(slot[p])), ("xcd", int(xcd[p]))}
+        if feats & need:
+            chosen.append(int(t))
+            need -= feats
+        if not need:
+            break
+    assert not need, f"no tokens cover {sorted(need)[:4]}"
+    for t in [int(p // k) for p in np.flatnonzero(ragged)[:8]]:
+        if t not in chosen:
+            chosen.append(t)
+    for t in rng.permutation(T):
+        if len(chosen) >= n_min:
+            break
+        if int(t) not in chosen:
+            chosen.append(int(t))
+    return sorted(chosen)

@@ -25,7 +25,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert m.abi_version() == 1
+    assert m.abi_version() == 2
     for s in range(5):
         assert m.status_string(s)
     assert m.status_string(99) == "unknown status"
@@ -61,6 +61,15 @@ def test_validation_codes():
     assert _route(good, x=FAKE + 4) == m.MOE_ERR_INVALID                     # misaligned
     assert _route(good, ws_bytes=16) == m.MOE_ERR_WORKSPACE
     assert m.library().moe_route(None, FAKE, 1, FAKE, None, FAKE, FAKE, FAKE, 1 << 40, 0) == m.MOE_ERR_INVALID
+    # the optional parts of the layer: renorm_skip in [0, 1), n_shared 0 or 1, act_quant an enum
+    # (MXFP8 activations only with MXFP4 weights)
+    assert _route(m.make_shape(256, 128, 16, 2, renorm_skip=-0.1)) == m.MOE_ERR_INVALID
+    assert _route(m.make_shape(256, 128, 16, 2, renorm_skip=1.0)) == m.MOE_ERR_INVALID
+    assert _route(m.make_shape(256, 128, 16, 2, renorm_skip=float("nan"))) == m.MOE_ERR_INVALID
+    assert _route(m.make_shape(256, 128, 16, 2, n_shared=2)) == m.MOE_ERR_INVALID
+    assert _route(m.make_shape(256, 128, 16, 2, n_shared=-1)) == m.MOE_ERR_INVALID
+    assert _route(m.make_shape(256, 128, 16, 2, act_quant=2)) == m.MOE_ERR_INVALID
+    assert _route(m.make_shape(256, 128, 16, 2, 1, 0, act_quant=m.MOE_AQ_MXFP8)) == m.MOE_ERR_UNSUPPORTED
 
 
 def test_validation_other_entry_points():
@@ -87,3 +96,25 @@ def test_validation_other_entry_points():
     assert L.moe_gather_experts(b(sh), FAKE, FAKE, 0, None, None, 0) == m.MOE_OK
     assert L.moe_fill_table(b(sh), FAKE, 100, FAKE, 0) == m.MOE_ERR_INVALID   # stride too small
     assert m.moe_workspace_bytes(m.make_shape(256, 128, 16, 17), 4) == 0
+    # workspace preparation: a null or misaligned workspace, or one too small for (shape, T)
+    assert L.moe_workspace_init(b(sh), 4, None, 1 << 40, 0, 0) == m.MOE_ERR_INVALID
+    assert L.moe_workspace_init(b(sh), 4, FAKE + 16, 1 << 40, 0, 0) == m.MOE_ERR_INVALID
+    assert L.moe_workspace_init(b(sh), 4, FAKE, 16, 0, 0) == m.MOE_ERR_WORKSPACE
+    assert L.moe_workspace_init(b(sh), -1, FAKE, 1 << 40, 0, 0) == m.MOE_ERR_INVALID
+    # moe_permute's workspace, when given, must be 256-byte aligned like every other
+    assert L.moe_permute(b(sh), FAKE, 4, FAKE, FAKE, FAKE, FAKE + 16, 1 << 40, 0) == m.MOE_ERR_INVALID
+    # the observed layer validates exactly as moe_layer does
+    obs = m.make_observer()
+    assert L.moe_layer_observed(b(sh), FAKE, 4, FAKE, None, FAKE, None, None, FAKE, None, None, FAKE, 1 << 40, 0,
+                                ctypes.byref(obs)) == m.MOE_ERR_INVALID      # y aliases x
+    assert L.moe_layer_observed(b(sh), None, 0, None, None, None, None, None, None, None, None, None, 0, 0,
+                                None) == m.MOE_OK                           # T = 0 is a no-op
+
+
+def test_workspace_header_is_first_and_fixed():
+    """The status word sits at offset 0 and the hand-over slots right after the header, at the same
+    place for every T, so one workspace serves calls of every token count up to its own."""
+    sh = m.make_shape(4096, 2048, 288, 8)
+    sizes = [m.moe_workspace_bytes(sh, T) for T in (1, 16, 17, 64, 4096)]
+    assert sizes == sorted(sizes) and sizes[0] > 256 + 8 * 16 * 288
+    assert m.MOE_WS_STATUS_OFFSET == 0

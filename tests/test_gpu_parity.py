@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DeviceLayer, oracle_layer, rel_l2, run_layer, small, tol
+from gpu_util import DeviceLayer, covering_sample, oracle_layer, rel_l2, run_layer, small, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -313,7 +313,9 @@ def test_glm_decode_zero_token(glm_layer):
 
 
 def test_glm_prefill_chunk_sampled(glm_layer):
-    """T=4096 chunk: routing bit-exact on every token; output checked on 6 sampled tokens."""
+    """T=4096 chunk, the bench's prefill leg: routing bit-exact on every token; the output checked on
+    at least 64 tokens chosen so that their picks fill every column slot of a 64-pick tile, fall in
+    every eighth of the tile list (one per XCD) and include ragged last tiles."""
     dl = glm_layer
     wl = dl.wl
     T = 4096
@@ -324,7 +326,8 @@ def test_glm_prefill_chunk_sampled(glm_layer):
     np.testing.assert_array_equal(idx.cpu().numpy(), oidx)
     counts = np.bincount(oidx.reshape(-1), minlength=wl.n_experts)
     assert counts.min() > 0        # nearly every expert active at this chunk size
-    sample = [0, 1, 777, 2048, 4000, 4095]
+    sample = covering_sample(oidx, wl.n_experts, 64, n_min=64)
+    print(f"  {len(sample)} sampled tokens", flush=True)
     xs = x[sample].contiguous()
     oy, _, _, _ = oracle_layer(dl, xs, idx_hint=oidx[sample])
     err = rel_l2(y[sample].float().cpu().numpy(), oy)

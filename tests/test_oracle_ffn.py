@@ -254,3 +254,58 @@ def test_negative_wrong_block_axis():
         for j in range(TINY.top_k):
             y_bad[t] += w[t, j] * ffn_wrong_axis(blobs[idx[t, j]], x64[t])
     _assert_caught(y_bad, y, "wrong block axis")
+
+
+# -------------------------------------------------------------------------------------------
+# the weighted combine at non-uniform weights: which weight goes with which pick
+# -------------------------------------------------------------------------------------------
+
+def test_combine_pairs_each_weight_with_its_pick():
+    """Identity router: token 0's logits are the golden case 1 3 0.5 2 (tests/golden/router_cases.txt:
+    k=2 picks experts 1 and 3 with weights 0.5195751544086155 and 0.48042484559138454).  The layer
+    output must be w0 * FFN_1(x) + w1 * FFN_3(x), each FFN a numpy matmul on weights decoded by
+    tests/indep.py; the same sum with the two weights swapped (a mis-paired combine) must miss the
+    oracle by far more than the fp32 tolerance."""
+    from golden_io import router_cases
+    logits, k, ids, ws = router_cases()[0]
+    wl = dataclasses.replace(TINY, n_experts=4, top_k=k, tokens=1)
+    lay = synth.make_layer(wl, 0, 7, "cpu")
+    blobs = [lay["blob"][e].numpy() for e in range(wl.n_experts)]
+    x = synth.make_x(wl, 7, "cpu").double().numpy()
+    x[0, :4] = logits                                        # exact in fp32 and fp64
+    x64 = np.ascontiguousarray(x)
+    wr = np.zeros((wl.n_experts, wl.d_model), dtype=np.float32)
+    wr[np.arange(4), np.arange(4)] = 1.0                     # logit e = x[e]
+    y, idx, w, _ = _layer(wl, x64, wr, None, blobs)
+    assert idx[0].tolist() == ids
+    np.testing.assert_allclose(w[0], ws, rtol=0, atol=4e-16)
+    f1 = _dense_ffn(blobs[ids[0]], x64[0], wl)
+    f3 = _dense_ffn(blobs[ids[1]], x64[0], wl)
+    want = ws[0] * f1 + ws[1] * f3
+    np.testing.assert_allclose(y[0], want, rtol=1e-12, atol=1e-14 * np.abs(want).max())
+    swapped = ws[1] * f1 + ws[0] * f3
+    _assert_caught(swapped, y[0], "weights swapped between picks")
+
+
+def test_combine_matches_numpy_sum_biased_router():
+    """k=3 of 16 with a logit bias that spreads the weights (non-uniform), routed_scaling 2.5 and a
+    residual: y[t] = 2.5 * sum_j w[t,j] * FFN_{idx[t,j]}(x[t]) + residual[t], with w recomputed in
+    numpy from numpy's own logits (sigmoid of the picks over their sum) and each FFN a numpy
+    matmul on independently decoded weights."""
+    wl = dataclasses.replace(TINY, top_k=3, tokens=6)
+    x64, wr, _, blobs = _inputs(wl, seed=11)
+    bias = np.float32(1.0) - np.float32(1.2) * (wl.n_experts - 1 - np.arange(wl.n_experts, dtype=np.float32))
+    res = np.ascontiguousarray(np.linspace(-1, 1, wl.tokens * wl.d_model).reshape(wl.tokens, wl.d_model))
+    y, idx, w, _ = _layer(wl, x64, wr, bias, blobs, scaling=2.5, residual=res)
+    l_np = x64 @ wr.astype(np.float64).T + bias.astype(np.float64)
+    sel = np.take_along_axis(l_np, idx.astype(np.int64), axis=1)
+    sig = 1.0 / (1.0 + np.exp(-sel))
+    w_np = sig / sig.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(w, w_np, rtol=1e-13)
+    assert (w.max(axis=1) - w.min(axis=1)).min() > 0.2       # the weights really differ
+    for t in range(wl.tokens):
+        ffns = [_dense_ffn(blobs[e], x64[t], wl) for e in idx[t]]
+        want = 2.5 * sum(w_np[t, j] * ffns[j] for j in range(wl.top_k)) + res[t]
+        np.testing.assert_allclose(y[t], want, rtol=1e-11, atol=1e-13 * np.abs(want).max())
+        rev = 2.5 * sum(w_np[t, wl.top_k - 1 - j] * ffns[j] for j in range(wl.top_k)) + res[t]
+        _assert_caught(rev - res[t], y[t] - res[t], "weights paired in reverse rank order")
