@@ -275,6 +275,21 @@ moe_status moe_layer_observed(const moe_shape *shape, const void *x, int32_t T, 
                               const void *residual, void *y, int32_t *topk_idx_out, float *topk_w_out,
                               void *ws, size_t ws_bytes, hipStream_t stream, const moe_observer *observer);
 
+/* moe_layer for callers that cannot allocate device memory - code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc - with the same arguments minus the staging buffer
+ * and the workspace.  Its intermediates live in a scratch array inside the library: 32 MiB of
+ * device memory per GPU the library runs on, held until the process ends.  Shapes and token counts
+ * whose moe_workspace_bytes-style layout needs more (at d_model 4096, d_ff 2048, 288 experts: more
+ * than 64 tokens) return MOE_ERR_WORKSPACE.  The call allocates nothing: no hipMalloc, no hipFree,
+ * no allocating library routine; its first call on a device clears the array's status word and
+ * hand-over slots with a fill kernel on `stream`.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU race (run them on one stream, or serialise them).  The
+ * array's status word cannot be read by the caller; a router timeout shows as idx -1 and NaN y,
+ * and the array then refuses to route for the rest of the process. */
+moe_status moe_layer_noalloc(const moe_shape *shape, const void *x, int32_t T, const float *w_router,
+                             const float *logit_bias, const moe_expert *d_table, const void *residual,
+                             void *y, int32_t *topk_idx_out, float *topk_w_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

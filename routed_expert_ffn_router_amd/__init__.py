@@ -83,6 +83,7 @@ _SIGS = {
     "moe_layer": (ctypes.c_int, [_SP, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
     "moe_layer_observed": (ctypes.c_int, [_SP, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P,
                                           ctypes.POINTER(moe_observer)]),
+    "moe_layer_noalloc": (ctypes.c_int, [_SP, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -245,3 +246,11 @@ def moe_layer(shape, x, T: int, w_router, logit_bias, d_table, staging, residual
         _check("moe_layer", _lib.moe_layer(*args))
     else:
         _check("moe_layer_observed", _lib.moe_layer_observed(*args, ctypes.byref(observer)))
+
+
+def moe_layer_noalloc(shape, x, T: int, w_router, logit_bias, d_table, residual, y, topk_idx_out=None,
+                      topk_w_out=None, stream=None):
+    """moe_layer with the library's own per-GPU scratch array instead of a workspace (no allocation)."""
+    _check("moe_layer_noalloc", _lib.moe_layer_noalloc(ctypes.byref(shape), _ptr(x), T, _ptr(w_router),
+                                                       _ptr(logit_bias), _ptr(d_table), _ptr(residual), _ptr(y),
+                                                       _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream)))

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -38,7 +40,7 @@ static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int act_terms(const moe_shape* s) { return s->act_dtype == MOE_DT_BF16 ? 2 : 4; }
 
-WsLayout ws_layout(const moe_shape* s, int32_t T) {
+WsLayout ws_layout(const moe_shape* s, int32_t T, bool slots_for_any_shape) {
     WsLayout L;
     memset(&L, 0, sizeof L);
     const size_t E = s->n_experts, k = s->top_k, d = s->d_model, f = s->d_ff;
@@ -57,7 +59,7 @@ WsLayout ws_layout(const moe_shape* s, int32_t T) {
     // hand-over: the same bytes in the layout of every T, used by nothing else, so that calls with
     // different T on one workspace keep them
     L.hdr = take(kWsHeaderBytes);
-    L.slots = take(8 * (size_t)kSmallTokens * E);
+    L.slots = take(8 * (size_t)kSmallTokens * (slots_for_any_shape ? (size_t)kMaxExperts : E));
     // write-only scratch of the one-token router's warm-up pass
     const size_t sink_rec = sizeof(TileDesc) * (size_t)L.max_tiles, sink_slots = 8 * (E + 1);
     L.sink = take(sink_rec > sink_slots ? sink_rec : sink_slots);
@@ -222,6 +224,57 @@ static moe_status run_ffn(const moe_shape* s, const moe_expert* table, const voi
 
 }  // namespace moe
 
+namespace moe {
+
+// ---------------------------------------------------------------------------------------------
+// moe_layer_noalloc's scratch: a device array of the library, one copy per GPU, for callers that
+// cannot allocate.  Host code never passes the array's name to a kernel or a copy (in host code it
+// is a stand-in, not a device address): each device's address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and the kernels receive that address.
+// ---------------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+static std::mutex g_scratch_mu;
+static uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's scratch address; the first call on a device also clears the array's status
+// word and logit hand-over slots (a fill kernel on `st`, ahead of the layer's kernels)
+static moe_status device_scratch(hipStream_t st, uint8_t** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        const size_t end = kWsHeaderBytes + 8 * (size_t)kSmallTokens * kMaxExperts;   // header + slots
+        static_assert(kWsHeaderBytes + 8 * (size_t)kSmallTokens * kMaxExperts <= kScratchBytes, "slots fit");
+        if (launch_ws_init((uint32_t*)p, end / 4, 0, st) != hipSuccess) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = (uint8_t*)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+static moe_status check_layer_args(const moe_shape* s, const void* x, const float* w_router,
+                                   const moe_expert* d_table, const void* staging, const void* residual,
+                                   const void* y) {
+    if (!x || !w_router || !d_table || !y) return MOE_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w_router, 16) || (residual && !aligned(residual, 16)) ||
+        (staging && !aligned(staging, 16)))
+        return MOE_ERR_INVALID;
+    if (x == y) return MOE_ERR_INVALID;
+    if (staging && s->wformat != MOE_WF_NVFP4) return MOE_ERR_INVALID;      // staging is the NVFP4 gather path
+    return MOE_OK;
+}
+
+static moe_status layer_launches(const moe_shape* s, const void* x, int32_t T, const float* w_router,
+                                 const float* logit_bias, const moe_expert* d_table, void* staging,
+                                 const void* residual, void* y, int32_t* topk_idx_out, float* topk_w_out,
+                                 uint8_t* w8, const WsLayout& L, hipStream_t stream);
+
+}  // namespace moe
+
 using namespace moe;
 
 extern "C" {
@@ -359,16 +412,42 @@ moe_status moe_layer_observed(const moe_shape* s, const void* x, int32_t T, cons
     MOE_TRY(check_shape(s));
     MOE_TRY(check_T(s, T));
     if (T == 0) return MOE_OK;
-    if (!x || !w_router || !d_table || !y || !ws) return MOE_ERR_INVALID;
-    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w_router, 16) || !aligned(ws, 256) ||
-        (residual && !aligned(residual, 16)) || (staging && !aligned(staging, 16)))
-        return MOE_ERR_INVALID;
-    if (x == y) return MOE_ERR_INVALID;
-    const bool nv = s->wformat == MOE_WF_NVFP4;
-    if (staging && !nv) return MOE_ERR_INVALID;      // staging is the NVFP4 gather path
+    if (!ws) return MOE_ERR_INVALID;
+    MOE_TRY(check_layer_args(s, x, w_router, d_table, staging, residual, y));
+    if (!aligned(ws, 256)) return MOE_ERR_INVALID;
     const WsLayout L = ws_layout(s, T);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-    uint8_t* w8 = (uint8_t*)ws;
+    return layer_launches(s, x, T, w_router, logit_bias, d_table, staging, residual, y, topk_idx_out, topk_w_out,
+                          (uint8_t*)ws, L, stream);
+}
+
+moe_status moe_layer_noalloc(const moe_shape* s, const void* x, int32_t T, const float* w_router,
+                             const float* logit_bias, const moe_expert* d_table, const void* residual, void* y,
+                             int32_t* topk_idx_out, float* topk_w_out, hipStream_t stream) {
+    MOE_TRY(check_shape(s));
+    MOE_TRY(check_T(s, T));
+    if (T == 0) return MOE_OK;
+    MOE_TRY(check_layer_args(s, x, w_router, d_table, nullptr, residual, y));
+    // every shape lays out the array with hand-over slots for the largest expert count, so that
+    // calls of different shapes never find another region's bytes in their slots
+    const WsLayout L = ws_layout(s, T, /*slots_for_any_shape=*/true);
+    if (L.total > kScratchBytes) return MOE_ERR_WORKSPACE;     // beyond the library's scratch array
+    uint8_t* ws = nullptr;
+    MOE_TRY(device_scratch(stream, &ws));
+    return layer_launches(s, x, T, w_router, logit_bias, d_table, nullptr, residual, y, topk_idx_out, topk_w_out, ws,
+                          L, stream);
+}
+
+}  // extern "C"
+
+namespace moe {
+
+// moe_layer's launch sequence on a validated, large enough workspace
+static moe_status layer_launches(const moe_shape* s, const void* x, int32_t T, const float* w_router,
+                                 const float* logit_bias, const moe_expert* d_table, void* staging,
+                                 const void* residual, void* y, int32_t* topk_idx_out, float* topk_w_out,
+                                 uint8_t* w8, const WsLayout& L, hipStream_t stream) {
+    const bool nv = s->wformat == MOE_WF_NVFP4;
     int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)(w8 + L.idx);
     float* w = topk_w_out ? topk_w_out : (float*)(w8 + L.w);
     double* logits = (double*)(w8 + L.logits);
@@ -446,4 +525,4 @@ moe_status moe_layer_observed(const moe_shape* s, const void* x, int32_t T, cons
     return MOE_OK;
 }
 
-}  // extern "C"
+}  // namespace moe

@@ -326,6 +326,7 @@ static_assert(sizeof(TileDesc) == 128, "tile record is 128 bytes");
 // workspace header: word 0 = status (MOE_WS_* error bits, sticky), word 1 = poll limit of the
 // few-token router (0: kPollLimitDefault; < 0: no polls)
 constexpr size_t kWsHeaderBytes = 256;
+constexpr int kMaxExperts = 1024;
 constexpr int kPollLimitDefault = 1 << 20;
 
 struct WsLayout {
@@ -341,7 +342,8 @@ int act_terms(const moe_shape* s);
 int logits_splits(const moe_shape* s, int T);   // K slices of the tiled router (1 for T <= 8)
 int super_step(int K, int ksplit);
 int act_super_step(int K, int variant);
-WsLayout ws_layout(const moe_shape* s, int32_t T);
+// slots_for_any_shape: hand-over slots sized for kMaxExperts (a workspace shared by every shape)
+WsLayout ws_layout(const moe_shape* s, int32_t T, bool slots_for_any_shape = false);
 
 hipError_t launch_router_logits(const moe_shape* s, const void* x, int T, const float* wr,
                                 const float* bias, double* logits, hipStream_t st);
