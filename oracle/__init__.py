@@ -59,7 +59,7 @@ def lib():
         L.oracle_dequant.restype = i32
         L.oracle_dequant.argtypes = [P, P, dbl, i64, i64, i32, P]
         L.oracle_route.restype = i32
-        L.oracle_route.argtypes = [P, i32, i32, P, P, i32, i32, P, P, P]
+        L.oracle_route.argtypes = [P, i32, i32, P, P, i32, i32, dbl, P, P, P]
         L.oracle_permute.restype = i32
         L.oracle_permute.argtypes = [P, i32, i32, i32, P, P, P]
         L.oracle_expert_ffn.restype = i32
@@ -67,7 +67,7 @@ def lib():
         L.oracle_combine.restype = i32
         L.oracle_combine.argtypes = [P, P, P, i32, i32, i32, dbl, P, P]
         L.oracle_layer.restype = i32
-        L.oracle_layer.argtypes = [P, i32, i32, i32, i32, i32, i32, dbl, P, P, P, P, P, P, P, P]
+        L.oracle_layer.argtypes = [P, i32, i32, i32, i32, i32, i32, dbl, dbl, P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -77,6 +77,11 @@ def _p(a: Optional[np.ndarray]):
         return None
     assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(v: float) -> float:
+    """A parameter as the fp32 value the C ABI carries, widened exactly to fp64."""
+    return float(np.float32(v))
 
 
 def _check(rc: int, what: str):
@@ -137,8 +142,9 @@ def dequant(q: np.ndarray, s: np.ndarray, rows: int, K: int, wformat: int, ts: f
 # ---------------------------------------------------------------------------------------------
 
 
-def route(x64: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], k: int):
-    """Returns (logits [T,E] f64, idx [T,k] i32, w [T,k] f64)."""
+def route(x64: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], k: int, renorm_skip: float = 0.0):
+    """Returns (logits [T,E] f64, idx [T,k] i32, w [T,k] f64); with renorm_skip, dropped picks have
+    idx -1 and w 0.  renorm_skip is taken as the fp32 value the C ABI's moe_shape carries."""
     T, d = x64.shape
     E = w_router.shape[0]
     wr = np.ascontiguousarray(w_router, dtype=np.float32)
@@ -146,7 +152,8 @@ def route(x64: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], k: 
     logits = np.empty((T, E), dtype=np.float64)
     idx = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float64)
-    _check(lib().oracle_route(_p(x64), T, d, _p(wr), _p(b), E, k, _p(logits), _p(idx), _p(w)), "route")
+    _check(lib().oracle_route(_p(x64), T, d, _p(wr), _p(b), E, k, _f32(renorm_skip), _p(logits), _p(idx), _p(w)),
+           "route")
     return logits, idx, w
 
 
@@ -194,7 +201,8 @@ def combine(o: np.ndarray, w: np.ndarray, pick_pos: np.ndarray, scaling: float =
 
 
 def layer(x64: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], blobs, d: int, f: int,
-          k: int, wformat: int, scaling: float = 1.0, residual: Optional[np.ndarray] = None):
+          k: int, wformat: int, scaling: float = 1.0, residual: Optional[np.ndarray] = None,
+          renorm_skip: float = 0.0):
     """Whole layer.  Returns (y [T,d] f64, idx [T,k] i32, w [T,k] f64, logits [T,E] f64)."""
     T = x64.shape[0]
     E = len(blobs)
@@ -205,7 +213,7 @@ def layer(x64: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], blo
     wr = np.ascontiguousarray(w_router, dtype=np.float32)
     b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     ptrs = _blob_ptrs(blobs)
-    _check(lib().oracle_layer(_p(x64), T, d, f, E, k, wformat, scaling, _p(wr), _p(b),
+    _check(lib().oracle_layer(_p(x64), T, d, f, E, k, wformat, scaling, _f32(renorm_skip), _p(wr), _p(b),
                               ctypes.cast(ptrs, ctypes.c_void_p), _p(residual), _p(y), _p(idx), _p(w),
                               _p(logits)), "layer")
     return y, idx, w, logits

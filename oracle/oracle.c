@@ -162,9 +162,15 @@ static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 /* x: [T][d] fp64 (the layer input, converted exactly); w_router: [E][d] fp32;
  * bias: [E] fp32 or NULL, added to the logit before selection.
  * Outputs: logits [T][E] (may be NULL), idx [T][k] in rank order, w [T][k] with
- * w = sigmoid(l_sel) / sum sigmoid(l_sel).  Returns 0, or -1 on bad sizes. */
+ * w = sigmoid(l_sel) / sum sigmoid(l_sel).
+ * renorm_skip (Strata-GLM blog, "Uncensoring without touching the weights": an expert skipped
+ * for its tiny routing weight is dropped cleanly and the remaining weights are renormalised):
+ * 0 leaves the picks as they are.  Otherwise every pick after the first whose weight above is
+ * below renorm_skip is dropped - idx -1, w 0 - and each kept pick's weight becomes
+ * sigmoid(l) / (sum of sigmoid(l) over the kept picks, in rank order).
+ * Returns 0, or -1 on bad sizes. */
 int oracle_route(const double *x, int T, int d, const float *w_router, const float *bias,
-                 int E, int k, double *logits, int32_t *idx, double *w) {
+                 int E, int k, double renorm_skip, double *logits, int32_t *idx, double *w) {
     if (T < 0 || d <= 0 || E <= 0 || k < 1 || k > E) return -1;
     #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
@@ -191,6 +197,18 @@ int oracle_route(const double *x, int T, int d, const float *w_router, const flo
         }
         for (int j = 0; j < k; ++j)
             w[(int64_t)t * k + j] = sigmoid(l[idx[(int64_t)t * k + j]]) / ssum;
+        if (renorm_skip > 0.0) {
+            double kept = 0.0;
+            for (int j = 0; j < k; ++j) {
+                int64_t p = (int64_t)t * k + j;
+                if (j > 0 && w[p] < renorm_skip) idx[p] = -1;
+                else kept += sigmoid(l[idx[p]]);
+            }
+            for (int j = 0; j < k; ++j) {
+                int64_t p = (int64_t)t * k + j;
+                w[p] = idx[p] < 0 ? 0.0 : sigmoid(l[idx[p]]) / kept;
+            }
+        }
         free(l);
         free(taken);
     }
@@ -199,6 +217,8 @@ int oracle_route(const double *x, int T, int d, const float *w_router, const flo
 
 /* ---------------------------------------------------------------------------------------- */
 /* permute: counting sort of the picks by expert, stable in pick order (p = t*k + j)         */
+/* A dropped pick (expert id -1) takes no position: pick_pos -1; sorted positions past the   */
+/* last kept pick hold -1.  Any other id outside [0, E) is an error (-1).                    */
 /* ---------------------------------------------------------------------------------------- */
 
 int oracle_permute(const int32_t *idx, int T, int k, int E, int32_t *offsets,
@@ -207,12 +227,18 @@ int oracle_permute(const int32_t *idx, int T, int k, int E, int32_t *offsets,
     int32_t *cursor = (int32_t *)calloc((size_t)E + 1, sizeof(int32_t));
     for (int e = 0; e <= E; ++e) offsets[e] = 0;
     for (int64_t p = 0; p < P; ++p) {
+        if (idx[p] == -1) continue;
         if (idx[p] < 0 || idx[p] >= E) { free(cursor); return -1; }
         offsets[idx[p] + 1] += 1;
     }
     for (int e = 0; e < E; ++e) offsets[e + 1] += offsets[e];
+    for (int64_t i = offsets[E]; i < P; ++i) sorted_pick[i] = -1;
     for (int64_t p = 0; p < P; ++p) {
         int e = idx[p];
+        if (e == -1) {
+            pick_pos[p] = -1;
+            continue;
+        }
         int32_t pos = offsets[e] + cursor[e]++;
         sorted_pick[pos] = (int32_t)p;
         pick_pos[p] = pos;
@@ -274,7 +300,8 @@ int oracle_expert_ffn(const uint8_t *const *blobs, int d, int f, int E, int wfor
 }
 
 /* ---------------------------------------------------------------------------------------- */
-/* combine: y[t] = scaling * sum_j w[t,j] * o[pick_pos[t*k+j]] (+ residual[t])              */
+/* combine: y[t] = scaling * sum_j w[t,j] * o[pick_pos[t*k+j]] (+ residual[t]), dropped     */
+/* picks (pick_pos -1) left out                                                              */
 /* ---------------------------------------------------------------------------------------- */
 
 int oracle_combine(const double *o, const double *w, const int32_t *pick_pos, int T, int k,
@@ -284,8 +311,11 @@ int oracle_combine(const double *o, const double *w, const int32_t *pick_pos, in
     for (int t = 0; t < T; ++t) {
         for (int c = 0; c < d; ++c) {
             double acc = 0.0;
-            for (int j = 0; j < k; ++j)
-                acc += w[(int64_t)t * k + j] * o[(int64_t)pick_pos[(int64_t)t * k + j] * d + c];
+            for (int j = 0; j < k; ++j) {
+                int32_t pos = pick_pos[(int64_t)t * k + j];
+                if (pos < 0) continue;                  /* a dropped pick */
+                acc += w[(int64_t)t * k + j] * o[(int64_t)pos * d + c];
+            }
             acc *= scaling;
             if (residual) acc += residual[(int64_t)t * d + c];
             y[(int64_t)t * d + c] = acc;
@@ -299,7 +329,7 @@ int oracle_combine(const double *o, const double *w, const int32_t *pick_pos, in
 /* ---------------------------------------------------------------------------------------- */
 
 int oracle_layer(const double *x, int T, int d, int f, int E, int k, int wformat,
-                 double scaling, const float *w_router, const float *bias,
+                 double scaling, double renorm_skip, const float *w_router, const float *bias,
                  const uint8_t *const *blobs, const double *residual, double *y,
                  int32_t *idx_out, double *w_out, double *logits_out) {
     if (T == 0) return 0;
@@ -310,7 +340,7 @@ int oracle_layer(const double *x, int T, int d, int f, int E, int k, int wformat
     int32_t *sorted_pick = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
     int32_t *pick_pos = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
     double *o = (double *)malloc(sizeof(double) * (size_t)P * d);
-    int rc = oracle_route(x, T, d, w_router, bias, E, k, logits_out, idx, w);
+    int rc = oracle_route(x, T, d, w_router, bias, E, k, renorm_skip, logits_out, idx, w);
     if (rc == 0) rc = oracle_permute(idx, T, k, E, offsets, sorted_pick, pick_pos);
     if (rc == 0) rc = oracle_expert_ffn(blobs, d, f, E, wformat, x, T, k, offsets, sorted_pick, o);
     if (rc == 0) rc = oracle_combine(o, w, pick_pos, T, k, d, scaling, residual, y);

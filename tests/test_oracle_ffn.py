@@ -309,3 +309,28 @@ def test_combine_matches_numpy_sum_biased_router():
         np.testing.assert_allclose(y[t], want, rtol=1e-11, atol=1e-13 * np.abs(want).max())
         rev = 2.5 * sum(w_np[t, wl.top_k - 1 - j] * ffns[j] for j in range(wl.top_k)) + res[t]
         _assert_caught(rev - res[t], y[t] - res[t], "weights paired in reverse rank order")
+
+
+def test_renorm_skip_layer_matches_numpy_and_catches_missing_renormalisation():
+    """With renorm-skip, y[t] = sum over the kept picks of w_kept * FFN(x[t]) (numpy, weights
+    recomputed from numpy's logits: the sigmoids of the kept picks over their sum); keeping the
+    unrenormalised weights instead is a planted mistake the tolerance must catch."""
+    wl = dataclasses.replace(TINY, top_k=4, tokens=6)
+    x64, wr, _, blobs = _inputs(wl, seed=5)
+    bias = np.float32(1.0) - np.float32(1.2) * (wl.n_experts - 1 - np.arange(wl.n_experts, dtype=np.float32))
+    tau = 0.2
+    y, idx, w, _ = oracle.layer(x64, wr, bias, blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat,
+                                renorm_skip=tau)
+    _, idx0, w0, _ = oracle.layer(x64, wr, bias, blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat)
+    assert (idx < 0).any(), "the bias makes some picks light enough to drop"
+    l_np = x64 @ wr.astype(np.float64).T + bias.astype(np.float64)
+    y_bad = np.zeros_like(y)
+    for t in range(wl.tokens):
+        kept = [j for j in range(wl.top_k) if idx[t, j] >= 0]
+        assert idx[t, kept].tolist() == idx0[t, kept].tolist()
+        sig = np.array([1.0 / (1.0 + np.exp(-l_np[t, idx[t, j]])) for j in kept])
+        ffns = [_dense_ffn(blobs[idx[t, j]], x64[t], wl) for j in kept]
+        want = sum((sig[i] / sig.sum()) * ffns[i] for i in range(len(kept)))
+        np.testing.assert_allclose(y[t], want, rtol=1e-11, atol=1e-13 * np.abs(want).max())
+        y_bad[t] = sum(w0[t, j] * ffns[i] for i, j in enumerate(kept))
+    _assert_caught(y_bad, y, "kept weights not renormalised")

@@ -136,3 +136,71 @@ def test_permute_matches_stable_sort(T, k, E):
 def test_permute_rejects_out_of_range():
     with pytest.raises(ValueError):
         oracle.permute(np.array([[0, 16]], dtype=np.int32), 16)
+
+
+def test_permute_dropped_picks_take_no_position():
+    """Expert id -1 (a pick dropped by renorm-skip) takes no position; the others are sorted
+    exactly as Python's stable sort sorts them without it; the positions past the last kept pick
+    hold -1; any other negative id is still refused."""
+    idx = np.array([[3, -1], [0, 3], [-1, 1], [2, 0]], dtype=np.int32)
+    offsets, sp, pp = oracle.permute(idx, 4)
+    flat = idx.reshape(-1)
+    kept = [p for p in range(8) if flat[p] >= 0]
+    want = sorted(kept, key=lambda p: (flat[p], p))
+    assert sp.tolist() == want + [-1, -1]
+    assert offsets.tolist() == [0, 2, 3, 4, 6]
+    assert pp[1] == -1 and pp[4] == -1
+    assert [pp[p] for p in want] == list(range(6))
+    with pytest.raises(ValueError):
+        oracle.permute(np.array([[0, -2]], dtype=np.int32), 4)
+
+
+# -------------------------------------------------------------------------------------------
+# renorm-skip: picks after the first whose weight is below the threshold are dropped and the
+# kept weights renormalised (Strata-GLM blog, "Uncensoring without touching the weights")
+# -------------------------------------------------------------------------------------------
+
+def _route_skip(logits, k, tau):
+    l = np.asarray(logits, dtype=np.float64)
+    E = l.shape[-1]
+    return oracle.route(np.ascontiguousarray(l.reshape(-1, E)), np.eye(E, dtype=np.float32), None, k, tau)
+
+
+def test_renorm_skip_golden():
+    """Logits 3 2 -2 0.5 with k=3: the third pick (logit 0.5) weighs 0.2535 before the skip.  A
+    threshold of 0.3 drops it, and the two kept picks then carry exactly the weights of the
+    hand-worked two-expert case with logits 3 and 2 (tests/golden/router_cases.txt, first line)."""
+    _, ids2, ws2 = router_cases()[0][1:]
+    _, idx, w = _route_skip([3, 2, -2, 0.5], 3, 0.3)
+    assert idx[0].tolist() == [0, 1, -1]
+    np.testing.assert_allclose(w[0], list(ws2) + [0.0], rtol=0, atol=4e-16)
+    # a threshold below the third weight keeps all three, bit for bit as without the skip
+    _, idx0, w0 = _route_skip([3, 2, -2, 0.5], 3, 0.0)
+    _, idx1, w1 = _route_skip([3, 2, -2, 0.5], 3, 0.25)
+    assert idx1.tolist() == idx0.tolist() == [[0, 1, 3]]
+    np.testing.assert_array_equal(w1, w0)
+    # a threshold above every weight but the first keeps the first pick alone, with weight 1
+    _, idx, w = _route_skip([3, 2, -2, 0.5], 3, 0.9)
+    assert idx[0].tolist() == [0, -1, -1] and w[0].tolist() == [1.0, 0.0, 0.0]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_renorm_skip_relations(seed):
+    """Against the same routing without the skip: the kept picks are the same experts in the same
+    slots, they form a prefix of the rank order that always holds rank 0, a pick is dropped exactly
+    when its unskipped weight is below the threshold, and each kept weight is its unskipped weight
+    divided by the kept picks' unskipped total."""
+    rng = np.random.default_rng(seed)
+    l = rng.normal(size=(200, 288)) * rng.uniform(0.5, 3.0)
+    tau = float(np.float32(rng.uniform(0.05, 0.2)))
+    _, idx0, w0 = _route_skip(l, 8, 0.0)
+    _, idx, w = _route_skip(l, 8, tau)
+    dropped = idx < 0
+    assert not dropped[:, 0].any()
+    assert np.all(np.diff(dropped.astype(int), axis=1) >= 0)          # a suffix of the ranks
+    np.testing.assert_array_equal(dropped[:, 1:], w0[:, 1:] < tau)
+    np.testing.assert_array_equal(np.where(dropped, -1, idx0), idx)
+    kept_total = np.where(dropped, 0.0, w0).sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(w, np.where(dropped, 0.0, w0 / kept_total), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=4 * 2.0**-52)
+    assert dropped.any() and not dropped.all(axis=1).any()
