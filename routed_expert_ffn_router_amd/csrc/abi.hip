@@ -109,7 +109,8 @@ static moe_status check_shape(const moe_shape* s) {
     if (s->n_shared != 0 && s->n_shared != 1) return MOE_ERR_INVALID;
     if (s->act_quant != MOE_AQ_EXACT && s->act_quant != MOE_AQ_MXFP8) return MOE_ERR_INVALID;
     if (s->act_quant == MOE_AQ_MXFP8 && s->wformat != MOE_WF_MXFP4) return MOE_ERR_UNSUPPORTED;
-    if (s->n_shared != 0 || s->renorm_skip != 0.0f || s->act_quant != MOE_AQ_EXACT) return MOE_ERR_UNSUPPORTED;
+    if (s->n_shared != 0 || s->act_quant != MOE_AQ_EXACT) return MOE_ERR_UNSUPPORTED;
+    if (s->renorm_skip > 0.0f && s->top_k > 64) return MOE_ERR_UNSUPPORTED;
     if (s->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
     if (s->d_model % 128 != 0 || s->d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
     if ((long long)s->d_model * s->d_ff > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
@@ -489,6 +490,7 @@ static moe_status layer_launches(const moe_shape* s, const void* x, int32_t T, c
         r.xs = w8 + L.xs;
         r.ss1 = super_step(s->d_model, ksplit_for(s->d_model, variant));
         r.split = nv ? 0 : 1;
+        r.tau = s->renorm_skip;
         if (nv) {
             r.tt = nv_tile_picks(s, T);
             MOE_HIP(launch_route_small(s, r, stream));

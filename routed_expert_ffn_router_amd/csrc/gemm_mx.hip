@@ -278,7 +278,8 @@ __global__ __launch_bounds__(512) void k_mx_down_combine(GemmArgs a, CombineArgs
         float accv = 0.f;
         for (int j = 0; j < k; ++j) {
             const int p = tok * k + j;
-            accv = fmaf(c.w[p], o_lds[c.pick_pos[p]][r], accv);
+            const int pos = c.pick_pos[p];
+            if (pos >= 0) accv = fmaf(c.w[p], o_lds[pos][r], accv);   // (a dropped pick has none)
         }
         float v = accv * c.scaling;
         const size_t off = (size_t)tok * a.d + r0 + r;
@@ -509,6 +510,7 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs 
         for (int j = 0; j < k; ++j) {
             const int p = tok * k + j;
             const int pos = c.pick_pos[p];
+            if (pos < 0) continue;                  // a dropped pick
             float o = 0.f;
             for (int sl = 0; sl < nsl; ++sl) o += o_part[sl][pos][r];
             accv = fmaf(c.w[p], o, accv);
@@ -691,13 +693,14 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
         static_assert(kMaxDecSlices == 2, "the K slices of a down unit are added below");
 #pragma unroll
         for (int j = 0; j < MAXP; ++j) {
-            const float p0 = o_part[0][pos[j]][r], p1 = o_part[1][pos[j]][r];   // slice 1 read even
+            const int pj = pos[j] < 0 ? 0 : pos[j];                             // a dropped pick: -1
+            const float p0 = o_part[0][pj][r], p1 = o_part[1][pj][r];           // slice 1 read even
             o[j] = nsl > 1 ? p0 + p1 : p0;                                     // when unused
         }
         float accv = 0.f;
 #pragma unroll
         for (int j = 0; j < MAXP; ++j)
-            if (j < k) accv = fmaf(wgt[j], o[j], accv);
+            if (j < k && pos[j] >= 0) accv = fmaf(wgt[j], o[j], accv);
         float val = accv * c.scaling;
         if (c.residual) val += resq;
         store_act((XT*)c.y, yoff, val);

@@ -387,6 +387,7 @@ struct RouteSmallArgs {
     uint8_t* xs;
     int ss1;                  // MFMAs per chunk of the gate/up GEMM (activation layout)
     int split;                // 1: the other workgroups split x into fp8 terms (MXFP4); 0: not
+    float tau;                // renorm-skip threshold (0: off)
 };
 hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipStream_t st);
 

@@ -384,40 +384,50 @@ __device__ __forceinline__ double sigmoid64(double z) { return 1.0 / (1.0 + exp(
 // pick j's key (from topk_rounds).  sig: the sigmoid of every expert's logit, computed
 // beforehand, or null (each lane computes its pick's: of the selected logit, where a -0 comes
 // back as +0, with the same sigmoid).  The sum is taken in rank order.
+// Renorm-skip (tau > 0, k <= 64; the Strata-GLM blog, "Uncensoring without touching the
+// weights"): a pick after the first whose weight is below tau is dropped - idx -1 (written by the
+// lane that holds that pick), weight 0 - and the kept weights are renormalised over the kept
+// picks' sigmoids, summed in rank order.  The decision is taken on the fp64 weight.
 __device__ __forceinline__ void topk_weights(unsigned long long my_key, const double* __restrict__ l,
-                                             const int32_t* idx, int k, float* w, const double* sig) {
+                                             int32_t* idx, int k, float* w, const double* sig, float tau) {
     const int lane = threadIdx.x & 63;
     double sg = 0.0;
     if (lane < k) sg = sig ? sig[idx[lane]] : sigmoid64(key_logit(my_key));
     double ssum = 0.0;
     for (int j = 0; j < k && j < 64; ++j) ssum += readlane_f64(sg, j);
+    if (tau > 0.0f) {
+        const bool drop = lane > 0 && lane < k && sg / ssum < (double)tau;
+        const unsigned long long dm = __ballot(drop);
+        double kept = 0.0;
+        for (int j = 0; j < k; ++j)
+            if (!((dm >> j) & 1ull)) kept += readlane_f64(sg, j);
+        if (lane < k) {
+            w[lane] = drop ? 0.0f : (float)(sg / kept);
+            if (drop) idx[lane] = -1;
+        }
+        return;
+    }
     for (int j = 64; j < k; ++j) ssum += sig ? sig[idx[j]] : sigmoid64(l[idx[j]]);   // k > 64 only
     if (lane < k) w[lane] = (float)(sg / ssum);
     for (int j = lane + 64; j < k; j += 64) w[j] = (float)((sig ? sig[idx[j]] : sigmoid64(l[idx[j]])) / ssum);
 }
 
+// (topk_rounds has lane j % 64 write idx[j]: the lane that topk_weights has drop pick j)
 template <int S>
 __device__ void topk_select(const double (&lv)[S], const double* __restrict__ l, int E, int k, int32_t* idx,
-                            float* w) {
+                            float* w, float tau) {
     unsigned long long kv[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) kv[s] = logit_key(lv[s]);
     const unsigned long long my_key = topk_rounds<S>(kv, E, k, idx);
-    topk_weights(my_key, l, idx, k, w, nullptr);
-}
-
-template <int S>
-__device__ void wave_topk(const double* __restrict__ l, int E, int k, int32_t* idx, float* w) {
-    double lv[S];
-    topk_load<S>(l, E, lv);
-    topk_select<S>(lv, l, E, k, idx, w);
+    topk_weights(my_key, l, idx, k, w, nullptr, tau);
 }
 
 // one wave per token; the logits are the sum, in slice order, of nsplit partial slices
 // [nsplit][T][E] (nsplit = 1: the logits themselves)
 template <int S>
 __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int T, int E, int k, int nsplit,
-                                              int32_t* __restrict__ idx, float* __restrict__ wout) {
+                                              float tau, int32_t* __restrict__ idx, float* __restrict__ wout) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const double* l = logits + (size_t)t * E;
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
             if (lane + 64 * s < E) lw[lane + 64 * s] = lv[s];
         __threadfence_block();
     }
-    topk_select<S>(lv, l, E, k, idx + (size_t)t * k, wout + (size_t)t * k);
+    topk_select<S>(lv, l, E, k, idx + (size_t)t * k, wout + (size_t)t * k, tau);
 }
 
 hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t* idx, float* w,
@@ -456,9 +466,11 @@ hipError_t launch_topk(const moe_shape* s, const double* logits, int T, int32_t*
     dim3 grid((T + 3) / 4);
     const int nsplit = logits_splits(s, T);
     if (s->n_experts <= 320)
-        MOE_LAUNCH(k_topk<5>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, nsplit, idx, w);
+        MOE_LAUNCH(k_topk<5>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, nsplit, s->renorm_skip, idx,
+                   w);
     else
-        MOE_LAUNCH(k_topk<16>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, nsplit, idx, w);
+        MOE_LAUNCH(k_topk<16>, grid, dim3(256), 0, st, logits, T, s->n_experts, s->top_k, nsplit, s->renorm_skip, idx,
+                   w);
     trace("topk", 1, st);
     return hipGetLastError();
 }
@@ -704,15 +716,26 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 }
             }
             lds_barrier();
+            // the picks that stay (bit j: pick j), the same in every wave: all k, or with renorm-skip
+            // those not dropped (rank 0 and every pick whose fp64 weight is not below tau)
+            unsigned long long km = k >= 64 ? ~0ull : ((1ull << k) - 1ull);
+            double sg = 0.0, ssum = 0.0;
+            if (wave == 1 || a.tau > 0.0f) {        // (wave 1 always: it writes the weights)
+                if (lane < k) sg = s_sig[s_idx[lane]];
+                for (int j = 0; j < k; ++j) ssum += readlane_f64(sg, j);
+            }
+            if (a.tau > 0.0f) km = __ballot(lane < k && !(lane > 0 && sg / ssum < (double)a.tau));
+            const int nkept = __popcll(km);
             if (wave == 0) {
-                // the records: the token's k experts are distinct, so pick p is a tile of its own
-                // at sorted position = the number of picks of lower experts (what the grouping
-                // below gives in this case)
+                // the records: the token's kept experts are distinct, so kept pick p is a tile of
+                // its own at sorted position = the number of kept picks of lower experts (what the
+                // grouping below gives in this case)
                 const int p = lane;
                 const int e = p < k ? s_idx[p] : 0;
+                const bool kept = (km >> p) & 1ull;
                 int pos = 0;
-                for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(e, q) < e;
-                if (p < k) {
+                for (int q = 0; q < k; ++q) pos += ((km >> q) & 1ull) && __builtin_amdgcn_readlane(e, q) < e;
+                if (kept) {
                     TileDesc* D = desc + pos;
                     put_expert(D, e);
                     D->i0 = pos;
@@ -726,24 +749,31 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                     idx[p] = e;
                     pick_pos[p] = pos;
                     sorted_pick[pos] = p;
+                } else if (p < k) {          // dropped: no expert, no position
+                    idx[p] = -1;
+                    pick_pos[p] = -1;
+                    sorted_pick[p] = -1;     // positions nkept .. k - 1 (p >= nkept for a dropped pick)
                 }
             } else if (wave == 1) {
-                // the weights, the sum in rank order
+                // the weights, the sums in rank order (over the kept picks)
                 const int p = lane;
-                const double sg = p < k ? s_sig[s_idx[p]] : 0.0;
-                double ssum = 0.0;
-                for (int j = 0; j < k; ++j) ssum += readlane_f64(sg, j);
-                if (p < k) wout[p] = (float)(sg / ssum);
+                double kept_sum = ssum;
+                if (nkept < k) {
+                    kept_sum = 0.0;
+                    for (int j = 0; j < k; ++j)
+                        if ((km >> j) & 1ull) kept_sum += readlane_f64(sg, j);
+                }
+                if (p < k) wout[p] = ((km >> p) & 1ull) ? (float)(sg / kept_sum) : 0.0f;
             } else {
-                // the expert offsets (picks of lower experts), the empty records, the tile count
+                // the expert offsets (kept picks of lower experts), the empty records, the tile count
                 for (int e = tid - 128; e <= E; e += 128) {
                     int lower = 0;
 #pragma unroll 8
-                    for (int q = 0; q < k; ++q) lower += s_idx[q] < e;
+                    for (int q = 0; q < k; ++q) lower += ((km >> q) & 1ull) && s_idx[q] < e;
                     offsets[e] = lower;
                 }
-                for (int id = k + tid - 128; id < a.max_tiles; id += 128) put_empty(desc, id, s_idx[0]);
-                if (tid == 128) *ntiles = k;
+                for (int id = nkept + tid - 128; id < a.max_tiles; id += 128) put_empty(desc, id, s_idx[0]);
+                if (tid == 128) *ntiles = nkept;
             }
             lds_barrier();      // the real pass rewrites what this one read from LDS
         }
@@ -806,7 +836,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 unsigned long long my_key = 0ull;
                 if (k > 8 || !topk_pass<S>(kv[j], E, k, s_idx + t * k, s_cand[wave], s_rk[wave], my_key))
                     my_key = topk_rounds<S>(kv[j], E, k, s_idx + t * k);
-                topk_weights(my_key, nullptr, s_idx + t * k, k, s_w + t * k, nullptr);
+                topk_weights(my_key, nullptr, s_idx + t * k, k, s_w + t * k, nullptr, a.tau);
             }
         }
     }
@@ -816,22 +846,37 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         put_refused(a.desc, a.idx, a.w, a.pick_pos, a.sorted_pick, a.offsets, a.ntiles);
         return;
     }
-    // the expert offsets: the number of picks of lower experts
+    // the expert offsets: the number of picks of lower experts (a dropped pick, id -1, is no
+    // expert's: as unsigned it is above every id)
     auto put_offsets = [&]() {
         for (int e = tid; e <= E; e += 256) {
             int lower = 0;
 #pragma unroll 8
-            for (int q = 0; q < P; ++q) lower += s_idx[q] < e;
+            for (int q = 0; q < P; ++q) lower += (uint32_t)s_idx[q] < (uint32_t)e;
             a.offsets[e] = lower;
         }
     };
+    // kept picks (P unless renorm-skip dropped some: they are no expert's and take no position)
+    int Pv = P;
+    if (a.tau > 0.0f) {
+        Pv = 0;
+#pragma unroll 8
+        for (int q = 0; q < P; ++q) Pv += s_idx[q] >= 0;
+        for (int i = Pv + tid; i < P; i += 256) a.sorted_pick[i] = -1;
+    }
     if (T == 1) {
-        // one token (more than kTabLds experts): each pick is a tile of its own, as above
+        // one token (more than kTabLds experts): each kept pick is a tile of its own, as above
         for (int p = tid; p < k; p += 256) {
             const int e = s_idx[p];
+            if (e < 0) {
+                a.idx[p] = -1;
+                a.w[p] = 0.0f;
+                a.pick_pos[p] = -1;
+                continue;
+            }
             int pos = 0;
 #pragma unroll 8
-            for (int q = 0; q < k; ++q) pos += s_idx[q] < e;
+            for (int q = 0; q < k; ++q) pos += (uint32_t)s_idx[q] < (uint32_t)e;
             TileDesc* D = a.desc + pos;
             put_expert(D, e);
             D->i0 = pos;
@@ -848,8 +893,8 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             a.sorted_pick[pos] = p;
         }
         put_offsets();
-        for (int id = k + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id, s_idx[0]);
-        if (tid == 0) *a.ntiles = k;
+        for (int id = Pv + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id, s_idx[0]);
+        if (tid == 0) *a.ntiles = Pv;
         return;
     }
     // Grouping without atomics or scans (P <= 512, two picks per thread): a pick's sorted
@@ -860,13 +905,17 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     for (int u = 0; u < 2; ++u) {
         const int p = tid + 256 * u;
         pos[u] = -1;
-        if (p < P) {
+        if (p < P && s_idx[p] < 0) {           // dropped: no expert, no position
+            a.idx[p] = -1;
+            a.w[p] = 0.0f;
+            a.pick_pos[p] = -1;
+        } else if (p < P) {
             const int e = s_idx[p];
             int lower = 0, before = 0, same = 0;
 #pragma unroll 8
             for (int q = 0; q < P; ++q) {
                 const int eq = s_idx[q];
-                lower += eq < e;
+                lower += (uint32_t)eq < (uint32_t)e;
                 same += eq == e;
                 before += (eq == e) & (q < p);
             }
@@ -905,7 +954,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     // the tile count, and empty records up to max_tiles
     int nt = 0;
 #pragma unroll 8
-    for (int q = 0; q < P; ++q) nt += s_start[q];
+    for (int q = 0; q < Pv; ++q) nt += s_start[q];
     for (int id = nt + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id, s_idx[0]);
     if (tid == 0) *a.ntiles = nt;
 }

@@ -53,6 +53,7 @@ class Workload:
     weight_std: float = 0.02
     skew_alpha: float = 0.0  # logit bias b_e = -alpha * ln(rank_e); 0 = flat routing
     routed_scaling: float = 1.0
+    renorm_skip: float = 0.0
 
     @property
     def torch_act_dtype(self):

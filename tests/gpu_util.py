@@ -22,7 +22,7 @@ def tol(wl) -> float:
 
 def shape_of(m, wl):
     return m.make_shape(wl.d_model, wl.d_ff, wl.n_experts, wl.top_k, wl.wformat, wl.act_dtype,
-                        wl.routed_scaling)
+                        wl.routed_scaling, wl.renorm_skip)
 
 
 class DeviceLayer:
@@ -68,11 +68,12 @@ def oracle_layer(dl, x, idx_hint=None, residual=None, scaling=None):
     if idx_hint is None:
         _, idx_hint, _ = oracle.route(x64, dl.router.cpu().numpy(),
                                       None if dl.bias is None else dl.bias.cpu().numpy(), wl.top_k)
-    blobs = dl.host_blobs(np.asarray(idx_hint).reshape(-1))
+    hint = np.asarray(idx_hint).reshape(-1)
+    blobs = dl.host_blobs(hint[hint >= 0])
     res = None if residual is None else oracle.to_f64(residual)
     return oracle.layer(x64, dl.router.cpu().numpy(), None if dl.bias is None else dl.bias.cpu().numpy(),
                         blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat,
-                        wl.routed_scaling if scaling is None else scaling, res)
+                        wl.routed_scaling if scaling is None else scaling, res, wl.renorm_skip)
 
 
 def small(name="tiny", **kw):
