@@ -65,9 +65,9 @@ def lib():
         L.oracle_expert_ffn.restype = i32
         L.oracle_expert_ffn.argtypes = [P, i32, i32, i32, i32, P, i32, i32, P, P, P]
         L.oracle_combine.restype = i32
-        L.oracle_combine.argtypes = [P, P, P, i32, i32, i32, dbl, P, P]
+        L.oracle_combine.argtypes = [P, P, P, i32, i32, i32, dbl, P, P, P]
         L.oracle_layer.restype = i32
-        L.oracle_layer.argtypes = [P, i32, i32, i32, i32, i32, i32, dbl, dbl, P, P, P, P, P, P, P, P]
+        L.oracle_layer.argtypes = [P, i32, i32, i32, i32, i32, i32, dbl, dbl, P, P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -190,20 +190,21 @@ def expert_ffn(blobs, d: int, f: int, wformat: int, x64: np.ndarray, k: int,
 
 
 def combine(o: np.ndarray, w: np.ndarray, pick_pos: np.ndarray, scaling: float = 1.0,
-            residual: Optional[np.ndarray] = None) -> np.ndarray:
+            residual: Optional[np.ndarray] = None, o_shared: Optional[np.ndarray] = None) -> np.ndarray:
     T, k = w.shape
     d = o.shape[1]
     y = np.empty((T, d), dtype=np.float64)
     _check(lib().oracle_combine(_p(np.ascontiguousarray(o)), _p(np.ascontiguousarray(w)),
                                 _p(np.ascontiguousarray(pick_pos, dtype=np.int32)), T, k, d, scaling,
-                                _p(residual), _p(y)), "combine")
+                                _p(o_shared), _p(residual), _p(y)), "combine")
     return y
 
 
 def layer(x64: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], blobs, d: int, f: int,
           k: int, wformat: int, scaling: float = 1.0, residual: Optional[np.ndarray] = None,
-          renorm_skip: float = 0.0):
-    """Whole layer.  Returns (y [T,d] f64, idx [T,k] i32, w [T,k] f64, logits [T,E] f64)."""
+          renorm_skip: float = 0.0, shared_blob: Optional[np.ndarray] = None):
+    """Whole layer (with the shared expert's blob, if given).  Returns (y [T,d] f64, idx [T,k] i32,
+    w [T,k] f64, logits [T,E] f64)."""
     T = x64.shape[0]
     E = len(blobs)
     y = np.empty((T, d), dtype=np.float64)
@@ -214,6 +215,7 @@ def layer(x64: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], blo
     b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     ptrs = _blob_ptrs(blobs)
     _check(lib().oracle_layer(_p(x64), T, d, f, E, k, wformat, scaling, _f32(renorm_skip), _p(wr), _p(b),
-                              ctypes.cast(ptrs, ctypes.c_void_p), _p(residual), _p(y), _p(idx), _p(w),
-                              _p(logits)), "layer")
+                              ctypes.cast(ptrs, ctypes.c_void_p),
+                              None if shared_blob is None else _p(np.ascontiguousarray(shared_blob)),
+                              _p(residual), _p(y), _p(idx), _p(w), _p(logits)), "layer")
     return y, idx, w, logits

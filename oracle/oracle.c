@@ -300,12 +300,15 @@ int oracle_expert_ffn(const uint8_t *const *blobs, int d, int f, int E, int wfor
 }
 
 /* ---------------------------------------------------------------------------------------- */
-/* combine: y[t] = scaling * sum_j w[t,j] * o[pick_pos[t*k+j]] (+ residual[t]), dropped     */
-/* picks (pick_pos -1) left out                                                              */
+/* combine: y[t] = scaling * sum_j w[t,j] * o[pick_pos[t*k+j]] (+ o_shared[t])              */
+/* (+ residual[t]), dropped picks (pick_pos -1) left out.  o_shared: the shared expert's    */
+/* output per token ("Project Maya", "What is in the 96.5 GB": shared experts beside the    */
+/* routed ones), added with weight 1 outside the routed scaling, or NULL.                   */
 /* ---------------------------------------------------------------------------------------- */
 
 int oracle_combine(const double *o, const double *w, const int32_t *pick_pos, int T, int k,
-                   int d, double scaling, const double *residual, double *y) {
+                   int d, double scaling, const double *o_shared, const double *residual,
+                   double *y) {
     if (T < 0 || k < 1 || d <= 0) return -1;
     #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
@@ -317,6 +320,7 @@ int oracle_combine(const double *o, const double *w, const int32_t *pick_pos, in
                 acc += w[(int64_t)t * k + j] * o[(int64_t)pos * d + c];
             }
             acc *= scaling;
+            if (o_shared) acc += o_shared[(int64_t)t * d + c];
             if (residual) acc += residual[(int64_t)t * d + c];
             y[(int64_t)t * d + c] = acc;
         }
@@ -328,10 +332,12 @@ int oracle_combine(const double *o, const double *w, const int32_t *pick_pos, in
 /* whole layer = route, permute, expert FFN, combine                                         */
 /* ---------------------------------------------------------------------------------------- */
 
+/* shared_blob: the shared expert's blob, or NULL for none.  Its output for every token is that
+ * expert's FFN of the token: the expert FFN above with one expert taking every token once. */
 int oracle_layer(const double *x, int T, int d, int f, int E, int k, int wformat,
                  double scaling, double renorm_skip, const float *w_router, const float *bias,
-                 const uint8_t *const *blobs, const double *residual, double *y,
-                 int32_t *idx_out, double *w_out, double *logits_out) {
+                 const uint8_t *const *blobs, const uint8_t *shared_blob, const double *residual,
+                 double *y, int32_t *idx_out, double *w_out, double *logits_out) {
     if (T == 0) return 0;
     int64_t P = (int64_t)T * k;
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
@@ -340,10 +346,21 @@ int oracle_layer(const double *x, int T, int d, int f, int E, int k, int wformat
     int32_t *sorted_pick = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
     int32_t *pick_pos = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
     double *o = (double *)malloc(sizeof(double) * (size_t)P * d);
+    double *o_shared = NULL;
     int rc = oracle_route(x, T, d, w_router, bias, E, k, renorm_skip, logits_out, idx, w);
     if (rc == 0) rc = oracle_permute(idx, T, k, E, offsets, sorted_pick, pick_pos);
     if (rc == 0) rc = oracle_expert_ffn(blobs, d, f, E, wformat, x, T, k, offsets, sorted_pick, o);
-    if (rc == 0) rc = oracle_combine(o, w, pick_pos, T, k, d, scaling, residual, y);
+    if (rc == 0 && shared_blob) {
+        /* one expert, every token: offsets {0, T}, token t at position t */
+        int32_t sh_off[2] = {0, T};
+        int32_t *sh_pick = (int32_t *)malloc(sizeof(int32_t) * (size_t)T);
+        for (int t = 0; t < T; ++t) sh_pick[t] = t;
+        o_shared = (double *)malloc(sizeof(double) * (size_t)T * d);
+        const uint8_t *sh_blobs[1] = {shared_blob};
+        rc = oracle_expert_ffn(sh_blobs, d, f, 1, wformat, x, T, 1, sh_off, sh_pick, o_shared);
+        free(sh_pick);
+    }
+    if (rc == 0) rc = oracle_combine(o, w, pick_pos, T, k, d, scaling, o_shared, residual, y);
     if (rc == 0 && idx_out) memcpy(idx_out, idx, sizeof(int32_t) * (size_t)P);
     if (rc == 0 && w_out) memcpy(w_out, w, sizeof(double) * (size_t)P);
     free(idx);
@@ -352,5 +369,6 @@ int oracle_layer(const double *x, int T, int d, int f, int E, int k, int wformat
     free(sorted_pick);
     free(pick_pos);
     free(o);
+    free(o_shared);
     return rc;
 }

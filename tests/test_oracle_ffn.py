@@ -334,3 +334,39 @@ def test_renorm_skip_layer_matches_numpy_and_catches_missing_renormalisation():
         np.testing.assert_allclose(y[t], want, rtol=1e-11, atol=1e-13 * np.abs(want).max())
         y_bad[t] = sum(w0[t, j] * ffns[i] for i, j in enumerate(kept))
     _assert_caught(y_bad, y, "kept weights not renormalised")
+
+
+# -------------------------------------------------------------------------------------------
+# the shared expert: every token's dense FFN, added outside the routed scaling
+# -------------------------------------------------------------------------------------------
+
+def _shared_inputs():
+    wl = dataclasses.replace(TINY, n_experts=TINY.n_experts + 1, tokens=5)   # blob E is the shared one
+    x64, wr, bias, blobs = _inputs(wl, seed=3)
+    return TINY, x64, np.ascontiguousarray(wr[:TINY.n_experts]), blobs[:TINY.n_experts], blobs[TINY.n_experts]
+
+
+def test_shared_expert_alone_is_its_dense_ffn():
+    """With the routed sum scaled to nothing, y is the shared expert's dense SwiGLU FFN of each token
+    (numpy matmuls on independently decoded weights) plus the residual."""
+    wl, x64, wr, blobs, sb = _shared_inputs()
+    res = np.ascontiguousarray(x64 * 0.5)
+    y, *_ = oracle.layer(x64, wr, None, blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat, 0.0, res,
+                         shared_blob=sb)
+    for t in range(x64.shape[0]):
+        want = _dense_ffn(sb, x64[t], wl) + res[t]
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-14 * np.abs(want).max())
+
+
+def test_shared_expert_sits_outside_routed_scaling():
+    """y(shared, routed_scaling 2.5) = 2.5 * y(no shared expert, scaling 1) + FFN_shared(x): the
+    shared expert is added with weight 1 after the scaling (the scaling factor of the windlass
+    README's negative controls, 2.5); scaling it with the routed sum is caught by far."""
+    wl, x64, wr, blobs, sb = _shared_inputs()
+    y1, *_ = oracle.layer(x64, wr, None, blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat, 1.0)
+    y, *_ = oracle.layer(x64, wr, None, blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat, 2.5, shared_blob=sb)
+    sh = np.stack([_dense_ffn(sb, x64[t], wl) for t in range(x64.shape[0])])
+    want = 2.5 * y1 + sh
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-14 * np.abs(want).max())
+    _assert_caught(2.5 * (y1 + sh), y, "shared expert inside the routed scaling")
+    _assert_caught(y1 + sh, y, "routed scaling ignored")
