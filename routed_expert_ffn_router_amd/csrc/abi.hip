@@ -52,7 +52,9 @@ WsLayout ws_layout(const moe_shape* s, int32_t T, bool slots_for_any_shape) {
     // the fused few-token path tiles with the smaller few-token tile: bound for both
     if (T <= kSmallTokens && (size_t)gemm_tile_tokens(0, L.nt) < tt) tt = (size_t)gemm_tile_tokens(0, L.nt);
     if (nv) tt = kNvTilePicks;
-    L.max_tiles = (int)((E < P ? E : P) + P / tt + 1);
+    // routed tiles, then the shared expert's T picks (positions P .. P + T - 1)
+    const size_t Pall = P + (s->n_shared ? (size_t)T : 0);
+    L.max_tiles = (int)((E < P ? E : P) + P / tt + 1 + (s->n_shared ? (size_t)T / tt + 1 : 0));
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
     // status word and poll limit (MOE_WS_STATUS_OFFSET = 0), then the fused router's logit
@@ -77,17 +79,17 @@ WsLayout ws_layout(const moe_shape* s, int32_t T, bool slots_for_any_shape) {
         // bf16 terms: x as two terms when it is fp32, h always as two
         L.xq = take((size_t)T * 2 * d * 2);
         L.xs = take(0);
-        L.hq = take(P * 2 * f * 2);
+        L.hq = take(Pall * 2 * f * 2);
         L.hs = take(0);
     } else {
         L.xq = take((size_t)T * L.nt * d);
         L.xs = take((size_t)T * L.nt * d / 32);
-        L.hq = take(P * L.nt * f);
-        L.hs = take(P * L.nt * f / 32);
+        L.hq = take(Pall * L.nt * f);
+        L.hs = take(Pall * L.nt * f / 32);
     }
-    L.o = take(4 * P * d);
+    L.o = take(4 * Pall * d);
     if (nv) {
-        L.stage_table = take(sizeof(moe_expert) * E);
+        L.stage_table = take(sizeof(moe_expert) * (E + s->n_shared));   // the shared expert's entry last
         L.stage_list = take(4 * E);
         L.stage_n = take(4);
         L.stage_ranges = take(8 * ((E + kStageGroup - 1) / kStageGroup));
@@ -109,7 +111,7 @@ static moe_status check_shape(const moe_shape* s) {
     if (s->n_shared != 0 && s->n_shared != 1) return MOE_ERR_INVALID;
     if (s->act_quant != MOE_AQ_EXACT && s->act_quant != MOE_AQ_MXFP8) return MOE_ERR_INVALID;
     if (s->act_quant == MOE_AQ_MXFP8 && s->wformat != MOE_WF_MXFP4) return MOE_ERR_UNSUPPORTED;
-    if (s->n_shared != 0 || s->act_quant != MOE_AQ_EXACT) return MOE_ERR_UNSUPPORTED;
+    if (s->act_quant != MOE_AQ_EXACT) return MOE_ERR_UNSUPPORTED;
     if (s->renorm_skip > 0.0f && s->top_k > 64) return MOE_ERR_UNSUPPORTED;
     if (s->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
     if (s->d_model % 128 != 0 || s->d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
@@ -145,6 +147,7 @@ static GemmArgs gemm_args(const moe_shape* s, const moe_expert* table, int32_t T
     a.E = s->n_experts;
     a.k = s->top_k;
     a.P = T * s->top_k;
+    a.Pall = a.P + (s->n_shared ? T : 0);
     a.sorted_pick = sorted_pick;
     a.tiles = (const int32_t*)(ws + L.tiles);
     a.ntiles = (const int32_t*)(ws + L.ntiles);
@@ -170,7 +173,7 @@ static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const 
     const int tt = nv_tile_picks(s, T);
     int32_t* tiles = (int32_t*)(ws + L.tiles);
     int32_t* ntiles = (int32_t*)(ws + L.ntiles);
-    if (!planned) MOE_HIP(launch_plan(s, offsets, tt, tiles, ntiles, st));
+    if (!planned) MOE_HIP(launch_plan(s, offsets, T, tt, tiles, ntiles, st));
     const bool bf = s->act_dtype == MOE_DT_BF16;
     const int NT = bf ? 1 : 2;
     if (!bf) MOE_HIP(launch_bf16_terms((const float*)x, T, s->d_model, (uint16_t*)(ws + L.xq), st));
@@ -187,7 +190,7 @@ static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const 
     int32_t* nlist = (int32_t*)(ws + L.stage_n);
     int32_t* ranges = (int32_t*)(ws + L.stage_ranges);
     moe_expert* staged = (moe_expert*)(ws + L.stage_table);
-    MOE_HIP(launch_stage_plan(s, offsets, tt, ntiles, list, nlist, ranges, st));
+    MOE_HIP(launch_stage_plan(s, offsets, tt, ntiles, list, nlist, ranges, table, staged, st));
     const size_t stride = moe_blob_stride(s);
     const long long P = (long long)T * s->top_k;
     const long long distinct = P < s->n_experts ? P : s->n_experts;
@@ -212,7 +215,7 @@ static moe_status run_ffn(const moe_shape* s, const moe_expert* table, const voi
     const int variant = gemm_variant(s, T);
     const int NT = L.nt;
     const int tt = gemm_tile_tokens(variant, NT);
-    MOE_HIP(launch_plan(s, offsets, tt, (int32_t*)(ws + L.tiles), (int32_t*)(ws + L.ntiles), st));
+    MOE_HIP(launch_plan(s, offsets, T, tt, (int32_t*)(ws + L.tiles), (int32_t*)(ws + L.ntiles), st));
     const int SS1 = act_super_step(s->d_model, variant);
     MOE_HIP(launch_act_split(s, x, T, s->d_model, SS1, NT, ws + L.xq, ws + L.xs, st));
     GemmArgs a = gemm_args(s, table, T, sorted_pick, offsets, ws, L, o);
@@ -456,8 +459,8 @@ static moe_status layer_launches(const moe_shape* s, const void* x, int32_t T, c
     int32_t* sorted_pick = (int32_t*)(w8 + L.sorted_pick);
     int32_t* pick_pos = (int32_t*)(w8 + L.pick_pos);
     float* o = (float*)(w8 + L.o);
-    if ((!nv || !staging) && T <= kSmallTokens && s->top_k <= 64 && (long long)T * s->top_k <= kMaxFusedPicks &&
-        s->d_model <= 8192) {
+    if ((!nv || !staging) && T <= kSmallTokens && s->top_k <= 64 &&
+        (long long)T * (s->top_k + s->n_shared) <= kMaxFusedPicks && s->d_model <= 8192) {
         // few tokens: fused router (logits, top-k, permute, plan, activation split), the gate/up
         // GEMM, and the down GEMM fused with the weighted combine: three launches per layer
         // (NVFP4: the fused router, its two GEMMs and the combine)
@@ -491,6 +494,7 @@ static moe_status layer_launches(const moe_shape* s, const void* x, int32_t T, c
         r.ss1 = super_step(s->d_model, ksplit_for(s->d_model, variant));
         r.split = nv ? 0 : 1;
         r.tau = s->renorm_skip;
+        r.shared = s->n_shared;
         if (nv) {
             r.tt = nv_tile_picks(s, T);
             MOE_HIP(launch_route_small(s, r, stream));
@@ -508,6 +512,8 @@ static moe_status layer_launches(const moe_shape* s, const void* x, int32_t T, c
         a.as = w8 + L.hs;
         CombineArgs c;
         c.T = T;
+        c.shared = s->n_shared;
+        c.P = T * s->top_k;
         c.w = w;
         c.pick_pos = pick_pos;
         c.residual = residual;

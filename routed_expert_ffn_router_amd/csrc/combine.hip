@@ -6,10 +6,11 @@ namespace moe {
 // y[t] = s * sum_j w[t,j] * o[pick_pos[t*k+j]] (+ residual[t]); one thread per 4 columns,
 // the k terms summed in rank order in fp32 (picks with pick_pos -1 left out), rounded once to the
 // output dtype.
+// With a shared expert (shared = 1) its output, row T k + t of o, is added after the scaling.
 template <typename XT>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, const float* __restrict__ w,
                                                  const int32_t* __restrict__ pick_pos, int T, int k, int d,
-                                                 float scaling, const XT* __restrict__ residual,
+                                                 float scaling, int shared, const XT* __restrict__ residual,
                                                  XT* __restrict__ y) {
     const int t = blockIdx.y;
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -26,6 +27,13 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, co
         acc.w = fmaf(wj, v.w, acc.w);
     }
     float r[4] = {acc.x * scaling, acc.y * scaling, acc.z * scaling, acc.w * scaling};
+    if (shared) {
+        const float4 v = *(const float4*)(o + ((size_t)T * k + t) * d + c);
+        r[0] += v.x;
+        r[1] += v.y;
+        r[2] += v.z;
+        r[3] += v.w;
+    }
     const size_t b = (size_t)t * d + c;
     if (residual) {
 #pragma unroll
@@ -42,10 +50,10 @@ hipError_t launch_combine(const moe_shape* s, const float* o, const float* w, co
     dim3 grid((d / 4 + 255) / 256, T);
     if (s->act_dtype == MOE_DT_BF16)
         MOE_LAUNCH(k_combine<uint16_t>, grid, dim3(256), 0, st, o, w, pick_pos, T, s->top_k, d,
-                           s->routed_scaling, (const uint16_t*)residual, (uint16_t*)y);
+                   s->routed_scaling, s->n_shared, (const uint16_t*)residual, (uint16_t*)y);
     else
         MOE_LAUNCH(k_combine<float>, grid, dim3(256), 0, st, o, w, pick_pos, T, s->top_k, d,
-                           s->routed_scaling, (const float*)residual, (float*)y);
+                   s->routed_scaling, s->n_shared, (const float*)residual, (float*)y);
     trace("combine", 1, st);
     return hipGetLastError();
 }
@@ -90,8 +98,9 @@ hipError_t launch_fill_table(const moe_shape* s, const uint8_t* base, size_t str
                              hipStream_t st) {
     trace("fill_table", 0, st);
     const BlobSizes z = blob_sizes(s);
-    MOE_LAUNCH(k_fill_table, dim3((s->n_experts + 255) / 256), dim3(256), 0, st, base, stride,
-                       s->n_experts, z.nq, z.ns, (int)(s->wformat == MOE_WF_NVFP4), table);
+    const int n = s->n_experts + s->n_shared;       // the shared expert's entry last
+    MOE_LAUNCH(k_fill_table, dim3((n + 255) / 256), dim3(256), 0, st, base, stride, n, z.nq, z.ns,
+               (int)(s->wformat == MOE_WF_NVFP4), table);
     trace("fill_table", 1, st);
     return hipGetLastError();
 }

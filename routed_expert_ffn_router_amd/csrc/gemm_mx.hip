@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void k_mx_gemm(GemmArgs a, int ss2) {
     const int tile = blockIdx.x;
     if (tile >= *a.ntiles) return;
     const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
-    const int ntok = min(TT, a.offsets[e + 1] - i0);
+    const int ntok = min(TT, range_end(a, e) - i0);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int K = GATEUP ? a.d : a.f;
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void k_mx_gemm(GemmArgs a, int ss2) {
         const int tc = n * (16 / NT) + li / NT, t = li % NT;
         bval[n] = tc < ntok;
         int arow = 0;
-        if (bval[n]) arow = GATEUP ? a.sorted_pick[i0 + tc] / a.k : (i0 + tc);
+        if (bval[n]) arow = GATEUP ? pos_token(a, i0 + tc) : (i0 + tc);
         bq[n] = a.aq + ((size_t)arow * NT + t) * K + lg * 32 * SS + (size_t)kss0 * 128 * SS;
         bs[n] = a.as + ((size_t)arow * NT + t) * (K / 32) + lg * SS + (size_t)kss0 * 4 * SS;
     }
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(512) void k_mx_down_combine(GemmArgs a, CombineArgs
     const int ntiles = *a.ntiles;
     for (int tile = wave; tile < ntiles; tile += 8) {
         const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
-        const int ntok = min(TT, a.offsets[e + 1] - i0);
+        const int ntok = min(TT, range_end(a, e) - i0);
         const moe_expert ex = a.table[e];
         const uint8_t* const aq[1] = {ex.down_q + (size_t)(r0 + li) * (K / 2) + lg * 16 * SS};
         const uint8_t* const as[1] = {ex.down_s + (size_t)(r0 + li) * (K / 32) + lg * SS};
@@ -282,6 +282,7 @@ __global__ __launch_bounds__(512) void k_mx_down_combine(GemmArgs a, CombineArgs
             if (pos >= 0) accv = fmaf(c.w[p], o_lds[pos][r], accv);   // (a dropped pick has none)
         }
         float v = accv * c.scaling;
+        if (c.shared) v += o_lds[c.P + tok][r];                            // the shared expert, unscaled
         const size_t off = (size_t)tok * a.d + r0 + r;
         if (c.residual) v += load_act((const XT*)c.residual, off);
         store_act((XT*)c.y, off, v);
@@ -516,6 +517,11 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs 
             accv = fmaf(c.w[p], o, accv);
         }
         float v = accv * c.scaling;
+        if (c.shared) {                                  // the shared expert, unscaled
+            float o = 0.f;
+            for (int sl = 0; sl < nsl; ++sl) o += o_part[sl][c.P + tok][r];
+            v += o;
+        }
         const size_t off = (size_t)tok * a.d + r0 + r;
         if (c.residual) v += load_act((const XT*)c.residual, off);
         store_act((XT*)c.y, off, v);
@@ -547,7 +553,7 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
     const int r0 = blockIdx.x * 16;
     const int K = a.f;
     const int nsl = K / kDecKSlice;
-    const int P = a.P, ncols = P * NT;
+    const int P = a.P, ncols = a.Pall * NT;         // picks; h columns (with the shared expert's)
     // 1. tile records (16-byte chunks, one per thread), this thread's pick weight and position,
     // and the residual of the output it will write (thread q = tid writes token q/16, row
     // r0 + q%16): one round trip
@@ -702,6 +708,10 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
         for (int j = 0; j < MAXP; ++j)
             if (j < k && pos[j] >= 0) accv = fmaf(wgt[j], o[j], accv);
         float val = accv * c.scaling;
+        if (c.shared) {                                  // the shared expert, unscaled
+            const float s0 = o_part[0][c.P + tok][r], s1 = o_part[1][c.P + tok][r];
+            val += nsl > 1 ? s0 + s1 : s0;
+        }
         if (c.residual) val += resq;
         store_act((XT*)c.y, yoff, val);
     }
@@ -741,7 +751,7 @@ hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineA
     trace("down_combine", 0, st);
     dim3 grid(a.d / 16);
     const bool bf = s->act_dtype == MOE_DT_BF16;
-    if (a.P * NT <= kDownLdsCols && a.f <= kDownMaxF && a.max_tiles <= kDownMaxTiles) {
+    if (a.Pall * NT <= kDownLdsCols && a.f <= kDownMaxF && a.max_tiles <= kDownMaxTiles) {
         if (bf) {
             if (NT == 2) MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
             else MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 4>), grid, dim3(512), 0, st, a, c);
@@ -915,7 +925,7 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
     const int tile = xcd * TPX + tq;
     if (tile >= nt) return;
     const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
-    const int ntok = min(TT, a.offsets[e + 1] - i0);
+    const int ntok = min(TT, range_end(a, e) - i0);
     const moe_expert ex = a.table[e];
 
     // tile row r (0..255) -> weight row; down rows past d re-read row d - 1 (not stored)
@@ -935,7 +945,7 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
     auto b_col_ptr = [&](int c, bool scale) -> const uint8_t* {
         const int tc = c / NT, t = c % NT;
         const int tcc = tc < ntok ? tc : 0;
-        const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tcc] / a.k) : (size_t)(i0 + tcc);
+        const size_t arow = GATEUP ? (size_t)pos_token(a, i0 + tcc) : (size_t)(i0 + tcc);
         return scale ? a.as + (arow * NT + t) * (size_t)(K / 32) : a.aq + (arow * NT + t) * (size_t)K;
     };
     // this wave's direct loads: weight rows 64 w .. 64 w + 63 (4 instructions of 16 rows, a

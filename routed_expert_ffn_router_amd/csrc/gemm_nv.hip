@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
     }
     if (tile < t0 || tile >= t1) return;
     const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
-    const int ntok = min(TTP, a.offsets[e + 1] - i0);
+    const int ntok = min(TTP, range_end(a, e) - i0);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int K = GATEUP ? a.d : a.f;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
     for (int n = 0; n < NCF; ++n) {
         const int c = n * 16 + li, tc = c / NT, t = c % NT;
         const int tcc = tc < ntok ? tc : 0;
-        const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tcc] / a.k) : (size_t)(i0 + tcc);
+        const size_t arow = GATEUP ? (size_t)pos_token(a, i0 + tcc) : (size_t)(i0 + tcc);
         bp[n] = (const uint16_t*)a.aq + (arow * NT + t) * (size_t)K + (size_t)s0 * 128 + lg * 32;
     }
 
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
     const int tile = t_lo + xcd * TPX + tq;
     if (tile >= t_hi) return;
     const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
-    const int ntok = min(kNvTilePicksMany, a.offsets[e + 1] - i0);
+    const int ntok = min(kNvTilePicksMany, range_end(a, e) - i0);
     const moe_expert ex = a.table[e];
 
     auto a_row = [&](int r, bool scale) -> const uint8_t* {
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
     auto b_col = [&](int c) -> const uint8_t* {
         const int tc = c / NT, t = c % NT;
         const int tcc = tc < ntok ? tc : 0;
-        const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tcc] / a.k) : (size_t)(i0 + tcc);
+        const size_t arow = GATEUP ? (size_t)pos_token(a, i0 + tcc) : (size_t)(i0 + tcc);
         return a.aq + (arow * NT + t) * (size_t)K * 2;
     };
     // staging: A codes (2 chunks per thread), A scales (threads < 64: 16 bytes = two rows' 8),
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
     }
     if (tile < t0 || tile >= t1) return;
     const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
-    const int ntok = min(min(kNvTilePicks, NCOL / NT), a.offsets[e + 1] - i0);
+    const int ntok = min(min(kNvTilePicks, NCOL / NT), range_end(a, e) - i0);
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
     const int ncol = ntok * NT, cpc = K / 8, nchunk = ncol * cpc;
     auto chunk_src = [&](int g) -> const uint8_t* {
         const int c = g / cpc, tc = c / NT, t = c % NT;
-        const size_t arow = GATEUP ? (size_t)(a.sorted_pick[i0 + tc] / a.k) : (size_t)(i0 + tc);
+        const size_t arow = GATEUP ? (size_t)pos_token(a, i0 + tc) : (size_t)(i0 + tc);
         return a.aq + ((arow * NT + t) * (size_t)K + (size_t)(g % cpc) * 8) * 2;
     };
     const int g0 = tid < nchunk ? tid : nchunk - 1;

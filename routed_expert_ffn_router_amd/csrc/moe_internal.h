@@ -358,7 +358,8 @@ hipError_t launch_permute(const moe_shape* s, const int32_t* idx, int T, int32_t
                           hipStream_t st);
 // zero words [0, nwords) of a workspace, except word 1 := poll_limit
 hipError_t launch_ws_init(uint32_t* ws, size_t nwords, int32_t poll_limit, hipStream_t st);
-hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int tile_tokens, int32_t* tiles,
+// tiles of the routed experts' ranges, then (n_shared) the shared expert's: positions [P, P + T)
+hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int T, int tile_tokens, int32_t* tiles,
                        int32_t* ntiles, hipStream_t st);
 
 // fused few-token router (route + permute + plan + activation split); T <= 16, P <= 1024
@@ -388,12 +389,16 @@ struct RouteSmallArgs {
     int ss1;                  // MFMAs per chunk of the gate/up GEMM (activation layout)
     int split;                // 1: the other workgroups split x into fp8 terms (MXFP4); 0: not
     float tau;                // renorm-skip threshold (0: off)
+    int shared;               // 1: a shared expert (table entry E) at sorted positions T * k + t
 };
 hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipStream_t st);
 
+// Sorted positions: [0, P) are the routed picks (P = T * k), grouped by expert through the offsets;
+// with a shared expert, [P, P + T) are its picks, token t at position P + t, and its table entry is E.
 struct GemmArgs {
     const moe_expert* table;
     int d, f, E, k, P;
+    int Pall;                 // P + T with a shared expert, else P
     const int32_t* sorted_pick;
     const int32_t* tiles;     // [max_tiles][2] = (expert, first sorted position)
     const int32_t* ntiles;
@@ -408,12 +413,21 @@ struct GemmArgs {
     const int32_t* tile_range;  // NVFP4 staged groups: [t0, t1) of the tiles to run, or null (all)
 };
 
+// end of expert e's range of sorted positions (the shared expert, e = E: P + T)
+__device__ __forceinline__ int range_end(const GemmArgs& a, int e) { return e < a.E ? a.offsets[e + 1] : a.Pall; }
+// token of sorted position i: a routed pick's through sorted_pick, the shared expert's i - P
+__device__ __forceinline__ int pos_token(const GemmArgs& a, int i) {
+    return i < a.P ? a.sorted_pick[i] / a.k : i - a.P;
+}
+
 // picks whose per-row outputs the fused down+combine kernel keeps in LDS (P = T * top_k)
 constexpr int kMaxFusedPicks = 512;
 constexpr int kMaxDecSlices = 2;          // d_ff / 1024 K slices kept in LDS by the down kernel
 
 struct CombineArgs {
     int T;
+    int shared;               // 1: add the shared expert's output (sorted position P + t), unscaled
+    int P;
     const float* w;           // [T][k] route weights
     const int32_t* pick_pos;  // [T][k] sorted position of each pick
     const void* residual;     // [T][d] or null
@@ -445,14 +459,16 @@ hipError_t launch_bf16_terms(const float* x, int rows, int K, uint16_t* terms, h
 hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int tile_picks, int max_tiles,
                           hipStream_t st);
 // the distinct experts of a plan, in groups of kStageGroup, with each group's tile range
+// (with a shared expert, its table entry is copied to staged[E]: it is read in place)
 hipError_t launch_stage_plan(const moe_shape* s, const int32_t* offsets, int tt, const int32_t* ntiles,
-                             int32_t* list, int32_t* nlist, int32_t* ranges, hipStream_t st);
+                             int32_t* list, int32_t* nlist, int32_t* ranges, const moe_expert* table,
+                             moe_expert* staged, hipStream_t st);
 hipError_t launch_gather_group(const moe_shape* s, const moe_expert* table, const int32_t* list,
                                const int32_t* nlist, int group, uint8_t* staging, size_t stride,
                                moe_expert* staged_by_expert, hipStream_t st);
 
 hipError_t launch_combine(const moe_shape* s, const float* o, const float* w, const int32_t* pick_pos,
-                          int T, const void* residual, void* y, hipStream_t st);
+                          int T, const void* residual, void* y, hipStream_t st);   // (s->n_shared: + o[T k + t])
 hipError_t launch_fill_table(const moe_shape* s, const uint8_t* base, size_t stride,
                              moe_expert* table, hipStream_t st);
 hipError_t launch_gather(const moe_shape* s, const moe_expert* table, const int32_t* list, int n,

@@ -214,9 +214,10 @@ hipError_t launch_permute(const moe_shape* s, const int32_t* idx, int T, int32_t
     return hipGetLastError();
 }
 
-// Tiles of at most `tt` consecutive sorted positions of one expert: tiles[i] = (expert, first).
-__global__ __launch_bounds__(kPermThreads) void k_plan(const int32_t* __restrict__ offsets, int E, int tt,
-                                                       int32_t* __restrict__ tiles,
+// Tiles of at most `tt` consecutive sorted positions of one expert: tiles[i] = (expert, first); then
+// the shared expert's (table entry E) over positions [P, P + Tsh), Tsh = T with a shared expert, else 0.
+__global__ __launch_bounds__(kPermThreads) void k_plan(const int32_t* __restrict__ offsets, int E, int tt, int P,
+                                                       int Tsh, int32_t* __restrict__ tiles,
                                                        int32_t* __restrict__ ntiles) {
     __shared__ int scratch[kPermWaves];
     const int e = threadIdx.x;
@@ -232,7 +233,12 @@ __global__ __launch_bounds__(kPermThreads) void k_plan(const int32_t* __restrict
         tiles[2 * (first + j)] = e;
         tiles[2 * (first + j) + 1] = o0 + j * tt;
     }
-    if (e == 0) *ntiles = total;
+    const int nsh = (Tsh + tt - 1) / tt;
+    for (int j = threadIdx.x; j < nsh; j += kPermThreads) {
+        tiles[2 * (total + j)] = E;
+        tiles[2 * (total + j) + 1] = P + j * tt;
+    }
+    if (e == 0) *ntiles = total + nsh;
 }
 
 // workspace preparation: the header (status 0, poll limit) and the hand-over slots (0)
@@ -249,11 +255,11 @@ hipError_t launch_ws_init(uint32_t* ws, size_t nwords, int32_t poll_limit, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int tile_tokens, int32_t* tiles,
+hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int T, int tile_tokens, int32_t* tiles,
                        int32_t* ntiles, hipStream_t st) {
     trace("plan", 0, st);
-    MOE_LAUNCH(k_plan, dim3(1), dim3(kPermThreads), 0, st, offsets, s->n_experts, tile_tokens,
-                       tiles, ntiles);
+    MOE_LAUNCH(k_plan, dim3(1), dim3(kPermThreads), 0, st, offsets, s->n_experts, tile_tokens, T * s->top_k,
+               s->n_shared ? T : 0, tiles, ntiles);
     trace("plan", 1, st);
     return hipGetLastError();
 }
@@ -265,7 +271,9 @@ hipError_t launch_plan(const moe_shape* s, const int32_t* offsets, int tile_toke
 __global__ __launch_bounds__(kPermThreads) void k_stage_plan(const int32_t* __restrict__ offsets, int E, int tt,
                                                              const int32_t* __restrict__ ntiles,
                                                              int32_t* __restrict__ list, int32_t* __restrict__ nlist,
-                                                             int32_t* __restrict__ ranges, int max_groups) {
+                                                             int32_t* __restrict__ ranges, int max_groups,
+                                                             const moe_expert* __restrict__ table,
+                                                             moe_expert* __restrict__ staged, int shared) {
     __shared__ int scratch[kPermWaves];
     const int e = threadIdx.x;
     const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
@@ -290,16 +298,19 @@ __global__ __launch_bounds__(kPermThreads) void k_stage_plan(const int32_t* __re
     }
     if (e == 0) {
         *nlist = n;
+        // the last group's range runs to the end of the plan, the shared expert's tiles included
         if (n > 0) ranges[2 * (groups - 1) + 1] = *ntiles;
+        if (shared) staged[E] = table[E];       // the shared expert is read in place
     }
 }
 
 hipError_t launch_stage_plan(const moe_shape* s, const int32_t* offsets, int tt, const int32_t* ntiles,
-                             int32_t* list, int32_t* nlist, int32_t* ranges, hipStream_t st) {
+                             int32_t* list, int32_t* nlist, int32_t* ranges, const moe_expert* table,
+                             moe_expert* staged, hipStream_t st) {
     trace("stage_plan", 0, st);
     const int max_groups = (s->n_experts + kStageGroup - 1) / kStageGroup;
     MOE_LAUNCH(k_stage_plan, dim3(1), dim3(kPermThreads), 0, st, offsets, s->n_experts, tt, ntiles, list, nlist,
-               ranges, max_groups);
+               ranges, max_groups, table, staged, s->n_shared);
     trace("stage_plan", 1, st);
     return hipGetLastError();
 }

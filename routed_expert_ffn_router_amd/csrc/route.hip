@@ -593,7 +593,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     // the expert-table entry of expert e into a tile record: four 16-byte moves, from the LDS copy
     // of the table when there is one
     auto put_expert = [&](TileDesc* D, int e) {
-        const uint4* src = tab_lds ? &s_tab[4 * e] : (const uint4*)(a.table + e);
+        const uint4* src = (tab_lds && e < E) ? &s_tab[4 * e] : (const uint4*)(a.table + e);   // shared: E
         uint4* dst = (uint4*)&D->ex;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[i] = src[i];
@@ -606,6 +606,25 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         D->i0 = 0;
         D->ntok = 0;
         D->e = e;
+    };
+    // the shared expert's tiles (table entry E): tokens c tt .. of tile c, at sorted positions
+    // P + c tt .., record ids first, first + 1, ...; nothing without a shared expert
+    auto put_shared = [&](TileDesc* desc, int32_t* tiles, int first, int thread, int nthreads) {
+        const int tt = a.tt, nsh = a.shared ? (T + tt - 1) / tt : 0;
+        for (int c = thread; c < nsh; c += nthreads) {
+            TileDesc* D = desc + first + c;
+            const int ntok = min(tt, T - c * tt);
+            put_expert(D, E);
+            D->i0 = P + c * tt;
+            D->ntok = ntok;
+            D->e = E;
+            D->pad0 = 0;
+#pragma unroll
+            for (int j = 0; j < kDescTokens; ++j) D->tok[j] = j < ntok ? c * tt + j : 0;
+            tiles[2 * (first + c)] = E;
+            tiles[2 * (first + c) + 1] = P + c * tt;
+        }
+        return nsh;
     };
     // the outputs of a refused routing (see report_timeout), by all 256 threads
     auto put_refused = [&](TileDesc* desc, int32_t* idx, float* wout, int32_t* pick_pos, int32_t* sorted_pick,
@@ -754,6 +773,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                     pick_pos[p] = -1;
                     sorted_pick[p] = -1;     // positions nkept .. k - 1 (p >= nkept for a dropped pick)
                 }
+                put_shared(desc, tiles, nkept, lane, 64);
             } else if (wave == 1) {
                 // the weights, the sums in rank order (over the kept picks)
                 const int p = lane;
@@ -772,8 +792,9 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                     for (int q = 0; q < k; ++q) lower += ((km >> q) & 1ull) && s_idx[q] < e;
                     offsets[e] = lower;
                 }
-                for (int id = nkept + tid - 128; id < a.max_tiles; id += 128) put_empty(desc, id, s_idx[0]);
-                if (tid == 128) *ntiles = nkept;
+                const int nall = nkept + (a.shared ? 1 : 0);      // one token: one shared tile
+                for (int id = nall + tid - 128; id < a.max_tiles; id += 128) put_empty(desc, id, s_idx[0]);
+                if (tid == 128) *ntiles = nall;
             }
             lds_barrier();      // the real pass rewrites what this one read from LDS
         }
@@ -893,8 +914,9 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             a.sorted_pick[pos] = p;
         }
         put_offsets();
-        for (int id = Pv + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id, s_idx[0]);
-        if (tid == 0) *a.ntiles = Pv;
+        const int nall = Pv + put_shared(a.desc, a.tiles, Pv, tid, 256);
+        for (int id = nall + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id, s_idx[0]);
+        if (tid == 0) *a.ntiles = nall;
         return;
     }
     // Grouping without atomics or scans (P <= 512, two picks per thread): a pick's sorted
@@ -955,6 +977,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     int nt = 0;
 #pragma unroll 8
     for (int q = 0; q < Pv; ++q) nt += s_start[q];
+    nt += put_shared(a.desc, a.tiles, nt, tid, 256);
     for (int id = nt + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id, s_idx[0]);
     if (tid == 0) *a.ntiles = nt;
 }

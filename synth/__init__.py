@@ -54,6 +54,7 @@ class Workload:
     skew_alpha: float = 0.0  # logit bias b_e = -alpha * ln(rank_e); 0 = flat routing
     routed_scaling: float = 1.0
     renorm_skip: float = 0.0
+    n_shared: int = 0        # 1: one more expert blob (index n_experts), the shared expert
 
     @property
     def torch_act_dtype(self):
@@ -239,12 +240,13 @@ def skew_share(alpha: float, E: int = 288, k: int = 8, tokens: int = 20000, seed
 
 def make_experts(wl: Workload, layer: int = 0, seed: int = 0, device="cpu",
                  experts: Optional[list] = None, group: int = 16) -> torch.Tensor:
-    """Expert blobs [E, stride] uint8 for one layer, quantised from N(0, weight_std^2).
+    """Expert blobs [E + n_shared, stride] uint8 for one layer, quantised from N(0, weight_std^2)
+    (blob n_experts is the shared expert when there is one).
 
     ``experts`` restricts generation to a subset (others stay zero); each expert's bytes
     depend only on (seed, workload, layer, expert), never on the subset or the group size.
     """
-    d, f, E = wl.d_model, wl.d_ff, wl.n_experts
+    d, f, E = wl.d_model, wl.d_ff, wl.n_experts + wl.n_shared
     off = blob_offsets(d, f, wl.wformat)
     blob = torch.zeros(E, off["stride"], dtype=torch.uint8, device=device)
     fill_experts(blob, wl, layer, seed, experts, group)
@@ -253,7 +255,7 @@ def make_experts(wl: Workload, layer: int = 0, seed: int = 0, device="cpu",
 
 def fill_experts(blob: torch.Tensor, wl: Workload, layer: int = 0, seed: int = 0,
                  experts: Optional[list] = None, group: int = 16) -> None:
-    d, f, E = wl.d_model, wl.d_ff, wl.n_experts
+    d, f, E = wl.d_model, wl.d_ff, wl.n_experts + wl.n_shared
     off = blob_offsets(d, f, wl.wformat)
     ids = list(range(E)) if experts is None else list(experts)
     device = blob.device

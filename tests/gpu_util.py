@@ -22,7 +22,7 @@ def tol(wl) -> float:
 
 def shape_of(m, wl):
     return m.make_shape(wl.d_model, wl.d_ff, wl.n_experts, wl.top_k, wl.wformat, wl.act_dtype,
-                        wl.routed_scaling, wl.renorm_skip)
+                        wl.routed_scaling, wl.renorm_skip, wl.n_shared)
 
 
 class DeviceLayer:
@@ -39,7 +39,7 @@ class DeviceLayer:
         self.bias = None if lay["bias"] is None else lay["bias"].to("cuda").contiguous()
         self.blob = lay["blob"].to("cuda").contiguous()
         self.stride = self.blob.shape[1]
-        self.table = torch.empty(wl.n_experts * m.EXPERT_BYTES, dtype=torch.uint8, device="cuda")
+        self.table = torch.empty((wl.n_experts + wl.n_shared) * m.EXPERT_BYTES, dtype=torch.uint8, device="cuda")
         m.moe_fill_table(self.shape, self.blob, self.stride, self.table)
 
     def host_blobs(self, experts):
@@ -48,6 +48,10 @@ class DeviceLayer:
         for e in sorted(set(int(v) for v in experts)):
             out[e] = self.blob[e].cpu().numpy()
         return out
+
+    def shared_blob(self):
+        """Host copy of the shared expert's blob, or None."""
+        return self.blob[self.wl.n_experts].cpu().numpy() if self.wl.n_shared else None
 
 
 def run_layer(m, dl, x, residual=None):
@@ -73,7 +77,8 @@ def oracle_layer(dl, x, idx_hint=None, residual=None, scaling=None):
     res = None if residual is None else oracle.to_f64(residual)
     return oracle.layer(x64, dl.router.cpu().numpy(), None if dl.bias is None else dl.bias.cpu().numpy(),
                         blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat,
-                        wl.routed_scaling if scaling is None else scaling, res, wl.renorm_skip)
+                        wl.routed_scaling if scaling is None else scaling, res, wl.renorm_skip,
+                        dl.shared_blob())
 
 
 def small(name="tiny", **kw):
