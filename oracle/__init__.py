@@ -63,11 +63,15 @@ def lib():
         L.oracle_permute.restype = i32
         L.oracle_permute.argtypes = [P, i32, i32, i32, P, P, P]
         L.oracle_expert_ffn.restype = i32
-        L.oracle_expert_ffn.argtypes = [P, i32, i32, i32, i32, P, i32, i32, P, P, P]
+        L.oracle_expert_ffn.argtypes = [P, i32, i32, i32, i32, i32, P, i32, i32, P, P, P]
+        L.oracle_e4m3_round.restype = dbl
+        L.oracle_e4m3_round.argtypes = [dbl]
+        L.oracle_quant_mxfp8.restype = None
+        L.oracle_quant_mxfp8.argtypes = [P, i64]
         L.oracle_combine.restype = i32
         L.oracle_combine.argtypes = [P, P, P, i32, i32, i32, dbl, P, P, P]
         L.oracle_layer.restype = i32
-        L.oracle_layer.argtypes = [P, i32, i32, i32, i32, i32, i32, dbl, dbl, P, P, P, P, P, P, P, P, P]
+        L.oracle_layer.argtypes = [P, i32, i32, i32, i32, i32, i32, i32, dbl, dbl, P, P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -175,14 +179,25 @@ def _blob_ptrs(blobs: Sequence[Optional[np.ndarray]]):
     return arr
 
 
+def e4m3_round(v: float) -> float:
+    return lib().oracle_e4m3_round(v)
+
+
+def quant_mxfp8(v: np.ndarray) -> np.ndarray:
+    """The opt-in activation quantiser on a copy of v (length a multiple of 32, blocks of 32)."""
+    out = np.ascontiguousarray(v, dtype=np.float64).copy()
+    lib().oracle_quant_mxfp8(_p(out), out.size)
+    return out
+
+
 def expert_ffn(blobs, d: int, f: int, wformat: int, x64: np.ndarray, k: int,
-               offsets: np.ndarray, sorted_pick: np.ndarray) -> np.ndarray:
+               offsets: np.ndarray, sorted_pick: np.ndarray, act_quant: int = 0) -> np.ndarray:
     """o [T*k, d]; row i belongs to pick sorted_pick[i]."""
     T = x64.shape[0]
     E = len(blobs)
     o = np.empty((T * k, d), dtype=np.float64)
     ptrs = _blob_ptrs(blobs)
-    _check(lib().oracle_expert_ffn(ctypes.cast(ptrs, ctypes.c_void_p), d, f, E, wformat, _p(x64), T, k,
+    _check(lib().oracle_expert_ffn(ctypes.cast(ptrs, ctypes.c_void_p), d, f, E, wformat, act_quant, _p(x64), T, k,
                                    _p(np.ascontiguousarray(offsets, dtype=np.int32)),
                                    _p(np.ascontiguousarray(sorted_pick, dtype=np.int32)), _p(o)),
            "expert_ffn")
@@ -202,7 +217,7 @@ def combine(o: np.ndarray, w: np.ndarray, pick_pos: np.ndarray, scaling: float =
 
 def layer(x64: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], blobs, d: int, f: int,
           k: int, wformat: int, scaling: float = 1.0, residual: Optional[np.ndarray] = None,
-          renorm_skip: float = 0.0, shared_blob: Optional[np.ndarray] = None):
+          renorm_skip: float = 0.0, shared_blob: Optional[np.ndarray] = None, act_quant: int = 0):
     """Whole layer (with the shared expert's blob, if given).  Returns (y [T,d] f64, idx [T,k] i32,
     w [T,k] f64, logits [T,E] f64)."""
     T = x64.shape[0]
@@ -214,7 +229,7 @@ def layer(x64: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray], blo
     wr = np.ascontiguousarray(w_router, dtype=np.float32)
     b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     ptrs = _blob_ptrs(blobs)
-    _check(lib().oracle_layer(_p(x64), T, d, f, E, k, wformat, scaling, _f32(renorm_skip), _p(wr), _p(b),
+    _check(lib().oracle_layer(_p(x64), T, d, f, E, k, wformat, act_quant, scaling, _f32(renorm_skip), _p(wr), _p(b),
                               ctypes.cast(ptrs, ctypes.c_void_p),
                               None if shared_blob is None else _p(np.ascontiguousarray(shared_blob)),
                               _p(residual), _p(y), _p(idx), _p(w), _p(logits)), "layer")

@@ -105,6 +105,45 @@ int oracle_dequant(const uint8_t *q, const uint8_t *s, double ts, int64_t rows, 
 }
 
 /* ---------------------------------------------------------------------------------------- */
+/* the opt-in MXFP8 activation quantiser (an analogue of the on-the-fly 8-bit activations of */
+/* "Project Maya", section "A V100 has no BF16 and no FP8")                                   */
+/* ---------------------------------------------------------------------------------------- */
+
+/* The E4M3FN value nearest to v, ties to the even code, for |v| < 448 (no saturation needed
+ * here): below 2^-6 the subnormal grid m * 2^-9, else 8 steps per binade [2^e, 2^(e+1)).
+ * Exact in fp64: every step is a power of two and rint() rounds half to even. */
+double oracle_e4m3_round(double v) {
+    double a = fabs(v), q;
+    if (a < ldexp(1.0, -6)) {
+        q = ldexp(rint(ldexp(a, 9)), -9);
+    } else {
+        int ex;
+        frexp(a, &ex);                          /* a = m * 2^ex, m in [0.5, 1): binade 2^(ex - 1) */
+        double step = ldexp(1.0, ex - 1 - 3);
+        q = rint(a / step) * step;
+    }
+    return v < 0 ? -q : q;
+}
+
+/* Quantise n values (n a multiple of 32) in place, block by block of 32: with amax the block's
+ * largest magnitude, the scale is 2^S with S = floor(log2 amax) - 7 (at least -126; -126 for an
+ * all-zero block), so every |v| / 2^S < 256; each value becomes E4M3(v / 2^S) * 2^S. */
+void oracle_quant_mxfp8(double *v, int64_t n) {
+    for (int64_t b = 0; b < n; b += 32) {
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[b + i]));
+        int S = -126;
+        if (amax > 0.0) {
+            int ex;
+            frexp(amax, &ex);                   /* floor(log2 amax) = ex - 1 */
+            S = ex - 1 - 7;
+            if (S < -126) S = -126;
+        }
+        for (int i = 0; i < 32; ++i) v[b + i] = ldexp(oracle_e4m3_round(ldexp(v[b + i], -S)), S);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------- */
 /* expert blob: [gate_q | up_q | down_q | gate_s | up_s | down_s] (+ 3 fp32 tensor scales,  */
 /* padded to 256 bytes, for NVFP4).  gate/up are [f][d], down is [d][f]; blocks run along   */
 /* the reduction dimension of each row.                                                       */
@@ -252,9 +291,10 @@ int oracle_permute(const int32_t *idx, int T, int k, int E, int32_t *offsets,
 /* ---------------------------------------------------------------------------------------- */
 
 /* blobs[e]: host pointer to expert e's blob (NULL allowed for experts that receive
- * no pick).  o: [T*k][d], row i belongs to pick sorted_pick[i].  Returns 0, -1 on a
- * bad argument, -2 if a routed expert has no blob. */
-int oracle_expert_ffn(const uint8_t *const *blobs, int d, int f, int E, int wformat,
+ * no pick).  o: [T*k][d], row i belongs to pick sorted_pick[i].  act_quant 1: the FFN's
+ * inputs x and h are quantised first (oracle_quant_mxfp8; the opt-in activation mode), 0: used
+ * as they are.  Returns 0, -1 on a bad argument, -2 if a routed expert has no blob. */
+int oracle_expert_ffn(const uint8_t *const *blobs, int d, int f, int E, int wformat, int act_quant,
                       const double *x, int T, int k, const int32_t *offsets,
                       const int32_t *sorted_pick, double *o) {
     if (d <= 0 || f <= 0 || E <= 0 || k < 1) return -1;
@@ -263,6 +303,7 @@ int oracle_expert_ffn(const uint8_t *const *blobs, int d, int f, int E, int wfor
     double *Wu = (double *)malloc(sizeof(double) * (size_t)f * d);
     double *Wd = (double *)malloc(sizeof(double) * (size_t)d * f);
     double *h = (double *)malloc(sizeof(double) * (size_t)f);
+    double *xq = (double *)malloc(sizeof(double) * (size_t)d);
     int rc = 0;
     for (int e = 0; e < E && rc == 0; ++e) {
         if (offsets[e + 1] == offsets[e]) continue;
@@ -275,6 +316,11 @@ int oracle_expert_ffn(const uint8_t *const *blobs, int d, int f, int E, int wfor
         for (int32_t i = offsets[e]; i < offsets[e + 1]; ++i) {
             int t = sorted_pick[i] / k;
             const double *xt = x + (int64_t)t * d;
+            if (act_quant) {
+                memcpy(xq, xt, sizeof(double) * (size_t)d);
+                oracle_quant_mxfp8(xq, d);
+                xt = xq;
+            }
             #pragma omp parallel for schedule(static)
             for (int r = 0; r < f; ++r) {
                 double g = 0.0, u = 0.0;
@@ -284,6 +330,7 @@ int oracle_expert_ffn(const uint8_t *const *blobs, int d, int f, int E, int wfor
                 }
                 h[r] = g * sigmoid(g) * u;
             }
+            if (act_quant) oracle_quant_mxfp8(h, f);
             #pragma omp parallel for schedule(static)
             for (int c = 0; c < d; ++c) {
                 double acc = 0.0;
@@ -296,6 +343,7 @@ int oracle_expert_ffn(const uint8_t *const *blobs, int d, int f, int E, int wfor
     free(Wu);
     free(Wd);
     free(h);
+    free(xq);
     return rc;
 }
 
@@ -334,7 +382,7 @@ int oracle_combine(const double *o, const double *w, const int32_t *pick_pos, in
 
 /* shared_blob: the shared expert's blob, or NULL for none.  Its output for every token is that
  * expert's FFN of the token: the expert FFN above with one expert taking every token once. */
-int oracle_layer(const double *x, int T, int d, int f, int E, int k, int wformat,
+int oracle_layer(const double *x, int T, int d, int f, int E, int k, int wformat, int act_quant,
                  double scaling, double renorm_skip, const float *w_router, const float *bias,
                  const uint8_t *const *blobs, const uint8_t *shared_blob, const double *residual,
                  double *y, int32_t *idx_out, double *w_out, double *logits_out) {
@@ -349,7 +397,7 @@ int oracle_layer(const double *x, int T, int d, int f, int E, int k, int wformat
     double *o_shared = NULL;
     int rc = oracle_route(x, T, d, w_router, bias, E, k, renorm_skip, logits_out, idx, w);
     if (rc == 0) rc = oracle_permute(idx, T, k, E, offsets, sorted_pick, pick_pos);
-    if (rc == 0) rc = oracle_expert_ffn(blobs, d, f, E, wformat, x, T, k, offsets, sorted_pick, o);
+    if (rc == 0) rc = oracle_expert_ffn(blobs, d, f, E, wformat, act_quant, x, T, k, offsets, sorted_pick, o);
     if (rc == 0 && shared_blob) {
         /* one expert, every token: offsets {0, T}, token t at position t */
         int32_t sh_off[2] = {0, T};
@@ -357,7 +405,7 @@ int oracle_layer(const double *x, int T, int d, int f, int E, int k, int wformat
         for (int t = 0; t < T; ++t) sh_pick[t] = t;
         o_shared = (double *)malloc(sizeof(double) * (size_t)T * d);
         const uint8_t *sh_blobs[1] = {shared_blob};
-        rc = oracle_expert_ffn(sh_blobs, d, f, 1, wformat, x, T, 1, sh_off, sh_pick, o_shared);
+        rc = oracle_expert_ffn(sh_blobs, d, f, 1, wformat, act_quant, x, T, 1, sh_off, sh_pick, o_shared);
         free(sh_pick);
     }
     if (rc == 0) rc = oracle_combine(o, w, pick_pos, T, k, d, scaling, o_shared, residual, y);
