@@ -38,7 +38,12 @@ hipEvent_t launch_event(int which) { return t_launch_ev[which]; }
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-int act_terms(const moe_shape* s) { return s->act_dtype == MOE_DT_BF16 ? 2 : 4; }
+// activation terms per value: the opt-in MXFP8 mode takes one (the quantised value itself); the
+// exact mode two for bf16 and four for fp32 activations (their residuals are exact)
+int act_terms(const moe_shape* s) {
+    if (s->act_quant == MOE_AQ_MXFP8) return 1;
+    return s->act_dtype == MOE_DT_BF16 ? 2 : 4;
+}
 
 WsLayout ws_layout(const moe_shape* s, int32_t T, bool slots_for_any_shape) {
     WsLayout L;
@@ -111,7 +116,6 @@ static moe_status check_shape(const moe_shape* s) {
     if (s->n_shared != 0 && s->n_shared != 1) return MOE_ERR_INVALID;
     if (s->act_quant != MOE_AQ_EXACT && s->act_quant != MOE_AQ_MXFP8) return MOE_ERR_INVALID;
     if (s->act_quant == MOE_AQ_MXFP8 && s->wformat != MOE_WF_MXFP4) return MOE_ERR_UNSUPPORTED;
-    if (s->act_quant != MOE_AQ_EXACT) return MOE_ERR_UNSUPPORTED;
     if (s->renorm_skip > 0.0f && s->top_k > 64) return MOE_ERR_UNSUPPORTED;
     if (s->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
     if (s->d_model % 128 != 0 || s->d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;

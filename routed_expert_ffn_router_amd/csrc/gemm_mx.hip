@@ -45,6 +45,7 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const uint4& a, const uint4& b0, con
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+
 // acc[f][n] += A_f x B_n over nss super-steps (SS MFMAs each), CH super-steps per load burst.
 // aq/as: per-lane pointers to this lane's first weight block/scale; bq/bs: activation columns.
 template <int NA, int NTN, int SS, int CH>
@@ -115,7 +116,8 @@ __device__ __forceinline__ void sum_terms(v4f (&acc)[NA][NTN]) {
 template <int NT, int NTN, int KSPLIT, int SS, bool GATEUP>
 __global__ __launch_bounds__(256) void k_mx_gemm(GemmArgs a, int ss2) {
     constexpr int NA = GATEUP ? 4 : 2;      // A fragments per MFMA step
-    constexpr int TT = 16 * NTN / NT;       // tokens per tile
+    // tokens per tile: the tile's columns, at most the tokens a few-token tile record holds
+    constexpr int TT = (16 * NTN / NT) < kDescTokens ? 16 * NTN / NT : kDescTokens;
     constexpr int CH = GATEUP ? 1 : 2;
     const int tile = blockIdx.x;
     if (tile >= *a.ntiles) return;
@@ -168,6 +170,10 @@ __global__ __launch_bounds__(256) void k_mx_gemm(GemmArgs a, int ss2) {
 #pragma unroll
         for (int n = 0; n < NTN; ++n) acc[f][n] = v4f{0.f, 0.f, 0.f, 0.f};
     mx_accumulate<NA, NTN, SS, CH>(aq, as, bq, bs, bval, nss, acc);
+#pragma unroll
+    for (int f = 0; f < NA; ++f)
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) mfma_results_here(acc[f][n]);
 
     if constexpr (KSPLIT == 4) {
         __shared__ float red[3][NA * NTN * 4][64];
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(256) void k_mx_gemm(GemmArgs a, int ss2) {
 // ---------------------------------------------------------------------------------------------
 template <typename XT, int NT, int SS>
 __global__ __launch_bounds__(512) void k_mx_down_combine(GemmArgs a, CombineArgs c) {
-    constexpr int NTN = 1, TT = 16 / NT, CH = 4;
+    constexpr int NTN = 1, TT = (16 / NT) < kDescTokens ? 16 / NT : kDescTokens, CH = 4;
     __shared__ float o_lds[kMaxFusedPicks][16];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
@@ -265,6 +271,7 @@ __global__ __launch_bounds__(512) void k_mx_down_combine(GemmArgs a, CombineArgs
         const uint8_t* const bs[1] = {a.as + (arow * NT + t) * (K / 32) + lg * SS};
         v4f acc[1][1] = {{v4f{0.f, 0.f, 0.f, 0.f}}};
         mx_accumulate<1, NTN, SS, CH>(aq, as, bq, bs, bval, nss, acc);
+        mfma_results_here(acc[0][0]);
         sum_terms<1, NTN, NT>(acc);
         if (tc < ntok && t == 0) {
 #pragma unroll
@@ -497,6 +504,7 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs 
         const uint8_t* const bs[1] = {a.as + (arow * NT + t) * (K / 32) + lg * SS + (size_t)kss0 * 4 * SS};
         v4f acc[1][1] = {{v4f{0.f, 0.f, 0.f, 0.f}}};
         mx_accumulate<1, 1, SS, 2>(aq, as, bq, bs, bval, nss, acc);
+        mfma_results_here(acc[0][0]);
         sum_terms<1, 1, NT>(acc);
         if (tc < ntok && t == 0) {
 #pragma unroll
@@ -645,6 +653,7 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
                     acc = mfma_fp4_fp8(A[j][q][h], B[h][0], B[h][1], acc, (int)((sa[j][q] >> (8 * h)) & 0xffu),
                                        (int)((sb >> (8 * h)) & 0xffu));
             }
+            mfma_results_here(acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = sum_adjacent<NT>(acc[r]);
             if (tc < ntok && t == 0) {
@@ -741,7 +750,8 @@ hipError_t launch_gateup_dec(const GemmArgs& a, int NT, int max_tiles, hipStream
     // two workgroups per CU, each taking (tile, row block) pairs in turn
     const long long pairs = (long long)max_tiles * (a.f / 32);
     dim3 grid((unsigned)(pairs < 2LL * device_cus() ? pairs : 2LL * device_cus()));
-    if (NT == 2) MOE_LAUNCH(k_mx_gateup_dec<2>, grid, dim3(512), 0, st, a, ss2, (int)grid.x);
+    if (NT == 1) MOE_LAUNCH(k_mx_gateup_dec<1>, grid, dim3(512), 0, st, a, ss2, (int)grid.x);
+    else if (NT == 2) MOE_LAUNCH(k_mx_gateup_dec<2>, grid, dim3(512), 0, st, a, ss2, (int)grid.x);
     else MOE_LAUNCH(k_mx_gateup_dec<4>, grid, dim3(512), 0, st, a, ss2, (int)grid.x);
     trace("gemm_gate_up", 1, st);
     return hipGetLastError();
@@ -753,20 +763,24 @@ hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineA
     const bool bf = s->act_dtype == MOE_DT_BF16;
     if (a.Pall * NT <= kDownLdsCols && a.f <= kDownMaxF && a.max_tiles <= kDownMaxTiles) {
         if (bf) {
-            if (NT == 2) MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
+            if (NT == 1) MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 1>), grid, dim3(512), 0, st, a, c);
+            else if (NT == 2) MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
             else MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 4>), grid, dim3(512), 0, st, a, c);
         } else {
-            if (NT == 2) MOE_LAUNCH((k_mx_down_dec_lds<float, 2>), grid, dim3(512), 0, st, a, c);
+            if (NT == 1) MOE_LAUNCH((k_mx_down_dec_lds<float, 1>), grid, dim3(512), 0, st, a, c);
+            else if (NT == 2) MOE_LAUNCH((k_mx_down_dec_lds<float, 2>), grid, dim3(512), 0, st, a, c);
             else MOE_LAUNCH((k_mx_down_dec_lds<float, 4>), grid, dim3(512), 0, st, a, c);
         }
         trace("down_combine", 1, st);
         return hipGetLastError();
     }
     if (bf) {
-        if (NT == 2) MOE_LAUNCH((k_mx_down_dec<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
+        if (NT == 1) MOE_LAUNCH((k_mx_down_dec<uint16_t, 1>), grid, dim3(512), 0, st, a, c);
+        else if (NT == 2) MOE_LAUNCH((k_mx_down_dec<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
         else MOE_LAUNCH((k_mx_down_dec<uint16_t, 4>), grid, dim3(512), 0, st, a, c);
     } else {
-        if (NT == 2) MOE_LAUNCH((k_mx_down_dec<float, 2>), grid, dim3(512), 0, st, a, c);
+        if (NT == 1) MOE_LAUNCH((k_mx_down_dec<float, 1>), grid, dim3(512), 0, st, a, c);
+        else if (NT == 2) MOE_LAUNCH((k_mx_down_dec<float, 2>), grid, dim3(512), 0, st, a, c);
         else MOE_LAUNCH((k_mx_down_dec<float, 4>), grid, dim3(512), 0, st, a, c);
     }
     trace("down_combine", 1, st);
@@ -778,7 +792,12 @@ int gemm_variant(const moe_shape* s, int T) {
     return (P <= 8LL * s->n_experts) ? 0 : 1;
 }
 
-int gemm_tile_tokens(int variant, int NT) { return (variant == 0 ? 16 : 128) / NT; }
+// picks per tile: the MFMA columns over the terms per value; a few-token tile also at most the
+// tokens its tile record holds
+int gemm_tile_tokens(int variant, int NT) {
+    if (variant == 0) return 16 / NT < kDescTokens ? 16 / NT : kDescTokens;
+    return 128 / NT;
+}
 
 // activation layout super-step for the variant: the LDS-tiled many-picks GEMM reads chunks of 128
 int act_super_step(int K, int variant) { return variant == 1 ? 1 : super_step(K, ksplit_for(K, variant)); }
@@ -1084,6 +1103,10 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
+        for (int n = 0; n < 4; ++n) mfma_results_here(acc[j][n]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
         for (int n = 0; n < 4; ++n)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[j][n][r] = sum_adjacent<NT>(acc[j][n][r]);
@@ -1144,7 +1167,11 @@ static hipError_t launch_pf(const GemmArgs& a, int NT, int max_tiles, hipStream_
     // the workload's K (d_model 4096 for gate/up, d_ff 2048 for down) takes the straight-line instance
     constexpr int kFull = GATEUP ? 32 : 16;
     const bool full = (GATEUP ? a.d : a.f) == 128 * kFull;
-    if (NT == 2) {
+    if (NT == 1) {
+        // (single-term down runs the looped instance: the straight-line one spills at K = 2048)
+        if (full && GATEUP) MOE_LAUNCH((k_mx_pf<1, true, 32>), grid, dim3(256), 0, st, a, 1, cap);
+        else MOE_LAUNCH((k_mx_pf<1, GATEUP, 0>), grid, dim3(256), 0, st, a, 1, cap);
+    } else if (NT == 2) {
         if (full) MOE_LAUNCH((k_mx_pf<2, GATEUP, kFull>), grid, dim3(256), 0, st, a, 1, cap);
         else MOE_LAUNCH((k_mx_pf<2, GATEUP, 0>), grid, dim3(256), 0, st, a, 1, cap);
     } else {
@@ -1163,9 +1190,11 @@ static hipError_t launch_gemm(const GemmArgs& a, int NT, int variant, int max_ti
     const int ss2 = super_step(a.f, ksplit_for(a.f, variant));
     dim3 grid(max_tiles, (rows / 32) / (ks == 4 ? 1 : 4));
     if (variant == 0) {
-        if (ks == 4) return NT == 2 ? launch_one<GATEUP, 2, 1, 4>(a, SS, ss2, grid, st)
+        if (ks == 4) return NT == 1 ? launch_one<GATEUP, 1, 1, 4>(a, SS, ss2, grid, st)
+                          : NT == 2 ? launch_one<GATEUP, 2, 1, 4>(a, SS, ss2, grid, st)
                                     : launch_one<GATEUP, 4, 1, 4>(a, SS, ss2, grid, st);
-        return NT == 2 ? launch_one<GATEUP, 2, 1, 1>(a, SS, ss2, grid, st)
+        return NT == 1 ? launch_one<GATEUP, 1, 1, 1>(a, SS, ss2, grid, st)
+             : NT == 2 ? launch_one<GATEUP, 2, 1, 1>(a, SS, ss2, grid, st)
                        : launch_one<GATEUP, 4, 1, 1>(a, SS, ss2, grid, st);
     }
     return launch_pf<GATEUP>(a, NT, max_tiles, st);
@@ -1196,10 +1225,12 @@ hipError_t launch_down_combine(const moe_shape* s, const GemmArgs& a, const Comb
 #define MOE_DC_SS(XT, N) \
     do { if (SS == 4) MOE_DC(XT, N, 4); else if (SS == 2) MOE_DC(XT, N, 2); else MOE_DC(XT, N, 1); } while (0)
     if (bf) {
-        if (NT == 2) MOE_DC_SS(uint16_t, 2);
+        if (NT == 1) MOE_DC_SS(uint16_t, 1);
+        else if (NT == 2) MOE_DC_SS(uint16_t, 2);
         else MOE_DC_SS(uint16_t, 4);
     } else {
-        if (NT == 2) MOE_DC_SS(float, 2);
+        if (NT == 1) MOE_DC_SS(float, 1);
+        else if (NT == 2) MOE_DC_SS(float, 2);
         else MOE_DC_SS(float, 4);
     }
 #undef MOE_DC_SS

@@ -157,6 +157,10 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
             }
         }
     }
+#pragma unroll
+    for (int f = 0; f < NA; ++f)
+#pragma unroll
+        for (int n = 0; n < NCF; ++n) mfma_results_here(acc[f][n]);
     // K quarters summed through LDS in wave order
     __shared__ float red[3][NA * NCF * 4][64];
     if (wave > 0) {
@@ -349,6 +353,10 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
         if (st + 1 < nsteps) store_step(buf ^ 1);
         __syncthreads();
     }
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int n = 0; n < NCF; ++n) mfma_results_here(acc[f][n]);
     if constexpr (NT == 2) {
 #pragma unroll
         for (int f = 0; f < 4; ++f)
@@ -484,6 +492,7 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
         }
     }
     // 5. K quarters summed in quarter order by wave 0, then the epilogue
+    mfma_results_here(acc);
     part[wave][lane] = acc;
     __syncthreads();
     if (wave != 0) return;

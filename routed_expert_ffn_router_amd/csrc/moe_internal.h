@@ -69,12 +69,23 @@ __device__ __forceinline__ float max_xor32(float m) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// sum over lanes l and l ^ 1 (and l ^ 2 for NT = 4): the NT adjacent columns of one token
+// sum over lanes l and l ^ 1 (and l ^ 2 for NT = 4): the NT adjacent columns of one token (NT = 1:
+// the column itself)
 template <int NT>
 __device__ __forceinline__ float sum_adjacent(float v) {
-    v += __uint_as_float(dpp_u32<kDppXor1, 0xF>(0u, __float_as_uint(v)));
+    if constexpr (NT >= 2) v += __uint_as_float(dpp_u32<kDppXor1, 0xF>(0u, __float_as_uint(v)));
     if constexpr (NT == 4) v += __uint_as_float(dpp_u32<kDppXor2, 0xF>(0u, __float_as_uint(v)));
     return v;
+}
+
+// A matrix-core instruction reads its operands from all 64 lanes.  When its result is used only
+// inside a lane-dependent branch (a store by the lanes that hold valid columns), the compiler may
+// sink the MFMAs into that branch, where they run with the other lanes switched off and take no
+// operands from them.  Consuming each accumulator here, in every lane and outside any such
+// branch, keeps them in front of it.  (No instruction is emitted.)
+template <typename V>
+__device__ __forceinline__ void mfma_results_here(const V& acc) {
+    asm volatile("" ::"v"(acc));
 }
 
 // loads through global-address-space pointers: global_load rather than flat_load (pointers read

@@ -999,9 +999,16 @@ hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipSt
             else MOE_LAUNCH((k_route_small<XT, N, 16, 4, 1>), grid, dim3(256), 0, st, a);               \
         }                                                                                                \
     } while (0)
-    // activation terms: 2 for bf16 activations, 4 for fp32 (act_terms)
-    if (bf) MOE_RS(uint16_t, 2);
-    else MOE_RS(float, 4);
+    // activation terms (act_terms): 1 in the MXFP8 mode, else 2 for bf16 activations, 4 for fp32
+    const int nt = act_terms(s);
+    if (nt == 1) {
+        if (bf) MOE_RS(uint16_t, 1);
+        else MOE_RS(float, 1);
+    } else if (bf) {
+        MOE_RS(uint16_t, 2);
+    } else {
+        MOE_RS(float, 4);
+    }
 #undef MOE_RS
     trace("route_small", 1, st);
     return hipGetLastError();
@@ -1058,8 +1065,10 @@ hipError_t launch_act_split(const moe_shape* s, const void* x, int rows, int K, 
     const bool bf = s->act_dtype == MOE_DT_BF16;
 #define MOE_SPLIT(XT, N)                                                                    \
     MOE_LAUNCH((k_act_split<XT, N>), grid, dim3(256), 0, st, (const XT*)x, rows, K, SS, q, sc)
-    if (bf && NT == 2) MOE_SPLIT(uint16_t, 2);
+    if (bf && NT == 1) MOE_SPLIT(uint16_t, 1);
+    else if (bf && NT == 2) MOE_SPLIT(uint16_t, 2);
     else if (bf && NT == 4) MOE_SPLIT(uint16_t, 4);
+    else if (!bf && NT == 1) MOE_SPLIT(float, 1);
     else if (!bf && NT == 2) MOE_SPLIT(float, 2);
     else MOE_SPLIT(float, 4);
 #undef MOE_SPLIT

@@ -55,6 +55,7 @@ class Workload:
     routed_scaling: float = 1.0
     renorm_skip: float = 0.0
     n_shared: int = 0        # 1: one more expert blob (index n_experts), the shared expert
+    act_quant: int = 0       # 1: the layer's opt-in MXFP8 activation mode
 
     @property
     def torch_act_dtype(self):

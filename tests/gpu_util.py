@@ -16,13 +16,19 @@ def rel_l2(a, b) -> float:
 
 
 def tol(wl) -> float:
-    """Parity tolerance on rel-L2 of the layer output: 1e-4 for fp32, 8e-3 for bf16 output."""
+    """Parity tolerance on rel-L2 of the layer output: 1e-4 for fp32, 8e-3 for bf16 output.  In the
+    opt-in MXFP8 activation mode (compared with the oracle's mirrored mode) fp32 output gets 1e-3:
+    both sides quantise x identically, but h is quantised from fp32 sums on the GPU and fp64 sums in
+    the oracle, and an h value that lands within their difference of an E4M3 rounding midpoint
+    takes the neighbouring code (one step, at most 1/16 of that value)."""
+    if wl.act_quant:
+        return 1e-3 if wl.act_dtype == synth.F32 else 8e-3
     return 1e-4 if wl.act_dtype == synth.F32 else 8e-3
 
 
 def shape_of(m, wl):
     return m.make_shape(wl.d_model, wl.d_ff, wl.n_experts, wl.top_k, wl.wformat, wl.act_dtype,
-                        wl.routed_scaling, wl.renorm_skip, wl.n_shared)
+                        wl.routed_scaling, wl.renorm_skip, wl.n_shared, wl.act_quant)
 
 
 class DeviceLayer:
@@ -78,7 +84,7 @@ def oracle_layer(dl, x, idx_hint=None, residual=None, scaling=None):
     return oracle.layer(x64, dl.router.cpu().numpy(), None if dl.bias is None else dl.bias.cpu().numpy(),
                         blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat,
                         wl.routed_scaling if scaling is None else scaling, res, wl.renorm_skip,
-                        dl.shared_blob())
+                        dl.shared_blob(), wl.act_quant)
 
 
 def small(name="tiny", **kw):
