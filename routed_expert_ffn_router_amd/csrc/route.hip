@@ -516,7 +516,9 @@ __device__ __forceinline__ unsigned long long dummy_key(int e) {
 // chunks per lane of a wave's part (d / (4 / RW) <= 256 NC, d a multiple of 8).  Every load is
 // issued without a condition (reads past the part re-read its last four elements and are not
 // used), so that no branch separates them and all of a wave's loads are in flight together.
-template <typename XT, int NT, int S, int NC, int RW>
+// PLAIN: no renorm-skip and no shared expert, known at compile time, so that the one-token tail (a
+// chain of dependent steps, each worth tens of nanoseconds) carries none of their bookkeeping.
+template <typename XT, int NT, int S, int NC, int RW, bool PLAIN>
 __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     const XT* __restrict__ x = (const XT*)a.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
@@ -586,17 +588,26 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     __shared__ uint4 s_cand[4][128];                // top-k candidates, per wave
     __shared__ unsigned long long s_rk[4][8];       // keys of the picks in rank order, per wave
     const int P = T * k, tt = a.tt;
+    const float tau = PLAIN ? 0.0f : a.tau;        // renorm-skip threshold
+    const int shared = PLAIN ? 0 : a.shared;       // a shared expert (table entry E)
     // for E <= kTabLds the whole expert table is kept in LDS
     constexpr int kTabLds = 320, kTabRounds = (kTabLds * 4 + 255) / 256;
     constexpr bool tab_lds = S <= 5;
     __shared__ uint4 s_tab[tab_lds ? kTabLds * 4 : 1];
     // the expert-table entry of expert e into a tile record: four 16-byte moves, from the LDS copy
     // of the table when there is one
+    // (the shared expert, entry E, always from memory; the LDS copy holds the routed experts.  Two
+    // branches, so that the LDS path stays LDS loads rather than generic ones)
     auto put_expert = [&](TileDesc* D, int e) {
-        const uint4* src = (tab_lds && e < E) ? &s_tab[4 * e] : (const uint4*)(a.table + e);   // shared: E
         uint4* dst = (uint4*)&D->ex;
+        if (tab_lds && e < E) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = src[i];
+            for (int i = 0; i < 4; ++i) dst[i] = s_tab[4 * e + i];
+        } else {
+            const uint4* src = (const uint4*)(a.table + e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = src[i];
+        }
     };
     // an empty record still names a real expert (the first pick's, or expert 0), so that a stray
     // read of its pointers stays inside the weights
@@ -610,7 +621,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     // the shared expert's tiles (table entry E): tokens c tt .. of tile c, at sorted positions
     // P + c tt .., record ids first, first + 1, ...; nothing without a shared expert
     auto put_shared = [&](TileDesc* desc, int32_t* tiles, int first, int thread, int nthreads) {
-        const int tt = a.tt, nsh = a.shared ? (T + tt - 1) / tt : 0;
+        const int tt = a.tt, nsh = shared ? (T + tt - 1) / tt : 0;
         for (int c = thread; c < nsh; c += nthreads) {
             TileDesc* D = desc + first + c;
             const int ntok = min(tt, T - c * tt);
@@ -639,10 +650,10 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         for (int id = tid; id < a.max_tiles; id += 256) put_empty(desc, id, 0);
         if (tid == 0) *ntiles = 0;
     };
-    // status word and poll limit, written only by earlier launches
-    const uint32_t st0 = sload(&a.hdr[0]);
-    const int plim = (int)sload(&a.hdr[1]);
-    const int poll_limit = plim == 0 ? kPollLimitDefault : plim;     // < 0: no polls
+    // the status word and the poll limit (< 0: no polls), written only by earlier launches.  Vector
+    // loads, issued next to the first poll of the slots so that they cost no wait of their own (a
+    // scalar load in flight would make every LDS wait of the tail wait for it too)
+    auto poll_limit_of = [](uint32_t plim) { return plim == 0u ? kPollLimitDefault : (int)plim; };
     __shared__ int s_fail[4];                                           // per wave: its wait gave up
 
     if (T == 1 && tab_lds) {
@@ -686,44 +697,46 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             if (wave == 0) {
                 if (live) {
                     // poll the slots (lane l: experts l + 64 s) until none is zero, at most
-                    // poll_limit times; none at all on a workspace whose status is already set
+                    // poll_limit times; none at all on a workspace whose status is already set.
+                    // The reads of a round are all issued before its tests.
+                    const uint32_t st0 = gload4(&a.hdr[0]);
+                    const int poll_limit = poll_limit_of(gload4(&a.hdr[1]));
                     bool got = false;
-                    if (st0 == 0u) {
-                        for (int it = 0; it < poll_limit; ++it) {
-                            bool miss = false;
+                    for (int it = 0;; ++it) {
+                        bool miss = false;
 #pragma unroll
-                            for (int s = 0; s < S; ++s) {
-                                const unsigned long long v = get_slot(a.slots + min(lane + 64 * s, E - 1));
-                                kv[s] = ~v;
-                                miss |= (lane + 64 * s < E) & (v == 0ull);
-                            }
-                            if (__ballot(miss) == 0ull) {
-                                got = true;
-                                break;
-                            }
+                        for (int s = 0; s < S; ++s) {
+                            const unsigned long long v = get_slot(a.slots + min(lane + 64 * s, E - 1));
+                            kv[s] = ~v;
+                            miss |= (lane + 64 * s < E) & (v == 0ull);
+                        }
+                        if ((st0 != 0u) | (it >= poll_limit)) break;
+                        if (__ballot(miss) == 0ull) {
+                            got = true;
+                            break;
                         }
                     }
-                    if (lane == 0) {
-                        s_fail[0] = got ? 0 : 1;
-                        if (!got && st0 == 0u) report_timeout(a.hdr);
+                    if (!got) {
+                        // the pass still runs, on the stand-in keys, and its outputs are then
+                        // replaced by a refusal (a test here, not after the barrier, keeps the
+                        // common path free of it)
+#pragma unroll
+                        for (int s = 0; s < S; ++s) kv[s] = dummy_key(lane + 64 * s);
+                        if (lane == 0 && st0 == 0u) report_timeout(a.hdr);
                     }
+                    if (lane == 0) s_fail[0] = got ? 0 : 1;
                 } else {
                     // a branch of its own (the asm keeps it one), so that the warm-up pass does
                     // not wait for the poll in flight
                     asm volatile("" ::: "memory");
 #pragma unroll
                     for (int s = 0; s < S; ++s) kv[s] = dummy_key(lane + 64 * s);
-                    if (lane == 0) s_fail[0] = 0;
                 }
 #pragma unroll
                 for (int s = 0; s < S; ++s)
                     if (lane + 64 * s < E) s_key[lane + 64 * s] = kv[s];
             }
             lds_barrier();
-            if (s_fail[0]) {               // live pass only: nothing was routed
-                put_refused(desc, idx, wout, pick_pos, sorted_pick, offsets, ntiles);
-                return;
-            }
             if (wave == 0) {
                 unsigned long long my_key = 0ull;
                 if (k > 8 || !topk_pass<S>(kv, E, k, s_idx, s_cand[0], s_rk[0], my_key))
@@ -739,11 +752,11 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             // those not dropped (rank 0 and every pick whose fp64 weight is not below tau)
             unsigned long long km = k >= 64 ? ~0ull : ((1ull << k) - 1ull);
             double sg = 0.0, ssum = 0.0;
-            if (wave == 1 || a.tau > 0.0f) {        // (wave 1 always: it writes the weights)
+            if (wave == 1 || tau > 0.0f) {        // (wave 1 always: it writes the weights)
                 if (lane < k) sg = s_sig[s_idx[lane]];
                 for (int j = 0; j < k; ++j) ssum += readlane_f64(sg, j);
             }
-            if (a.tau > 0.0f) km = __ballot(lane < k && !(lane > 0 && sg / ssum < (double)a.tau));
+            if (tau > 0.0f) km = __ballot(lane < k && !(lane > 0 && sg / ssum < (double)tau));
             const int nkept = __popcll(km);
             if (wave == 0) {
                 // the records: the token's kept experts are distinct, so kept pick p is a tile of
@@ -753,7 +766,8 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 const int e = p < k ? s_idx[p] : 0;
                 const bool kept = (km >> p) & 1ull;
                 int pos = 0;
-                for (int q = 0; q < k; ++q) pos += ((km >> q) & 1ull) && __builtin_amdgcn_readlane(e, q) < e;
+                // (bitwise tests, not &&: no branch may separate the reads, so they go out together)
+                for (int q = 0; q < k; ++q) pos += (int)(PLAIN ? 1ull : (km >> q) & 1ull) & (int)(__builtin_amdgcn_readlane(e, q) < e);
                 if (kept) {
                     TileDesc* D = desc + pos;
                     put_expert(D, e);
@@ -789,14 +803,21 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 for (int e = tid - 128; e <= E; e += 128) {
                     int lower = 0;
 #pragma unroll 8
-                    for (int q = 0; q < k; ++q) lower += ((km >> q) & 1ull) && s_idx[q] < e;
+                    for (int q = 0; q < k; ++q) lower += (int)(PLAIN ? 1ull : (km >> q) & 1ull) & (int)(s_idx[q] < e);
                     offsets[e] = lower;
                 }
-                const int nall = nkept + (a.shared ? 1 : 0);      // one token: one shared tile
+                const int nall = nkept + (shared ? 1 : 0);      // one token: one shared tile
                 for (int id = nall + tid - 128; id < a.max_tiles; id += 128) put_empty(desc, id, s_idx[0]);
                 if (tid == 128) *ntiles = nall;
             }
             lds_barrier();      // the real pass rewrites what this one read from LDS
+        }
+        if (s_fail[0]) {
+            // the wait gave up: what the real pass wrote is replaced by a refusal, once every
+            // store of it has landed
+            __threadfence();
+            __syncthreads();
+            put_refused(a.desc, a.idx, a.w, a.pick_pos, a.sorted_pick, a.offsets, a.ntiles);
         }
         return;
     }
@@ -818,6 +839,8 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     // Every poll load is issued without a condition (indices past T or E re-read the last slot
     // and are not used), so that all of them are in flight together.
     constexpr int J = tab_lds ? kSmallT / 4 : 1;
+    const uint32_t st0 = gload4(&a.hdr[0]);
+    const int poll_limit = poll_limit_of(gload4(&a.hdr[1]));
     bool gave_up = st0 != 0u;      // a workspace whose status is set is not routed on
     for (int t0 = wave; t0 < T && !gave_up; t0 += 4 * J) {
         unsigned long long kv[J][S];
@@ -857,7 +880,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 unsigned long long my_key = 0ull;
                 if (k > 8 || !topk_pass<S>(kv[j], E, k, s_idx + t * k, s_cand[wave], s_rk[wave], my_key))
                     my_key = topk_rounds<S>(kv[j], E, k, s_idx + t * k);
-                topk_weights(my_key, nullptr, s_idx + t * k, k, s_w + t * k, nullptr, a.tau);
+                topk_weights(my_key, nullptr, s_idx + t * k, k, s_w + t * k, nullptr, tau);
             }
         }
     }
@@ -879,7 +902,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     };
     // kept picks (P unless renorm-skip dropped some: they are no expert's and take no position)
     int Pv = P;
-    if (a.tau > 0.0f) {
+    if (tau > 0.0f) {
         Pv = 0;
 #pragma unroll 8
         for (int q = 0; q < P; ++q) Pv += s_idx[q] >= 0;
@@ -989,15 +1012,21 @@ hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipSt
     dim3 grid(s->n_experts + 1);
     const bool bf = s->act_dtype == MOE_DT_BF16;
     const bool lng = s->d_model > 4096;
-#define MOE_RS(XT, N)                                                                                    \
+    const bool plain = s->renorm_skip == 0.0f && s->n_shared == 0;
+#define MOE_RS_P(XT, N, PL)                                                                              \
     do {                                                                                                 \
         if (s->n_experts <= 320) {                                                                       \
-            if (lng) MOE_LAUNCH((k_route_small<XT, N, 5, 8, 1>), grid, dim3(256), 0, st, a);            \
-            else MOE_LAUNCH((k_route_small<XT, N, 5, 4, 1>), grid, dim3(256), 0, st, a);                \
+            if (lng) MOE_LAUNCH((k_route_small<XT, N, 5, 8, 1, PL>), grid, dim3(256), 0, st, a);        \
+            else MOE_LAUNCH((k_route_small<XT, N, 5, 4, 1, PL>), grid, dim3(256), 0, st, a);            \
         } else {                                                                                         \
-            if (lng) MOE_LAUNCH((k_route_small<XT, N, 16, 8, 1>), grid, dim3(256), 0, st, a);           \
-            else MOE_LAUNCH((k_route_small<XT, N, 16, 4, 1>), grid, dim3(256), 0, st, a);               \
+            if (lng) MOE_LAUNCH((k_route_small<XT, N, 16, 8, 1, PL>), grid, dim3(256), 0, st, a);       \
+            else MOE_LAUNCH((k_route_small<XT, N, 16, 4, 1, PL>), grid, dim3(256), 0, st, a);           \
         }                                                                                                \
+    } while (0)
+#define MOE_RS(XT, N)                                                                                    \
+    do {                                                                                                 \
+        if (plain) MOE_RS_P(XT, N, true);                                                                \
+        else MOE_RS_P(XT, N, false);                                                                     \
     } while (0)
     // activation terms (act_terms): 1 in the MXFP8 mode, else 2 for bf16 activations, 4 for fp32
     const int nt = act_terms(s);
@@ -1010,6 +1039,7 @@ hipError_t launch_route_small(const moe_shape* s, const RouteSmallArgs& a, hipSt
         MOE_RS(float, 4);
     }
 #undef MOE_RS
+#undef MOE_RS_P
     trace("route_small", 1, st);
     return hipGetLastError();
 }
