@@ -187,23 +187,26 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def oracle_check(oracle, np, torch, wl, blob_of, router, bias, x, y, idx, tokens=None):
+def oracle_check(oracle, np, torch, wl, blob_of, router, bias, x, y, idx, tokens=None, shared_blob=None):
     """Parity of one layer call against the oracle: router indices of every token bit-exact,
     rel-L2 of y (computed without a residual) on `tokens` (all when None).  blob_of(e) returns
-    expert e's blob as a host array.  Returns (exact, rel_l2, oracle seconds)."""
+    expert e's blob as a host array; the workload's renorm_skip, act_quant and routed_scaling (and
+    the shared expert's blob, if any) are the layer's.  Returns (exact, rel_l2, oracle seconds)."""
     x64 = oracle.to_f64(x)
     wr = router.cpu().numpy()
     b = None if bias is None else bias.cpu().numpy()
     gidx = idx.cpu().numpy()
     t0 = time.perf_counter()
-    _, oidx, _ = oracle.route(x64, wr, b, wl.top_k)
+    _, oidx, _ = oracle.route(x64, wr, b, wl.top_k, wl.renorm_skip)
     exact = bool(np.array_equal(oidx, gidx))
     sel = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
     blobs = [None] * wl.n_experts
     for e in np.unique(oidx[sel].reshape(-1)):
-        blobs[int(e)] = blob_of(int(e))
+        if e >= 0:
+            blobs[int(e)] = blob_of(int(e))
     xs = np.ascontiguousarray(x64[sel])
-    oy, _, _, _ = oracle.layer(xs, wr, b, blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat, wl.routed_scaling, None)
+    oy, _, _, _ = oracle.layer(xs, wr, b, blobs, wl.d_model, wl.d_ff, wl.top_k, wl.wformat, wl.routed_scaling, None,
+                               wl.renorm_skip, shared_blob, wl.act_quant)
     secs = time.perf_counter() - t0
     err = rel_l2(oracle.to_f64(y)[sel], oy)
     return exact, err, secs
@@ -235,6 +238,197 @@ def host_info():
     return info
 
 
+def expert_entry(m, synth, wl, ptr):
+    """The 64-byte moe_expert record of a blob at device address ptr (host bytes)."""
+    off = synth.blob_offsets(wl.d_model, wl.d_ff, wl.wformat)
+    e = m.moe_expert()
+    for f in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s"):
+        setattr(e, f, ptr + off[f][0])
+    e.gate_ts = e.up_ts = e.down_ts = 1.0
+    return bytes(e)
+
+
+def time_graph(hip, S, step, reps, warm=3):
+    """Capture step() on stream S as one graph; returns (ms per replay, graph)."""
+    gexec, _ = hip.capture(S, step)
+    for _ in range(warm):
+        hip.launch(gexec, S)
+    hip.sync(S)
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, S)
+    for _ in range(reps):
+        hip.launch(gexec, S)
+    hip.record(e1, S)
+    return hip.elapsed_ms(e0, e1) / reps, gexec
+
+
+def time_calls(hip, S, call, reps, warm=2):
+    for _ in range(warm):
+        call()
+    hip.sync(S)
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, S)
+    for _ in range(reps):
+        call()
+    hip.record(e1, S)
+    return hip.elapsed_ms(e0, e1) / reps
+
+
+def rows_legs(args, m, synth, torch, np, hip, stream, S, stack, oracle, parity, log):
+    """The layer's optional parts, each timed on the decode stack's weights and checked against the
+    oracle in the same run: the shared expert with routed_scaling 2.5 (42-layer decode graph),
+    renorm-skip (42-layer decode graph under low-confidence routing, against the same routing
+    unskipped), the opt-in MXFP8 activations (the 4096-token chunk), and chunks of 16 to 2048
+    tokens between the decode and prefill paths."""
+    import dataclasses
+    wl0 = synth.WORKLOADS["decode"]
+    nl, E, d = stack.n, wl0.n_experts, wl0.d_model
+    rec = {}
+    steps = max(5, args.steps // 2)
+    xs = [synth.make_x(wl0, args.seed, "cuda", tokens=1, tag=f"x_rows_{l}") for l in range(nl)]
+    bufs = [torch.empty_like(xs[0]), torch.empty_like(xs[0])]
+    stride = stack.blob.shape[2]
+
+    # -- shared expert (routed_scaling 2.5): table of E + 1 entries, the last a blob of its own --
+    wl_sh = dataclasses.replace(wl0, n_shared=1, routed_scaling=2.5)
+    sh_shape = m.make_shape(d, wl0.d_ff, E, wl0.top_k, wl0.wformat, wl0.act_dtype, 2.5, 0.0, 1)
+    sh_blob = torch.empty(nl, 1, stride, dtype=torch.uint8, device="cuda")
+    sh_table = torch.empty(nl, (E + 1) * m.EXPERT_BYTES, dtype=torch.uint8, device="cuda")
+    tmp = torch.zeros(E + 1, stride, dtype=torch.uint8, device="cuda")   # fill_experts addresses blob E
+    for l in range(nl):
+        synth.fill_experts(tmp, wl_sh, l, args.seed, experts=[E])
+        sh_blob[l, 0] = tmp[E]
+        sh_table[l, :E * m.EXPERT_BYTES] = stack.table[l]
+        ent = torch.frombuffer(bytearray(expert_entry(m, synth, wl0, sh_blob[l, 0].data_ptr())), dtype=torch.uint8)
+        sh_table[l, E * m.EXPERT_BYTES:] = ent.cuda()
+    del tmp
+    ws = m.workspace(sh_shape, 1)
+    torch.cuda.synchronize()
+
+    def sh_step(observer=None):
+        for l in range(nl):
+            m.moe_layer(sh_shape, xs[l], 1, stack.router[l], None, sh_table[l], None, xs[l], bufs[l % 2], None, None,
+                        ws, stream=S, observer=observer)
+    ms, _ = time_graph(hip, S, sh_step, steps)
+    per = kernel_times(hip, m, S, sh_step, reps=2)
+    lb = 9 * m.moe_blob_stride(stack.shape) + E * d * 4 + 4 * d
+    rec["shared_expert"] = {"workload": "decode stack + one shared expert per layer, routed_scaling 2.5, T=1",
+                            "us_per_layer": 1000 * ms / nl, "layer_tokens_per_s": nl / (ms * 1e-3),
+                            "hbm_frac_layer": lb / (ms * 1e-3 / nl) / (HBM_PEAK_GBS * 1e9),
+                            "kernels_us": {k: float(np.mean(v)) for k, v in per.items()}}
+    log(f"# shared expert: {1000 * ms / nl:.2f} us/layer ({100 * rec['shared_expert']['hbm_frac_layer']:.1f}% of HBM "
+        f"on 9 experts/layer)")
+    if oracle is not None:
+        y0 = torch.empty_like(xs[0])
+        i0 = torch.empty(1, wl0.top_k, dtype=torch.int32, device="cuda")
+        errs, ok = [], True
+        for l in (0, nl - 1):
+            with torch.cuda.stream(stream):
+                m.moe_layer(sh_shape, xs[l], 1, stack.router[l], None, sh_table[l], None, None, y0, i0, None, ws,
+                            stream=S)
+            hip.sync(S)
+            exact, err, _ = oracle_check(oracle, np, torch, wl_sh, lambda e, l=l: stack.blob[l, e].cpu().numpy(),
+                                         stack.router[l], None, xs[l], y0, i0, None,
+                                         shared_blob=sh_blob[l, 0].cpu().numpy())
+            ok = ok and exact
+            errs.append(err)
+        parity["shared_expert"] = parity_entry(wl_sh, ok, max(errs), f"layers 0 and {nl - 1}, the token")
+    del sh_blob, sh_table
+
+    # -- renorm-skip: low-confidence routing (logit bias -2.5 puts the top picks near 0, where the
+    #    sigmoid weights spread), threshold 0.11, against the same routing without the skip --
+    bias = torch.full((E,), -2.5, dtype=torch.float32, device="cuda")
+    wl_rs = dataclasses.replace(wl0, renorm_skip=0.11)
+    res = {}
+    for tau in (0.0, 0.11):
+        sh = m.make_shape(d, wl0.d_ff, E, wl0.top_k, wl0.wformat, wl0.act_dtype, 1.0, tau)
+        ws = m.workspace(sh, 1)
+        idx = torch.empty(nl, 1, wl0.top_k, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+
+        def rs_step(observer=None, sh=sh, ws=ws, idx=idx):
+            for l in range(nl):
+                m.moe_layer(sh, xs[l], 1, stack.router[l], bias, stack.table[l], None, xs[l], bufs[l % 2], idx[l],
+                            None, ws, stream=S, observer=observer)
+        ms, _ = time_graph(hip, S, rs_step, steps)
+        kept = float((idx >= 0).sum().item()) / nl
+        res[tau] = {"us_per_layer": 1000 * ms / nl, "experts_per_layer": kept}
+        if oracle is not None and tau > 0:
+            y0 = torch.empty_like(xs[0])
+            i0 = torch.empty(1, wl0.top_k, dtype=torch.int32, device="cuda")
+            with torch.cuda.stream(stream):
+                m.moe_layer(sh, xs[0], 1, stack.router[0], bias, stack.table[0], None, None, y0, i0, None, ws,
+                            stream=S)
+            hip.sync(S)
+            exact, err, _ = oracle_check(oracle, np, torch, wl_rs, lambda e: stack.blob[0, e].cpu().numpy(),
+                                         stack.router[0], bias, xs[0], y0, i0)
+            parity["renorm_skip"] = parity_entry(wl_rs, exact, err, "layer 0, the token")
+    rec["renorm_skip"] = {"workload": "decode stack, logit bias -2.5 (low-confidence routing), threshold 0.11",
+                          "skip": res[0.11], "no_skip": res[0.0],
+                          "speedup": res[0.0]["us_per_layer"] / res[0.11]["us_per_layer"]}
+    log(f"# renorm-skip: {res[0.11]['us_per_layer']:.2f} us/layer with {res[0.11]['experts_per_layer']:.2f} experts "
+        f"against {res[0.0]['us_per_layer']:.2f} us with 8")
+
+    # -- opt-in MXFP8 activations, the 4096-token chunk --
+    wl_aq = dataclasses.replace(synth.WORKLOADS["prefill"], act_quant=1)
+    aq_shape = m.make_shape(d, wl0.d_ff, E, wl0.top_k, wl0.wformat, wl0.act_dtype, 1.0, 0.0, 0, 1)
+    T = 4096
+    x = synth.make_x(wl_aq, args.seed, "cuda", tokens=T, tag="x_prefill")
+    y = torch.empty_like(x)
+    idx = torch.empty(T, wl0.top_k, dtype=torch.int32, device="cuda")
+    ws = m.workspace(aq_shape, T)
+    torch.cuda.synchronize()
+    call = lambda observer=None: m.moe_layer(aq_shape, x, T, stack.router[0], None, stack.table[0], None, None, y, idx,
+                                             None, ws, stream=S, observer=observer)
+    ms = time_calls(hip, S, call, max(3, steps // 3))
+    per = kernel_times(hip, m, S, call, reps=2)
+    flops = 2.0 * 3 * d * wl0.d_ff * T * wl0.top_k
+    rec["mxfp8_activations"] = {"workload": "prefill chunk T=4096, opt-in MXFP8 activations (one E4M3 term)",
+                                "ms_per_layer": ms, "tokens_per_s": T / (ms * 1e-3),
+                                "fp4_mfma_frac": flops / (ms * 1e-3) / (FP4_PEAK_TFLOPS * 1e12),
+                                "kernels_us": {k: float(np.mean(v)) for k, v in per.items()}}
+    log(f"# MXFP8 activations, prefill T=4096: {ms:.3f} ms/layer; kernels (us): "
+        + ", ".join(f"{k} {v:.1f}" for k, v in rec["mxfp8_activations"]["kernels_us"].items()))
+    if oracle is not None:
+        sample = [0, 2047, 4095]
+        exact, err, _ = oracle_check(oracle, np, torch, wl_aq, lambda e: stack.blob[0, e].cpu().numpy(),
+                                     stack.router[0], None, x, y, idx, sample)
+        parity["mxfp8_activations"] = parity_entry(wl_aq, exact, err, f"T=4096, against the oracle's mirrored mode, "
+                                                   f"y of tokens {sample}")
+    del x, y, ws
+
+    # -- chunks between decode and prefill (layer 0) --
+    wl_p = synth.WORKLOADS["prefill"]
+    Tmax = 2048
+    ws = m.workspace(stack.shape, Tmax)
+    mid = {}
+    worst, exact_all = 0.0, True
+    for T in (16, 32, 48, 64, 128, 256, 512, 1024, 2048):
+        x = synth.make_x(wl_p, args.seed, "cuda", tokens=T, tag=f"x_mid{T}")
+        y = torch.empty_like(x)
+        idx = torch.empty(T, wl0.top_k, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        call = lambda observer=None: m.moe_layer(stack.shape, x, T, stack.router[0], None, stack.table[0], None, None,
+                                                 y, idx, None, ws, stream=S, observer=observer)
+        ms = time_calls(hip, S, call, max(5, steps // 2))
+        touched = len(np.unique(idx.cpu().numpy()))
+        b = algorithmic_layer_bytes(wl_p, touched, T)
+        mid[str(T)] = {"ms_per_layer": ms, "tokens_per_s": T / (ms * 1e-3), "experts": touched,
+                       "hbm_frac": b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+        if oracle is not None:
+            exact, err, _ = oracle_check(oracle, np, torch, wl_p, lambda e: stack.blob[0, e].cpu().numpy(),
+                                         stack.router[0], None, x, y, idx, [0, T - 1])
+            exact_all = exact_all and exact
+            worst = err if err != err else max(worst, err)
+    rec["mid_chunks"] = mid
+    log("# chunks: " + ", ".join(f"T={t}: {r['ms_per_layer'] * 1000:.0f} us ({r['tokens_per_s'] / 1e3:.0f}k tok/s, "
+                                 f"{100 * r['hbm_frac']:.0f}% HBM)" for t, r in mid.items()))
+    if oracle is not None:
+        parity["mid_chunks"] = parity_entry(wl_p, exact_all, worst, "T=16..2048: indices of every token, y of the "
+                                            "first and last token")
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,7 +437,7 @@ def main():
     ap.add_argument("--layers", type=int, default=42)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--only", choices=["decode", "prefill", "batched", "nvfp4"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "batched", "nvfp4", "rows"], default=None)
     ap.add_argument("--nv-layers", type=int, default=8, help="NVFP4 decode stack depth")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -289,7 +483,7 @@ def main():
     wl_dec = synth.WORKLOADS["decode"]
     nl = args.layers
     stack = None
-    if want("decode") or want("batched") or want("prefill"):
+    if want("decode") or want("batched") or want("prefill") or want("rows"):
         log(f"# building the {nl}-layer decode stack in HBM")
         stack = Stack(m, synth, torch, wl_dec, nl, args.seed, log)
 
@@ -482,6 +676,11 @@ def main():
         out["nvfp4"] = rec
         del nst
 
+    # ---------------- the layer's optional parts and the mid-size chunks ----------------
+    if want("rows"):
+        out["rows"] = rows_legs(args, m, synth, torch, np, hip, stream, S, stack, oracle if check else None, parity,
+                                log)
+
     # ---------------- batched parity: layers 0 and 41, all 64 tokens ----------------
     if want("batched") and check:
         wl = synth.WORKLOADS["batched"]
@@ -594,7 +793,7 @@ def main():
                      "config": {"workload": first}})
     line["cpu_baseline"] = cpu
     line["parity"] = dict(parity, all_pass=all_pass) if parity else None
-    for k in ("prefill", "batched", "nvfp4"):
+    for k in ("prefill", "batched", "nvfp4", "rows"):
         if k in out:
             line[k] = {kk: vv for kk, vv in out[k].items()}
     failed = bool(parity) and not all_pass
