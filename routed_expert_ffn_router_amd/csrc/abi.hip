@@ -179,7 +179,7 @@ static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const 
     int32_t* ntiles = (int32_t*)(ws + L.ntiles);
     if (!planned) MOE_HIP(launch_plan(s, offsets, T, tt, tiles, ntiles, st));
     const bool bf = s->act_dtype == MOE_DT_BF16;
-    const int NT = bf ? 1 : 2;
+    const int NT = bf ? 1 : 2;      // bf16 terms of x and of h: one with bf16 activations, two with fp32
     if (!bf) MOE_HIP(launch_bf16_terms((const float*)x, T, s->d_model, (uint16_t*)(ws + L.xq), st));
     GemmArgs a = gemm_args(s, table, T, sorted_pick, offsets, ws, L, o);
     const uint8_t* xin = bf ? (const uint8_t*)x : ws + L.xq;
@@ -187,7 +187,7 @@ static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const 
         a.aq = xin;
         MOE_HIP(launch_nv_gemm(a, true, NT, tt, L.max_tiles, st));
         a.aq = ws + L.hq;
-        MOE_HIP(launch_nv_gemm(a, false, 2, tt, L.max_tiles, st));
+        MOE_HIP(launch_nv_gemm(a, false, NT, tt, L.max_tiles, st));
         return MOE_OK;
     }
     int32_t* list = (int32_t*)(ws + L.stage_list);
@@ -206,7 +206,7 @@ static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const 
         a.aq = xin;
         MOE_HIP(launch_nv_gemm(a, true, NT, tt, L.max_tiles, st));
         a.aq = ws + L.hq;
-        MOE_HIP(launch_nv_gemm(a, false, 2, tt, L.max_tiles, st));
+        MOE_HIP(launch_nv_gemm(a, false, NT, tt, L.max_tiles, st));
     }
     return MOE_OK;
 }

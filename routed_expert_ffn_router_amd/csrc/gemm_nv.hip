@@ -7,9 +7,10 @@
 // multiply applies the E4M3 block scale, and the product is rounded to bf16.  That product is
 // exact in bf16 (at most 2 + 4 significant bits), so the bf16 matrix cores
 // (V_MFMA_F32_16X16X32_BF16) see the weights exactly;
-// the tensor scale multiplies the fp32 accumulator.  Activations are the bf16 operand: bf16 x as
-// it is, an fp32 x or the SwiGLU output h as two bf16 terms (hi = bf16(v), lo = bf16(v - hi)),
-// each term one MFMA column.
+// the tensor scale multiplies the fp32 accumulator.  Activations are the bf16 operand, NT terms
+// of each value, each term one MFMA column: with bf16 activations x as it is and the SwiGLU output
+// h rounded to bf16 (NT = 1); with fp32 activations x and h as two bf16 terms (hi = bf16(v),
+// lo = bf16(v - hi)), which keep fp32-level accuracy (NT = 2).
 //
 // K order of one MFMA: lane l supplies 8 consecutive K of row (A) or column (B) l % 16; any
 // assignment of K to lane groups works when both operands share it (measured on gfx950).  Here a
@@ -58,6 +59,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) { return f32_to_bf16_bits(f); }
 
+// h value v of row `row` as NT bf16 terms of a pick's [NT][f] block: bf16(v), and with NT = 2 also
+// bf16(v - bf16(v))
+template <int NT>
+__device__ __forceinline__ void put_h_terms(uint16_t* hb, int f, int row, float v) {
+    const uint16_t hi = bf16_rne(v);
+    hb[row] = hi;
+    if constexpr (NT == 2) hb[f + row] = bf16_rne(v - bf16_bits_to_f32(hi));
+}
+
 // bf16 terms of fp32 activations: hi = bf16(v), lo = bf16(v - hi); layout [rows][2][K]
 __global__ __launch_bounds__(256) void k_bf16_terms(const float* __restrict__ x, size_t n, int K,
                                                    uint16_t* __restrict__ terms) {
@@ -81,7 +91,7 @@ hipError_t launch_bf16_terms(const float* x, int rows, int K, uint16_t* terms, h
 
 // NT: bf16 terms per activation (1: bf16 x read in place; 2: hi/lo terms); TTP: picks per tile
 // (MFMA columns = TTP * NT, in NCF 16-column fragments).  GATEUP: the gate and up rows of one
-// 32-row block, SwiGLU, and h as two bf16 terms; else the down rows, o in fp32.
+// 32-row block, SwiGLU, and h as NT bf16 terms; else the down rows, o in fp32.
 template <int NT, bool GATEUP, int TTP>
 __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
     constexpr int NA = GATEUP ? 4 : 2;      // 16-row fragments: gate lo/hi, up lo/hi (or down lo/hi)
@@ -195,20 +205,16 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
         if (tc >= ntok || t != 0) continue;
         const size_t pos = (size_t)i0 + tc;
         if constexpr (GATEUP) {
-            // h = silu(g) u for rows T0 + 4 lg + r (half 0) and T0 + 16 + 4 lg + r (half 1), as two
-            // bf16 terms [P][2][f]
-            uint16_t* hb = (uint16_t*)a.hq + pos * 2 * (size_t)a.f;
+            // h = silu(g) u for rows T0 + 4 lg + r (half 0) and T0 + 16 + 4 lg + r (half 1), as NT
+            // bf16 terms [P][NT][f]
+            uint16_t* hb = (uint16_t*)a.hq + pos * NT * (size_t)a.f;
 #pragma unroll
             for (int half = 0; half < 2; ++half)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float g = acc[half][n][r] * ex.gate_ts, u = acc[2 + half][n][r] * ex.up_ts;
-                    const float hv = g / (1.0f + __expf(-g)) * u;
-                    const uint16_t hi = bf16_rne(hv);
-                    const uint16_t lo = bf16_rne(hv - bf16_bits_to_f32(hi));
                     const int row = T0 + 16 * half + 4 * lg + r;
-                    hb[row] = hi;
-                    hb[a.f + row] = lo;
+                    put_h_terms<NT>(hb, a.f, row, g / (1.0f + __expf(-g)) * u);
                 }
         } else {
             float* dst = a.o + pos * (size_t)a.d + T0 + 4 * lg;
@@ -371,18 +377,14 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
         if (tc >= ntok || t != 0) continue;
         const size_t pos = (size_t)i0 + tc;
         if constexpr (GATEUP) {
-            uint16_t* hb = (uint16_t*)a.hq + pos * 2 * (size_t)a.f;
+            uint16_t* hb = (uint16_t*)a.hq + pos * NT * (size_t)a.f;
 #pragma unroll
             for (int half = 0; half < 2; ++half)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float gv = acc[half][n][r] * ex.gate_ts, uv = acc[2 + half][n][r] * ex.up_ts;
-                    const float hv = gv / (1.0f + __expf(-gv)) * uv;
-                    const uint16_t hi = bf16_rne(hv);
-                    const uint16_t lo = bf16_rne(hv - bf16_bits_to_f32(hi));
                     const int row = mblk * 64 + wm * 32 + 16 * half + 4 * lg + r;
-                    hb[row] = hi;
-                    hb[a.f + row] = lo;
+                    put_h_terms<NT>(hb, a.f, row, gv / (1.0f + __expf(-gv)) * uv);
                 }
         } else {
             float* dst = a.o + pos * (size_t)a.d + mblk * 128 + wm * 64 + 4 * lg;
@@ -511,17 +513,12 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
     if (tc >= ntok || t != 0) return;
     const size_t pos = (size_t)i0 + tc;
     if constexpr (GATEUP) {
-        // h = silu(g) u for rows T0 + 4 lg + r, as two bf16 terms [P][2][f]
-        uint16_t* hb = (uint16_t*)a.hq + pos * 2 * (size_t)a.f;
+        // h = silu(g) u for rows T0 + 4 lg + r, as NT bf16 terms [P][NT][f]
+        uint16_t* hb = (uint16_t*)a.hq + pos * NT * (size_t)a.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float g = r4[0][r] * ex.gate_ts, u = r4[1][r] * ex.up_ts;
-            const float hv = g / (1.0f + __expf(-g)) * u;
-            const uint16_t hi = bf16_rne(hv);
-            const uint16_t lo = bf16_rne(hv - bf16_bits_to_f32(hi));
-            const int rr = T0 + 4 * lg + r;
-            hb[rr] = hi;
-            hb[a.f + rr] = lo;
+            put_h_terms<NT>(hb, a.f, T0 + 4 * lg + r, g / (1.0f + __expf(-g)) * u);
         }
     } else {
 #pragma unroll
@@ -547,15 +544,15 @@ hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int tile_picks
         const int MT = gateup ? a.f / 64 : a.d / 128;
         const int cap = (max_tiles + 7) / 8;
         dim3 g2((unsigned)(8 * cap * MT));
-        if (!gateup) MOE_LAUNCH((k_nv_pf<2, false>), g2, dim3(256), 0, st, a, cap);
+        if (!gateup && NT == 1) MOE_LAUNCH((k_nv_pf<1, false>), g2, dim3(256), 0, st, a, cap);
+        else if (!gateup) MOE_LAUNCH((k_nv_pf<2, false>), g2, dim3(256), 0, st, a, cap);
         else if (NT == 1) MOE_LAUNCH((k_nv_pf<1, true>), g2, dim3(256), 0, st, a, cap);
         else MOE_LAUNCH((k_nv_pf<2, true>), g2, dim3(256), 0, st, a, cap);
     } else if ((gateup ? a.d : a.f) <= kNvDecMaxK) {
         // LDS columns: a tile holds at most one pick per token, so min(tile picks, T) * NT;
         // super-steps per K quarter: 4 (K <= 2048), 12 (K <= 6144) or 16
         const int K = gateup ? a.d : a.f;
-        const int NTk = gateup ? NT : 2;
-        const bool narrow = (long long)(a.P / a.k < kNvTilePicks ? a.P / a.k : kNvTilePicks) * NTk <= 2;
+        const bool narrow = (long long)(a.P / a.k < kNvTilePicks ? a.P / a.k : kNvTilePicks) * NT <= 2;
         const int nsw = K <= 2048 ? 4 : (K <= 6144 ? 12 : 16);
         dim3 g3(max_tiles, rows / (gateup ? 16 : 32));
 #define MOE_NVD(N, G, S, NC) MOE_LAUNCH((k_nv_dec<N, G, S, NC>), g3, dim3(512), 0, st, a)
@@ -570,14 +567,16 @@ hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int tile_picks
             if (narrow) MOE_NVD_S(N, G, 2);                                                 \
             else MOE_NVD_S(N, G, 2 * kNvTilePicks);                                         \
         } while (0)
-        if (!gateup) MOE_NVD2(2, false);
+        if (!gateup && NT == 1) MOE_NVD2(1, false);
+        else if (!gateup) MOE_NVD2(2, false);
         else if (NT == 1) MOE_NVD2(1, true);
         else MOE_NVD2(2, true);
 #undef MOE_NVD2
 #undef MOE_NVD_S
 #undef MOE_NVD
     } else {
-        if (!gateup) MOE_NV(2, false, kNvTilePicks);
+        if (!gateup && NT == 1) MOE_NV(1, false, kNvTilePicks);
+        else if (!gateup) MOE_NV(2, false, kNvTilePicks);
         else if (NT == 1) MOE_NV(1, true, kNvTilePicks);
         else MOE_NV(2, true, kNvTilePicks);
     }
