@@ -226,25 +226,25 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
     }
 }
 
-// Many picks per expert: an LDS-tiled version.  A workgroup (4 waves, 2 x 2) owns one tile of up
-// to kNvTilePicksMany picks (64 * NT columns) and 128 weight rows (gate/up: the same 64 row indices
+// Many picks per expert: an LDS-tiled version.  A workgroup (4 waves) owns one tile of up to
+// kNvTilePicksMany picks (64 * NT columns) and 128 weight rows (gate/up: the same 64 row indices
 // of gate and up).  K advances 128 at a time through double-buffered LDS: the global loads of step
-// s + 1 are in flight while step s computes.  Each wave decodes its four 16-row weight fragments
-// once per step (32 bf16 per lane each) and runs them against every column fragment of its half
-// of the tile.  Workgroups are spread over the 8 XCDs by tile range, row block fastest.
+// s + 1 are in flight while step s computes.  Each wave decodes its two 16-row weight fragments
+// once per step (32 bf16 per lane each) and runs them against every column fragment of the tile,
+// so that each decode feeds twice the MFMAs of a 2 x 2 split of the waves.  Workgroups are spread
+// over the 8 XCDs by tile range, row block fastest.
 constexpr int kNvPfRows = 128, kNvPfBStride = 272;   // bf16 column: 256 bytes per step + pad
 
 template <int NT, bool GATEUP>
 __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap) {
     constexpr int BN = kNvTilePicksMany * NT;       // columns of the tile
-    constexpr int NCF = BN / 32;                     // column fragments per wave (half the tile)
+    constexpr int NCF = BN / 16;                     // column fragments per wave (the whole tile)
     __shared__ __align__(16) uint8_t lA[2][kNvPfRows][64];
     __shared__ __align__(16) uint8_t lAs[2][kNvPfRows][8];
     __shared__ __align__(16) uint8_t lB[2][BN * kNvPfBStride];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
-    const int wm = wave & 1, wn = wave >> 1;
     const int K = GATEUP ? a.d : a.f;
     const int MT = GATEUP ? a.f / 64 : a.d / 128;
     int t_lo = 0, t_hi = *a.ntiles;
@@ -324,13 +324,15 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
         for (int i = 0; i < NBC; ++i) *(uint4*)(&lB[buf][0] + dstB[i]) = vB[i];
     };
 
-    int arow[4];
+    // wave w decodes two 16-row fragments (gate/up: rows 16 w .. of gate and of up; down: rows
+    // 32 w ..) once per step and runs them against every column fragment of the tile, so that a
+    // decoded fragment feeds 4 NCF MFMAs
+    int arow[2];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-        arow[f] = GATEUP ? ((f >> 1) * 64 + wm * 32 + (f & 1) * 16 + li) : (wm * 64 + f * 16 + li);
-    v4f_nv acc[4][NCF];
+    for (int f = 0; f < 2; ++f) arow[f] = GATEUP ? (f * 64 + wave * 16 + li) : (wave * 32 + f * 16 + li);
+    v4f_nv acc[2][NCF];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int n = 0; n < NCF; ++n) acc[f][n] = v4f_nv{0.f, 0.f, 0.f, 0.f};
     const int nsteps = K / 128;
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
         const int buf = st & 1;
         if (st + 1 < nsteps) load_step(st + 1);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
+        for (int f = 0; f < 2; ++f) {
             const uint4 codes = *(const uint4*)&lA[buf][arow[f]][lg * 16];
             const v2f_t bs = e4m3x2_to_f32(*(const uint16_t*)&lAs[buf][arow[f]][2 * lg]);
             const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
                 const bf16x8_t af = nv_dequant8(w[h], h < 2 ? bs[0] : bs[1]);
 #pragma unroll
                 for (int n = 0; n < NCF; ++n) {
-                    const int col = wn * (BN / 2) + n * 16 + li;
+                    const int col = n * 16 + li;
                     const uint4 bv = *(const uint4*)&lB[buf][col * kNvPfBStride + (lg * 32 + 8 * h) * 2];
                     acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, as_bf16x8(bv), acc[f][n], 0, 0, 0);
                 }
@@ -360,12 +362,12 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
         __syncthreads();
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int n = 0; n < NCF; ++n) mfma_results_here(acc[f][n]);
     if constexpr (NT == 2) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < 2; ++f)
 #pragma unroll
             for (int n = 0; n < NCF; ++n)
 #pragma unroll
@@ -373,23 +375,21 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
     }
 #pragma unroll
     for (int n = 0; n < NCF; ++n) {
-        const int c = wn * (BN / 2) + n * 16 + li, tc = c / NT, t = c % NT;
+        const int c = n * 16 + li, tc = c / NT, t = c % NT;
         if (tc >= ntok || t != 0) continue;
         const size_t pos = (size_t)i0 + tc;
         if constexpr (GATEUP) {
             uint16_t* hb = (uint16_t*)a.hq + pos * NT * (size_t)a.f;
 #pragma unroll
-            for (int half = 0; half < 2; ++half)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float gv = acc[half][n][r] * ex.gate_ts, uv = acc[2 + half][n][r] * ex.up_ts;
-                    const int row = mblk * 64 + wm * 32 + 16 * half + 4 * lg + r;
-                    put_h_terms<NT>(hb, a.f, row, gv / (1.0f + __expf(-gv)) * uv);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const float gv = acc[0][n][r] * ex.gate_ts, uv = acc[1][n][r] * ex.up_ts;
+                const int row = mblk * 64 + wave * 16 + 4 * lg + r;
+                put_h_terms<NT>(hb, a.f, row, gv / (1.0f + __expf(-gv)) * uv);
+            }
         } else {
-            float* dst = a.o + pos * (size_t)a.d + mblk * 128 + wm * 64 + 4 * lg;
+            float* dst = a.o + pos * (size_t)a.d + mblk * 128 + wave * 32 + 4 * lg;
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
+            for (int f = 0; f < 2; ++f)
                 *(float4*)(dst + 16 * f) = make_float4(acc[f][n][0] * ex.down_ts, acc[f][n][1] * ex.down_ts,
                                                        acc[f][n][2] * ex.down_ts, acc[f][n][3] * ex.down_ts);
         }
