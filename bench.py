@@ -159,8 +159,10 @@ def measured_traffic(kernel):
     rec = json.load(open(path)).get(kernel)
     if not rec:
         return None
-    src = os.path.join(ROOT, "routed_expert_ffn_router_amd", "csrc", rec["source"])
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    h = hashlib.sha256()
+    for name in rec["sources"]:         # the kernel's file and the header its helpers live in
+        h.update(open(os.path.join(ROOT, "routed_expert_ffn_router_amd", "csrc", name), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
         return None
     return rec["bytes_per_launch"]
 
