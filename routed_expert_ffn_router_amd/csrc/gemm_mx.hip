@@ -477,7 +477,9 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
 // down projection + weighted combine for few picks: workgroup = 16 output rows; its 16 waves
 // take (tile, K slice) units in turn (K slice = kDecKSlice of d_ff; eight waves per workgroup), park each unit's 16 outputs
 // per pick in LDS, and the workgroup sums slices and picks in a fixed order.
-template <typename XT, int NT>
+// PLAIN: no renorm-skip and no shared expert (known at compile time): every pick has a position,
+// so the combine carries no test for dropped picks and no shared row (about 0.5 us of its tail)
+template <typename XT, int NT, bool PLAIN>
 __global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs c) {
     constexpr int SS = 4;
     __shared__ float o_part[kMaxDecSlices][kMaxFusedPicks][16];
@@ -519,13 +521,13 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs 
         for (int j = 0; j < k; ++j) {
             const int p = tok * k + j;
             const int pos = c.pick_pos[p];
-            if (pos < 0) continue;                  // a dropped pick
+            if (!PLAIN && pos < 0) continue;        // a dropped pick
             float o = 0.f;
             for (int sl = 0; sl < nsl; ++sl) o += o_part[sl][pos][r];
             accv = fmaf(c.w[p], o, accv);
         }
         float v = accv * c.scaling;
-        if (c.shared) {                                  // the shared expert, unscaled
+        if (!PLAIN && c.shared) {                        // the shared expert, unscaled
             float o = 0.f;
             for (int sl = 0; sl < nsl; ++sl) o += o_part[sl][c.P + tok][r];
             v += o;
@@ -545,7 +547,7 @@ constexpr int kDownMaxF = 2048;
 constexpr int kDownMaxTiles = 32;
 constexpr int kDownFillRounds = (kDownLdsCols * (kDownMaxF / 16 + kDownMaxF / 512) + 511) / 512;
 
-template <typename XT, int NT>
+template <typename XT, int NT, bool PLAIN>
 __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineArgs c) {
     constexpr int SS = 4, NSS = kDecKSlice / (128 * SS);
     constexpr int MAXP = kDownLdsCols / NT;
@@ -708,16 +710,16 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
         static_assert(kMaxDecSlices == 2, "the K slices of a down unit are added below");
 #pragma unroll
         for (int j = 0; j < MAXP; ++j) {
-            const int pj = pos[j] < 0 ? 0 : pos[j];                             // a dropped pick: -1
+            const int pj = (PLAIN || pos[j] >= 0) ? pos[j] : 0;                 // a dropped pick: -1
             const float p0 = o_part[0][pj][r], p1 = o_part[1][pj][r];           // slice 1 read even
             o[j] = nsl > 1 ? p0 + p1 : p0;                                     // when unused
         }
         float accv = 0.f;
 #pragma unroll
         for (int j = 0; j < MAXP; ++j)
-            if (j < k && pos[j] >= 0) accv = fmaf(wgt[j], o[j], accv);
+            if (j < k && (PLAIN || pos[j] >= 0)) accv = fmaf(wgt[j], o[j], accv);
         float val = accv * c.scaling;
-        if (c.shared) {                                  // the shared expert, unscaled
+        if (!PLAIN && c.shared) {                        // the shared expert, unscaled
             const float s0 = o_part[0][c.P + tok][r], s1 = o_part[1][c.P + tok][r];
             val += nsl > 1 ? s0 + s1 : s0;
         }
@@ -761,28 +763,30 @@ hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineA
     trace("down_combine", 0, st);
     dim3 grid(a.d / 16);
     const bool bf = s->act_dtype == MOE_DT_BF16;
-    if (a.Pall * NT <= kDownLdsCols && a.f <= kDownMaxF && a.max_tiles <= kDownMaxTiles) {
-        if (bf) {
-            if (NT == 1) MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 1>), grid, dim3(512), 0, st, a, c);
-            else if (NT == 2) MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
-            else MOE_LAUNCH((k_mx_down_dec_lds<uint16_t, 4>), grid, dim3(512), 0, st, a, c);
-        } else {
-            if (NT == 1) MOE_LAUNCH((k_mx_down_dec_lds<float, 1>), grid, dim3(512), 0, st, a, c);
-            else if (NT == 2) MOE_LAUNCH((k_mx_down_dec_lds<float, 2>), grid, dim3(512), 0, st, a, c);
-            else MOE_LAUNCH((k_mx_down_dec_lds<float, 4>), grid, dim3(512), 0, st, a, c);
-        }
-        trace("down_combine", 1, st);
-        return hipGetLastError();
-    }
-    if (bf) {
-        if (NT == 1) MOE_LAUNCH((k_mx_down_dec<uint16_t, 1>), grid, dim3(512), 0, st, a, c);
-        else if (NT == 2) MOE_LAUNCH((k_mx_down_dec<uint16_t, 2>), grid, dim3(512), 0, st, a, c);
-        else MOE_LAUNCH((k_mx_down_dec<uint16_t, 4>), grid, dim3(512), 0, st, a, c);
+    const bool plain = s->renorm_skip == 0.0f && s->n_shared == 0;
+    const bool lds = a.Pall * NT <= kDownLdsCols && a.f <= kDownMaxF && a.max_tiles <= kDownMaxTiles;
+#define MOE_DD(K, XT, N, PL) MOE_LAUNCH((K<XT, N, PL>), grid, dim3(512), 0, st, a, c)
+#define MOE_DD_NT(K, XT, PL)                                                                  \
+    do {                                                                                      \
+        if (NT == 1) MOE_DD(K, XT, 1, PL);                                                    \
+        else if (NT == 2) MOE_DD(K, XT, 2, PL);                                               \
+        else MOE_DD(K, XT, 4, PL);                                                            \
+    } while (0)
+#define MOE_DD_PL(K, XT)                                                                      \
+    do {                                                                                      \
+        if (plain) MOE_DD_NT(K, XT, true);                                                    \
+        else MOE_DD_NT(K, XT, false);                                                         \
+    } while (0)
+    if (lds) {
+        if (bf) MOE_DD_PL(k_mx_down_dec_lds, uint16_t);
+        else MOE_DD_PL(k_mx_down_dec_lds, float);
     } else {
-        if (NT == 1) MOE_LAUNCH((k_mx_down_dec<float, 1>), grid, dim3(512), 0, st, a, c);
-        else if (NT == 2) MOE_LAUNCH((k_mx_down_dec<float, 2>), grid, dim3(512), 0, st, a, c);
-        else MOE_LAUNCH((k_mx_down_dec<float, 4>), grid, dim3(512), 0, st, a, c);
+        if (bf) MOE_DD_PL(k_mx_down_dec, uint16_t);
+        else MOE_DD_PL(k_mx_down_dec, float);
     }
+#undef MOE_DD_PL
+#undef MOE_DD_NT
+#undef MOE_DD
     trace("down_combine", 1, st);
     return hipGetLastError();
 }
