@@ -34,15 +34,15 @@ __global__ __launch_bounds__(256) void k_logits_gemv(const XT* __restrict__ x, i
 // Router logits on the fp64 matrix cores (V_MFMA_F64_16X16X4_F64), for T > 8.  Products of
 // bf16 (or fp32) x and fp32 Wr are exact in fp64 and summed in fp64, so the top-k decides on the
 // same numbers as a sequential fp64 sum up to the last bits.  A workgroup (4 waves) owns 32
-// tokens x 64 experts and one K slice of the split; wave w computes tokens 16 (w & 1) + [0, 16)
-// against experts 32 (w >> 1) + [0, 32) as two 16x16 blocks.  Operand layout (measured): lane l
+// tokens x 96 experts (288 = 3 x 96, no idle columns) and one K slice of the split; wave w computes
+// tokens 16 (w & 1) + [0, 16) against experts 48 (w >> 1) + [0, 48) as three 16x16 blocks.  Operand layout (measured): lane l
 // supplies row or column l % 16 at K = l / 16; result register r of lane l is row 4 r + l / 16,
 // column l % 16.  Within each group of 16 K values, the four MFMAs j = 0..3 take K = 4 (l / 16) + j
 // (each K once), so a lane reads its four values with one 16-byte LDS load.  The K slice is staged
 // through LDS 64 columns at a time as fp32, rows padded to 68 floats (16-byte aligned).  Slice z's
 // partial sums go to part[z][t][e]; slice 0 also adds the bias.  The top-k sums the slices in
 // order z = 0, 1, ...
-constexpr int kLgTok = 32, kLgExp = 64, kLgK = 64;
+constexpr int kLgTok = 32, kLgExp = 96, kLgK = 64;
 
 template <typename XT>
 __global__ __launch_bounds__(256) void k_logits_mfma(const XT* __restrict__ x, int T, int d,
@@ -54,36 +54,40 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const XT* __restrict__ x, i
     const int t0 = blockIdx.x * kLgTok, e0 = blockIdx.y * kLgExp, z = blockIdx.z;
     const int kb = z * kslice;
     typedef double d4 __attribute__((ext_vector_type(4)));
-    d4 acc[2] = {d4{0, 0, 0, 0}, d4{0, 0, 0, 0}};
+    constexpr int NB = kLgExp / 32;                      // 16-expert blocks per wave
+    d4 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = d4{0, 0, 0, 0};
     const int tr = (wave & 1) * 16 + (lane & 15);        // A row (token) of this lane
-    const int ec = (wave >> 1) * 32 + (lane & 15);       // B column (expert) of block 0
+    const int ec = (wave >> 1) * (kLgExp / 2) + (lane & 15);   // B column (expert) of block 0
     const int kl = lane >> 4;
-    // staging: x 32 x 64 (8 consecutive per thread), Wr 64 x 64 (4 float4 per thread); rows past
-    // the end re-read the last row (their results are not stored)
+    // staging: x 32 x 64 (8 consecutive per thread), Wr kLgExp x 64 (kLgExp / 16 float4 per thread);
+    // rows past the end re-read the last row (their results are not stored)
+    constexpr int NW = kLgExp / 16;
     const int xr = tid >> 3, xc = (tid & 7) * 8;
     const XT* xsrc = x + (size_t)min(t0 + xr, T - 1) * d + kb + xc;
-    const float* wsrc[4];
-    int wrow[4], wcol[4];
+    const float* wsrc[NW];
+    int wrow[NW], wcol[NW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NW; ++i) {
         const int q = i * 256 + tid;
         wrow[i] = q >> 4;
         wcol[i] = (q & 15) * 4;
         wsrc[i] = wr + (size_t)min(e0 + wrow[i], E - 1) * d + kb + wcol[i];
     }
-    float4 xv0, xv1, wv[4];
+    float4 xv0, xv1, wv[NW];
     auto load_chunk = [&](int k0) {
         xv0 = load_act4(xsrc + k0, 0);
         xv1 = load_act4(xsrc + k0, 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wv[i] = *(const float4*)(wsrc[i] + k0);
+        for (int i = 0; i < NW; ++i) wv[i] = *(const float4*)(wsrc[i] + k0);
     };
     auto store_chunk = [&](int buf) {
         float* xd = &xs[buf][xr][xc];
         xd[0] = xv0.x; xd[1] = xv0.y; xd[2] = xv0.z; xd[3] = xv0.w;
         xd[4] = xv1.x; xd[5] = xv1.y; xd[6] = xv1.z; xd[7] = xv1.w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NW; ++i) {
             float* wd = &ws[buf][wrow[i]][wcol[i]];
             wd[0] = wv[i].x; wd[1] = wv[i].y; wd[2] = wv[i].z; wd[3] = wv[i].w;
         }
@@ -98,25 +102,28 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const XT* __restrict__ x, i
 #pragma unroll
         for (int kk = 0; kk < kLgK; kk += 16) {
             const float4 a4 = *(const float4*)&xs[buf][tr][kk + 4 * kl];
-            const float4 b4 = *(const float4*)&ws[buf][ec][kk + 4 * kl];
-            const float4 c4 = *(const float4*)&ws[buf][ec + 16][kk + 4 * kl];
-            const float av[4] = {a4.x, a4.y, a4.z, a4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w},
-                        cv[4] = {c4.x, c4.y, c4.z, c4.w};
+            float4 b4[NB];
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) b4[jb] = *(const float4*)&ws[buf][ec + 16 * jb][kk + 4 * kl];
+            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[j], (double)bv[j], acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[j], (double)cv[j], acc[1], 0, 0, 0);
+#pragma unroll
+                for (int jb = 0; jb < NB; ++jb) {
+                    const float bv = j == 0 ? b4[jb].x : j == 1 ? b4[jb].y : j == 2 ? b4[jb].z : b4[jb].w;
+                    acc[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[j], (double)bv, acc[jb], 0, 0, 0);
+                }
             }
         }
         if (ch + 1 < nch) store_chunk(buf ^ 1);
         __syncthreads();
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = t0 + (wave & 1) * 16 + 4 * r + (lane >> 4);
-            const int e = e0 + (wave >> 1) * 32 + 16 * j + (lane & 15);
+            const int e = e0 + (wave >> 1) * (kLgExp / 2) + 16 * j + (lane & 15);
             if (t < T && e < E) {
                 double v = acc[j][r];
                 if (z == 0 && bias) v += (double)bias[e];
