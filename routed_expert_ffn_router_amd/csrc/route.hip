@@ -500,7 +500,9 @@ constexpr int kSmallT = 16;
 
 // Routing refused (the status word was already nonzero, or the wait for the logits gave up):
 // record a timeout in the status word (only if it was clean), and leave outputs that fail loudly
-// downstream - no tile, idx -1, w NaN (so y is NaN), positions 0 (in bounds for every reader).
+// downstream: idx -1 and w NaN, so that y is NaN.  Several tokens: no tile, positions 0 (in bounds
+// for every reader).  One token: the pass runs on stand-in picks (real experts, so the GEMMs stay
+// in bounds) with the NaN weights.
 __device__ __forceinline__ void report_timeout(uint32_t* status) {
     __hip_atomic_fetch_or(status, MOE_WS_ROUTE_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     // branches, so that the LDS path stays LDS loads rather than generic ones)
     auto put_expert = [&](TileDesc* D, int e) {
         uint4* dst = (uint4*)&D->ex;
-        if (tab_lds && e < E) {
+        if (tab_lds && (PLAIN || e < E)) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst[i] = s_tab[4 * e + i];
         } else {
@@ -694,6 +696,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             unsigned long long kv[S];
 #pragma unroll
             for (int s = 0; s < S; ++s) kv[s] = 0ull;
+            bool refused = false;       // (wave 0) the wait gave up, or the workspace was refused
             if (live) {
                 tstore(0, tab0);
                 tstore(1, tab1);
@@ -724,14 +727,13 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                         }
                     }
                     if (!got) {
-                        // the pass still runs, on the stand-in keys, and its outputs are then
-                        // replaced by a refusal (a test here, not after the barrier, keeps the
-                        // common path free of it)
+                        // the pass still runs: its picks come from the stand-in keys, its weights
+                        // from key 0 (a NaN logit, below), and the indices it writes are -1
 #pragma unroll
                         for (int s = 0; s < S; ++s) kv[s] = dummy_key(lane + 64 * s);
                         if (lane == 0 && st0 == 0u) report_timeout(a.hdr);
                     }
-                    if (lane == 0) s_fail[0] = got ? 0 : 1;
+                    refused = !got;
                 } else {
                     // a branch of its own (the asm keeps it one), so that the warm-up pass does
                     // not wait for the poll in flight
@@ -739,9 +741,11 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
 #pragma unroll
                     for (int s = 0; s < S; ++s) kv[s] = dummy_key(lane + 64 * s);
                 }
+                // the keys whose sigmoids make the weights: after a refusal key 0 for every expert,
+                // whose logit is a NaN, so that every weight and y are NaN
 #pragma unroll
                 for (int s = 0; s < S; ++s)
-                    if (lane + 64 * s < E) s_key[lane + 64 * s] = kv[s];
+                    if (lane + 64 * s < E) s_key[lane + 64 * s] = refused ? 0ull : kv[s];
             }
             lds_barrier();
             if (wave == 0) {
@@ -755,6 +759,51 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 }
             }
             lds_barrier();
+            if constexpr (PLAIN) {
+                // every pick stays.  Records: the token's experts are distinct, so pick p is a tile of
+                // its own at sorted position = the number of picks of lower experts (what the grouping
+                // below gives in this case)
+                if (wave == 0) {
+                    const int p = lane;
+                    const int e = p < k ? s_idx[p] : 0;
+                    int pos = 0;
+                    for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(e, q) < e;
+                    if (p < k) {
+                        TileDesc* D = desc + pos;
+                        put_expert(D, e);
+                        D->i0 = pos;
+                        D->ntok = 1;
+                        D->e = e;
+                        D->pad0 = 0;
+#pragma unroll
+                        for (int c = 0; c < kDescTokens; ++c) D->tok[c] = 0;
+                        tiles[2 * pos] = e;
+                        tiles[2 * pos + 1] = pos;
+                        idx[p] = refused ? -1 : e;
+                        pick_pos[p] = pos;
+                        sorted_pick[pos] = p;
+                    }
+                } else if (wave == 1) {
+                    // the weights, the sum in rank order
+                    const int p = lane;
+                    const double sg = p < k ? s_sig[s_idx[p]] : 0.0;
+                    double ssum = 0.0;
+                    for (int j = 0; j < k; ++j) ssum += readlane_f64(sg, j);
+                    if (p < k) wout[p] = (float)(sg / ssum);
+                } else {
+                    // the expert offsets (picks of lower experts), the empty records, the tile count
+                    for (int e = tid - 128; e <= E; e += 128) {
+                        int lower = 0;
+#pragma unroll 8
+                        for (int q = 0; q < k; ++q) lower += s_idx[q] < e;
+                        offsets[e] = lower;
+                    }
+                    for (int id = k + tid - 128; id < a.max_tiles; id += 128) put_empty(desc, id, s_idx[0]);
+                    if (tid == 128) *ntiles = k;
+                }
+                lds_barrier();      // the real pass rewrites what this one read from LDS
+                continue;
+            }
             // the picks that stay (bit j: pick j), the same in every wave: all k, or with renorm-skip
             // those not dropped (rank 0 and every pick whose fp64 weight is not below tau)
             unsigned long long km = k >= 64 ? ~0ull : ((1ull << k) - 1ull);
@@ -774,7 +823,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 const bool kept = (km >> p) & 1ull;
                 int pos = 0;
                 // (bitwise tests, not &&: no branch may separate the reads, so they go out together)
-                for (int q = 0; q < k; ++q) pos += (int)(PLAIN ? 1ull : (km >> q) & 1ull) & (int)(__builtin_amdgcn_readlane(e, q) < e);
+                for (int q = 0; q < k; ++q) pos += (int)((km >> q) & 1ull) & (int)(__builtin_amdgcn_readlane(e, q) < e);
                 if (kept) {
                     TileDesc* D = desc + pos;
                     put_expert(D, e);
@@ -786,7 +835,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                     for (int c = 0; c < kDescTokens; ++c) D->tok[c] = 0;
                     tiles[2 * pos] = e;
                     tiles[2 * pos + 1] = pos;
-                    idx[p] = e;
+                    idx[p] = refused ? -1 : e;
                     pick_pos[p] = pos;
                     sorted_pick[pos] = p;
                 } else if (p < k) {          // dropped: no expert, no position
@@ -810,7 +859,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 for (int e = tid - 128; e <= E; e += 128) {
                     int lower = 0;
 #pragma unroll 8
-                    for (int q = 0; q < k; ++q) lower += (int)(PLAIN ? 1ull : (km >> q) & 1ull) & (int)(s_idx[q] < e);
+                    for (int q = 0; q < k; ++q) lower += (int)((km >> q) & 1ull) & (int)(s_idx[q] < e);
                     offsets[e] = lower;
                 }
                 const int nall = nkept + (shared ? 1 : 0);      // one token: one shared tile
@@ -818,13 +867,6 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 if (tid == 128) *ntiles = nall;
             }
             lds_barrier();      // the real pass rewrites what this one read from LDS
-        }
-        if (s_fail[0]) {
-            // the wait gave up: what the real pass wrote is replaced by a refusal, once every
-            // store of it has landed
-            __threadfence();
-            __syncthreads();
-            put_refused(a.desc, a.idx, a.w, a.pick_pos, a.sorted_pick, a.offsets, a.ntiles);
         }
         return;
     }
