@@ -708,9 +708,11 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 if (live) {
                     // poll the slots (lane l: experts l + 64 s) until none is zero, at most
                     // poll_limit times; none at all on a workspace whose status is already set.
-                    // The reads of a round are all issued before its tests.
-                    const uint32_t st0 = gload4(&a.hdr[0]);
-                    const int poll_limit = poll_limit_of(gload4(&a.hdr[1]));
+                    // The reads of a round are all issued before its tests.  The status word and
+                    // the poll limit (one 8-byte read: the header is 256-byte aligned) are read
+                    // in every round beside the slots: read once before the loop, they cost a
+                    // round trip of their own before the first poll.
+                    uint32_t st0 = 0u;
                     bool got = false;
                     for (int it = 0;; ++it) {
                         bool miss = false;
@@ -720,7 +722,9 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                             kv[s] = ~v;
                             miss |= (lane + 64 * s < E) & (v == 0ull);
                         }
-                        if ((st0 != 0u) | (it >= poll_limit)) break;
+                        const unsigned long long h = get_slot((const unsigned long long*)a.hdr);
+                        st0 = (uint32_t)h;
+                        if ((st0 != 0u) | (it >= poll_limit_of((uint32_t)(h >> 32)))) break;
                         if (__ballot(miss) == 0ull) {
                             got = true;
                             break;
