@@ -20,7 +20,6 @@
 // KSPLIT = 1 they own four different row groups (many tokens per expert: prefill).  The K loop
 // issues every load of a chunk of CH super-steps before its MFMAs, so each wave keeps
 // CH * 64 * SS bytes per weight fragment in flight.
-#include <utility>
 
 #include "moe_internal.h"
 
@@ -855,26 +854,6 @@ constexpr int kScLoads = 6;                   // direct loads per wave and group
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 __device__ __forceinline__ int swz_b(int c) { return ((c >> 1) ^ ((c & 1) << 2)) & 7; }
 
-typedef const __attribute__((address_space(1))) void* dma_src_t;
-typedef __attribute__((address_space(3))) void* dma_dst_t;
-// lane l's 16 (4) bytes at src land at lds + 16 l (4 l); lds must be the same in every lane
-__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds) {
-    __builtin_amdgcn_global_load_lds((dma_src_t)src, (dma_dst_t)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* lds) {
-    __builtin_amdgcn_global_load_lds((dma_src_t)src, (dma_dst_t)lds, 4, 0, 0);
-}
-// wait until at most N vector-memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// workgroup barrier for the stage ring: this wave's LDS reads are complete and the compiler
-// moves no memory access across it.  Unlike __syncthreads it does not wait for this wave's
-// direct loads still in flight (they target other stages; each is waited for with wait_vm
-// before the barrier that publishes its stage).
-__device__ __forceinline__ void ring_barrier() { lds_barrier(); }
 
 struct PfFrags {
     uint4 a[8];
@@ -912,15 +891,6 @@ __device__ __forceinline__ void pf_mfma(const PfFrags& fr, v4f (&acc)[8][4]) {
             acc[j][n] = mfma_fp4_fp8(fr.a[j], fr.b[n][0], fr.b[n][1], acc[j][n], fr.sa[j], fr.sb[n]);
 }
 
-template <int Q>
-struct StepPos {
-    static constexpr int value = Q;
-};
-// f(StepPos<B>), f(StepPos<B + 1>), ... in order, for each index of the sequence
-template <int B, typename F, int... I>
-__device__ __forceinline__ void for_steps(F&& f, std::integer_sequence<int, I...>) {
-    (f(StepPos<B + I>{}), ...);
-}
 
 // FULL: 0, or the step count K / 128 that this instance runs as straight-line code
 template <int NT, bool GATEUP, int FULL>

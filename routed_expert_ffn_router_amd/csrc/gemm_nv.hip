@@ -396,6 +396,242 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
     }
 }
 
+// The same tile for single-term activations (bf16 x in place, h as one bf16 term), fed by a ring
+// of four LDS stages that global_load_lds fills three steps ahead, with no register round trip.
+// A stage holds one 128-K step: the rows' code bytes, the tile's activation columns and the rows'
+// E4M3 scale bytes.  While the MFMAs of step s run, the fragments of step s + 1 are read from LDS
+// and decoded into a second register set.  Consecutive lanes read consecutive bytes (4 lanes per
+// 64-byte row chunk, 16 per 256-byte column chunk): the vector L1 serves a load one lane quad at a
+// time.  In LDS the rows' 16-byte parts are XOR-swizzled (no bank conflicts, measured); the
+// columns' units are XOR-swizzled by column, which leaves 4 conflict cycles per column read
+// (measured) that cost no time: the kernel ran as fast with the column reads taken out.
+// Like the register-staged kernel, this one is bound by its loads, more by the cache lines a step
+// requests than by its bytes (the decode, the MFMAs or the column reads, each taken out, changed
+// the time by at most 7%).  Against it: 5% faster at K = 6144 (48 steps); at K = 2048 slower, one
+// workgroup per CU leaving the ring's fill and drain exposed, so short K stays there.
+//
+// Stage layout (bytes): row r (0..127) at 64 r, its 16-byte part p in slot p ^ swz_a(r % 16);
+// column c (0..63) at 8192 + 256 c, its 16-byte unit u in slot u ^ (c % 16); row r's 8 scale
+// bytes at 24576 + 8 r.
+constexpr int kNrA = 0, kNrB = 8192, kNrS = 24576, kNrStage = 25600;
+constexpr int kNrLoads = 7;      // direct loads per wave and stage: 2 code, 4 activation, 1 scale
+constexpr int kNrMinK = 4096;    // shortest K that takes the ring
+
+__device__ __forceinline__ int swz_rows(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
+
+// the fragments of one step: two decoded 16-row weight fragments (4 MFMAs of 32 K each) and the
+// tile's four 16-column activation fragments
+struct NrFrags {
+    bf16x8_t a[2][4];
+    uint4 b[4][4];
+};
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 1) void k_nv_pf_ring(GemmArgs a, int tiles_per_xcd_cap) {
+    constexpr int NSTG = 4;                          // stages in the ring
+    __shared__ __align__(16) uint8_t stg0[kNrStage];
+    __shared__ __align__(16) uint8_t stg1[kNrStage];
+    __shared__ __align__(16) uint8_t stg2[kNrStage];
+    __shared__ __align__(16) uint8_t stg3[kNrStage];
+    constexpr int BN = kNvTilePicksMany;             // columns of the tile (one term per pick)
+    constexpr int NCF = BN / 16;
+    static_assert(kNrB == 128 * 64 && kNrS == kNrB + BN * 256 && kNrStage == kNrS + 128 * 8, "stage layout");
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int K = GATEUP ? a.d : a.f;
+    const int MT = GATEUP ? a.f / 64 : a.d / 128;
+    int t_lo = 0, t_hi = *a.ntiles;
+    if (a.tile_range) {
+        t_lo = a.tile_range[0];
+        t_hi = a.tile_range[1];
+    }
+    const int nt = t_hi - t_lo;
+    const int g = blockIdx.x, xcd = g & 7, sidx = g >> 3;
+    const int mblk = sidx % MT, tq = sidx / MT;
+    const int TPX = (nt + 7) >> 3;
+    if (nt <= 0 || tq >= TPX || tq >= tiles_per_xcd_cap) return;
+    const int tile = t_lo + xcd * TPX + tq;
+    if (tile >= t_hi) return;
+    const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
+    const int ntok = min(kNvTilePicksMany, range_end(a, e) - i0);
+    const moe_expert ex = a.table[e];
+
+    // tile row r (0..127) -> weight row (gate/up: rows 0..63 gate, 64..127 up, same indices)
+    auto a_row = [&](int r, bool scale) -> const uint8_t* {
+        int mr;
+        const uint8_t* base;
+        if (GATEUP) {
+            mr = mblk * 64 + (r & 63);
+            base = (r < 64) ? (scale ? ex.gate_s : ex.gate_q) : (scale ? ex.up_s : ex.up_q);
+        } else {
+            mr = mblk * 128 + r;
+            base = scale ? ex.down_s : ex.down_q;
+        }
+        return base + (size_t)mr * (scale ? K / 16 : K / 2);
+    };
+    // tile column c (0..63) = pick c; columns past the tile re-read column 0
+    auto b_col = [&](int c) -> const uint8_t* {
+        const int tcc = c < ntok ? c : 0;
+        const size_t arow = GATEUP ? (size_t)pos_token(a, i0 + tcc) : (size_t)(i0 + tcc);
+        return a.aq + arow * (size_t)K * 2;
+    };
+    // this wave's direct loads: rows 32 w .. 32 w + 31 (two instructions of 16 rows, a lane quad
+    // per row), columns 16 w .. 16 w + 15 (four instructions of 4 columns, 16 lanes per column),
+    // and the scale bytes of rows 32 w .. (one instruction, two lanes of 4 bytes per row)
+    const uint8_t* srcA[2];
+    const uint8_t* srcB[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = (wave * 2 + j) * 16 + (lane >> 2);
+        srcA[j] = a_row(r, false) + (((lane & 3) ^ swz_rows(r & 15)) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = (wave * 4 + j) * 4 + (lane >> 4);
+        srcB[j] = b_col(c) + (((lane & 15) ^ (c & 15)) * 16);
+    }
+    const uint8_t* srcS = a_row(wave * 32 + (lane >> 1), true) + (lane & 1) * 4;
+    const int nsteps = K / 128, last = nsteps - 1;
+    auto issue = [&](int st, uint8_t* stg) {
+        const size_t oa = (size_t)st * 64, ob = (size_t)st * 256, os = (size_t)st * 8;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma16(srcA[j] + oa, stg + kNrA + (wave * 2 + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(srcB[j] + ob, stg + kNrB + (wave * 4 + j) * 1024);
+        dma4(srcS + os, stg + kNrS + wave * 256);
+    };
+
+    // wave w's two 16-row fragments (gate/up: rows 16 w .. of gate and of up; down: rows 32 w ..)
+    int arow[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) arow[f] = GATEUP ? (f * 64 + wave * 16 + li) : (wave * 32 + f * 16 + li);
+    // fragments of the step in stage stg: code parts and scale pairs first, then the columns;
+    // each lane group takes K [32 lg, 32 lg + 32) of the step, MFMA h its [8 h, 8 h + 8)
+    auto read_step = [&](const uint8_t* stg, NrFrags& fr) {
+        uint4 codes[2];
+        uint32_t sp[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            codes[f] = *(const uint4*)(stg + kNrA + arow[f] * 64 + ((lg ^ swz_rows(li)) * 16));
+            sp[f] = *(const uint16_t*)(stg + kNrS + arow[f] * 8 + 2 * lg);
+        }
+#pragma unroll
+        for (int n = 0; n < NCF; ++n)
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+                fr.b[n][h] = *(const uint4*)(stg + kNrB + (n * 16 + li) * 256 + (((lg * 4 + h) ^ li) * 16));
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const v2f_t bs = e4m3x2_to_f32(sp[f]);
+            const uint32_t w[4] = {codes[f].x, codes[f].y, codes[f].z, codes[f].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) fr.a[f][h] = nv_dequant8(w[h], h < 2 ? bs[0] : bs[1]);
+        }
+    };
+    v4f_nv acc[2][NCF];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int n = 0; n < NCF; ++n) acc[f][n] = v4f_nv{0.f, 0.f, 0.f, 0.f};
+    auto run_step = [&](const NrFrags& fr) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int n = 0; n < NCF; ++n)
+                    acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.a[f][h], as_bf16x8(fr.b[n][h]), acc[f][n],
+                                                                        0, 0, 0);
+    };
+    auto stage_buf = [&](auto i) -> uint8_t* {
+        constexpr int I = decltype(i)::value;
+        if constexpr (I == 0) return stg0;
+        else if constexpr (I == 1) return stg1;
+        else if constexpr (I == 2) return stg2;
+        else return stg3;
+    };
+
+    NrFrags fr0, fr1;
+    // every step issues one stage, clamped to the last (past the end the ring is refilled with
+    // copies of the last stage that no step reads); before step s reads stage s + 1, the loads of
+    // stages s + 2 and s + 3 may still be in flight
+    for_steps<0>([&](auto i) { issue(min(decltype(i)::value, last), stage_buf(i)); },
+                 std::make_integer_sequence<int, NSTG>{});
+    wait_vm<(NSTG - 1) * kNrLoads>();
+    ring_barrier();
+    read_step(stg0, fr0);
+    // step s (s % 8 == Q): stage s is in registers; wait for stage s + 1, refill stage s's buffer
+    // with step s + 4, read and decode stage s + 1 into the other register set (past the end:
+    // unused values), run the MFMAs of step s
+    auto step = [&](int s, auto pos) {
+        constexpr int Q = decltype(pos)::value;
+        NrFrags& cur = (Q & 1) ? fr1 : fr0;
+        NrFrags& nxt = (Q & 1) ? fr0 : fr1;
+        wait_vm<(NSTG - 2) * kNrLoads>();
+        ring_barrier();                        // also: every wave has stage s in registers
+        __builtin_amdgcn_sched_barrier(0);
+        issue(min(s + NSTG, last), stage_buf(StepPos<Q % NSTG>{}));
+        read_step(stage_buf(StepPos<(Q + 1) % NSTG>{}), nxt);
+        run_step(cur);
+        // schedule: the code and scale reads of step s + 1 first, then its column reads and
+        // direct loads one at a time between the MFMAs of step s, the decode's arithmetic beside
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kNrLoads; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 32 - 16 - kNrLoads; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // eight steps per loop iteration: two turns of the ring, four of the register-set pairs
+    constexpr int U = 8;
+    int s = 0;
+    for (; s + U <= nsteps; s += U)
+        for_steps<0>([&](auto i) { step(s + decltype(i)::value, i); }, std::make_integer_sequence<int, U>{});
+    for_steps<0>([&](auto i) { if (s + decltype(i)::value < nsteps) step(s + decltype(i)::value, i); },
+                 std::make_integer_sequence<int, U - 1>{});
+    wait_vm<0>();                              // no direct load outlives the workgroup
+
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int n = 0; n < NCF; ++n) mfma_results_here(acc[f][n]);
+#pragma unroll
+    for (int n = 0; n < NCF; ++n) {
+        const int tc = n * 16 + li;
+        if (tc >= ntok) continue;
+        const size_t pos = (size_t)i0 + tc;
+        if constexpr (GATEUP) {
+            uint16_t* hb = (uint16_t*)a.hq + pos * (size_t)a.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float gv = acc[0][n][r] * ex.gate_ts, uv = acc[1][n][r] * ex.up_ts;
+                const int row = mblk * 64 + wave * 16 + 4 * lg + r;
+                put_h_terms<1>(hb, a.f, row, gv / (1.0f + __expf(-gv)) * uv);
+            }
+        } else {
+            float* dst = a.o + pos * (size_t)a.d + mblk * 128 + wave * 32 + 4 * lg;
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+                *(float4*)(dst + 16 * f) = make_float4(acc[f][n][0] * ex.down_ts, acc[f][n][1] * ex.down_ts,
+                                                       acc[f][n][2] * ex.down_ts, acc[f][n][3] * ex.down_ts);
+        }
+    }
+}
+
 // Few picks per expert ("decode"): a workgroup of 8 waves owns one tile (up to kNvTilePicks
 // picks) and one block of output rows: the same 16 row indices of gate and of up, or 32 down
 // rows.  Wave w takes the 16-row fragment w / 4 over the K quarter w % 4 and requests all of its
@@ -544,8 +780,14 @@ hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int tile_picks
         const int MT = gateup ? a.f / 64 : a.d / 128;
         const int cap = (max_tiles + 7) / 8;
         dim3 g2((unsigned)(8 * cap * MT));
-        if (!gateup && NT == 1) MOE_LAUNCH((k_nv_pf<1, false>), g2, dim3(256), 0, st, a, cap);
+        // single-term activations and a long K (at least kNrMinK): the ring-fed kernel, one
+        // workgroup per CU; else the register-staged one, whose smaller LDS lets workgroups share a
+        // CU and hide each other's start and end (which a short K does not amortise)
+        const bool ring = NT == 1 && (gateup ? a.d : a.f) >= kNrMinK;
+        if (!gateup && ring) MOE_LAUNCH((k_nv_pf_ring<false>), g2, dim3(256), 0, st, a, cap);
+        else if (!gateup && NT == 1) MOE_LAUNCH((k_nv_pf<1, false>), g2, dim3(256), 0, st, a, cap);
         else if (!gateup) MOE_LAUNCH((k_nv_pf<2, false>), g2, dim3(256), 0, st, a, cap);
+        else if (ring) MOE_LAUNCH((k_nv_pf_ring<true>), g2, dim3(256), 0, st, a, cap);
         else if (NT == 1) MOE_LAUNCH((k_nv_pf<1, true>), g2, dim3(256), 0, st, a, cap);
         else MOE_LAUNCH((k_nv_pf<2, true>), g2, dim3(256), 0, st, a, cap);
     } else if ((gateup ? a.d : a.f) <= kNvDecMaxK) {

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "moe.h"
 
 namespace moe {
@@ -116,6 +118,41 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------------------------
+// direct global -> LDS loads (global_load_lds) for the stage rings of the many-picks GEMMs
+// ---------------------------------------------------------------------------------------------
+typedef const __attribute__((address_space(1))) void* dma_src_t;
+typedef __attribute__((address_space(3))) void* dma_dst_t;
+// lane l's 16 (4) bytes at src land at lds + 16 l (4 l); lds must be the same in every lane
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds((dma_src_t)src, (dma_dst_t)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds((dma_src_t)src, (dma_dst_t)lds, 4, 0, 0);
+}
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// workgroup barrier for the stage ring: this wave's LDS reads are complete and the compiler
+// moves no memory access across it.  Unlike __syncthreads it does not wait for this wave's
+// direct loads still in flight (they target other stages; each is waited for with wait_vm
+// before the barrier that publishes its stage).
+__device__ __forceinline__ void ring_barrier() { lds_barrier(); }
+
+// compile-time step positions of the unrolled ring loops
+template <int Q>
+struct StepPos {
+    static constexpr int value = Q;
+};
+// f(StepPos<B>), f(StepPos<B + 1>), ... in order, for each index of the sequence
+template <int B, typename F, int... I>
+__device__ __forceinline__ void for_steps(F&& f, std::integer_sequence<int, I...>) {
+    (f(StepPos<B + I>{}), ...);
 }
 
 // ---------------------------------------------------------------------------------------------
