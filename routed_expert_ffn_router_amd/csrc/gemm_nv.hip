@@ -670,22 +670,59 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
     const moe_expert ex = a.table[e];
     const int T0 = (GATEUP ? 16 : 32) * blockIdx.y;
     const int NS = K / 128, s0 = (kq * NS) / 4, nss = ((kq + 1) * NS) / 4 - s0;
-    // 1. activation columns c = (pick c / NT, term c % NT), K bf16 each, as 16-byte chunks; the
-    // first round is requested before the weights
+    // 1. activation columns c = (pick c / NT, term c % NT), K bf16 each, as 16-byte chunks.  With
+    // at most two columns (ALL_FIRST) every round is requested before the weights, and so are the
+    // scale bytes (step 2), so that the LDS stores below wait for them alone and the barrier after
+    // them need not wait for the weights: each super-step's MFMAs then start when its own weights
+    // are in.  With more columns the first round goes first and the rest follow the weights.
     const int ncol = ntok * NT, cpc = K / 8, nchunk = ncol * cpc;
+    constexpr bool ALL_FIRST = NCOL <= 2;
+    constexpr int RF = ALL_FIRST ? (NCOL * (KMAX / 8) + 511) / 512 : 1;     // rounds requested first
+    // with at most two columns their bases are found once (one token-index round trip for all
+    // rounds, not one per round)
+    const uint8_t* colb[2] = {a.aq, a.aq};
+    if constexpr (ALL_FIRST) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int cc = c < ncol ? c : ncol - 1, tc = cc / NT, t = cc % NT;
+            const size_t arow = GATEUP ? (size_t)pos_token(a, i0 + tc) : (size_t)(i0 + tc);
+            colb[c] = a.aq + (arow * NT + t) * (size_t)K * 2;
+        }
+    }
     auto chunk_src = [&](int g) -> const uint8_t* {
-        const int c = g / cpc, tc = c / NT, t = c % NT;
-        const size_t arow = GATEUP ? (size_t)pos_token(a, i0 + tc) : (size_t)(i0 + tc);
-        return a.aq + ((arow * NT + t) * (size_t)K + (size_t)(g % cpc) * 8) * 2;
+        if constexpr (ALL_FIRST) {
+            return colb[g >= cpc ? 1 : 0] + (size_t)(g % cpc) * 16;
+        } else {
+            const int c = g / cpc, tc = c / NT, t = c % NT;
+            const size_t arow = GATEUP ? (size_t)pos_token(a, i0 + tc) : (size_t)(i0 + tc);
+            return a.aq + ((arow * NT + t) * (size_t)K + (size_t)(g % cpc) * 8) * 2;
+        }
     };
-    const int g0 = tid < nchunk ? tid : nchunk - 1;
-    const uint4 v0 = gload16(chunk_src(g0));
-    // 2. this wave's weights: row of fragment f (gate: f = 0, up: f = 1; down: rows 16 f ..),
-    // super-steps s0 .. s0 + nss (past nss: re-read; a quarter without steps, K < 512, re-reads
-    // step s0, which is inside the row)
+    // (every round's load is issued, without a branch; chunks past the columns re-read the last)
+    uint4 vx[RF];
+#pragma unroll
+    for (int r = 0; r < RF; ++r) {
+        const int g = tid + 512 * r;
+        vx[r] = gload16(chunk_src(g < nchunk ? g : nchunk - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);     // requested in this order: columns, scales, weights
+    // 2. the scale bytes of this wave's quarter, 8 per super-step and row: lane (li, lg) loads
+    // those of super-steps lg, lg + 4, .. of row li (past nss: super-step nss - 1 again, not
+    // used), one 8-byte load each, for LDS with the columns
     const int row = GATEUP ? T0 + li : T0 + 16 * f + li;
     const uint8_t* mq = GATEUP ? (f == 0 ? ex.gate_q : ex.up_q) : ex.down_q;
     const uint8_t* ms = GATEUP ? (f == 0 ? ex.gate_s : ex.up_s) : ex.down_s;
+    const uint8_t* srow = ms + (size_t)row * (K / 16) + (size_t)s0 * 8;
+    uint2 S2[NSW / 4];
+#pragma unroll
+    for (int i = 0; i < NSW / 4; ++i) {
+        const int q = 4 * i + lg, qq = q < nss ? q : (nss > 0 ? nss - 1 : 0);
+        S2[i] = gload8(srow + (size_t)qq * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. this wave's weights: row of fragment f (gate: f = 0, up: f = 1; down: rows 16 f ..),
+    // super-steps s0 .. s0 + nss (past nss: re-read; a quarter without steps, K < 512, re-reads
+    // step s0, which is inside the row)
     const uint8_t* aq = mq + (size_t)row * (K / 2) + (size_t)s0 * 64 + lg * 16;
     uint4 A[NSW];
 #pragma unroll
@@ -693,25 +730,28 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
         const int qq = q < nss ? q : (nss > 0 ? nss - 1 : 0);
         A[q] = gload16(aq + (size_t)qq * 64);
     }
-    // the scale bytes of this wave's quarter, 8 per super-step and row: lane (li, lg) loads those
-    // of super-steps lg, lg + 4, .. of row li (past nss: super-step nss - 1 again, not used), one
-    // 8-byte load each, for LDS with the columns
-    const uint8_t* srow = ms + (size_t)row * (K / 16) + (size_t)s0 * 8;
-    uint2 S2[NSW / 4];
+    // 4. the columns and scale bytes into LDS (further rounds, for many columns, after the weights).
+    // Their registers are taken here, in straight-line code, so that the wait for them counts the
+    // weight loads issued since and leaves those in flight
 #pragma unroll
-    for (int i = 0; i < NSW / 4; ++i) {
-        const int q = 4 * i + lg, qq = q < nss ? q : (nss > 0 ? nss - 1 : 0);
-        S2[i] = *(const uint2*)(srow + (size_t)qq * 8);
+    for (int r = 0; r < RF; ++r) asm volatile("" ::"v"(vx[r].x), "v"(vx[r].y), "v"(vx[r].z), "v"(vx[r].w));
+#pragma unroll
+    for (int i = 0; i < NSW / 4; ++i) asm volatile("" ::"v"(S2[i].x), "v"(S2[i].y));
+#pragma unroll
+    for (int r = 0; r < RF; ++r) {
+        const int g = tid + 512 * r;
+        if (g < nchunk) *(uint4*)(b_lds + (size_t)(g / cpc) * cst + (size_t)(g % cpc) * 16) = vx[r];
     }
-    // 3. the columns into LDS (further rounds, for many columns, after the weights)
-    asm volatile("" ::"v"(v0.x), "v"(v0.y), "v"(v0.z), "v"(v0.w));
-    if (tid < nchunk) *(uint4*)(b_lds + (size_t)(g0 / cpc) * cst + (size_t)(g0 % cpc) * 16) = v0;
 #pragma unroll
     for (int i = 0; i < NSW / 4; ++i) *(uint2*)&s_sc[wave][li][8 * (4 * i + lg)] = S2[i];
-    for (int g = tid + 512; g < nchunk; g += 512)
-        *(uint4*)(b_lds + (size_t)(g / cpc) * cst + (size_t)(g % cpc) * 16) = gload16(chunk_src(g));
-    __syncthreads();
-    // 4. MFMAs: lane group lg takes K [32 lg, 32 lg + 32) of a super-step, MFMA h its [8h, 8h + 8);
+    if constexpr (ALL_FIRST) {
+        lds_barrier();              // not waiting for the weights in flight
+    } else {
+        for (int g = tid + 512; g < nchunk; g += 512)
+            *(uint4*)(b_lds + (size_t)(g / cpc) * cst + (size_t)(g % cpc) * 16) = gload16(chunk_src(g));
+        __syncthreads();
+    }
+    // 5. MFMAs: lane group lg takes K [32 lg, 32 lg + 32) of a super-step, MFMA h its [8h, 8h + 8);
     // columns past the tile read its last column (their results are not used)
     const int col = li < ncol ? li : ncol - 1;
     const uint8_t* bl = b_lds + (size_t)col * cst + (size_t)s0 * 256 + lg * 64;
@@ -729,7 +769,7 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
             }
         }
     }
-    // 5. K quarters summed in quarter order by wave 0, then the epilogue
+    // 6. K quarters summed in quarter order by wave 0, then the epilogue
     mfma_results_here(acc);
     part[wave][lane] = acc;
     __syncthreads();

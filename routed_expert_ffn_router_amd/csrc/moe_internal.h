@@ -97,6 +97,11 @@ __device__ __forceinline__ uint4 gload16(const void* p) {
     const u32x4_t v = *(__attribute__((address_space(1))) const u32x4_t*)p;
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 gload8(const void* p) {
+    const u32x2_t v = *(__attribute__((address_space(1))) const u32x2_t*)p;
+    return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ uint32_t gload4(const void* p) {
     return *(__attribute__((address_space(1))) const uint32_t*)p;
 }
