@@ -788,11 +788,15 @@ def main():
             "kernels_us": dec["kernels_us"],
         })
     else:
-        first = next(k for k in ("prefill", "batched", "nvfp4") if k in out)
-        r = out[first] if first != "nvfp4" else out["nvfp4"]["T1_in_place"]
-        line.update({"value": r.get("tokens_per_s", r.get("layer_tokens_per_s")), "unit": "tokens/s",
-                     "ms_per_step": r.get("ms_per_layer", r.get("ms_per_step")),
-                     "config": {"workload": first}})
+        first = next((k for k in ("prefill", "batched", "nvfp4") if k in out), None)
+        if first is None:         # only the optional rows ran: their figures are under "rows"
+            line.update({"value": None, "unit": "layer-tokens/s", "ms_per_step": None,
+                         "config": {"workload": "rows"}})
+        else:
+            r = out[first] if first != "nvfp4" else out["nvfp4"]["T1_in_place"]
+            line.update({"value": r.get("tokens_per_s", r.get("layer_tokens_per_s")), "unit": "tokens/s",
+                         "ms_per_step": r.get("ms_per_layer", r.get("ms_per_step")),
+                         "config": {"workload": first}})
     line["cpu_baseline"] = cpu
     line["parity"] = dict(parity, all_pass=all_pass) if parity else None
     for k in ("prefill", "batched", "nvfp4", "rows"):

@@ -113,16 +113,27 @@ hipError_t launch_fill_table(const moe_shape* s, const uint8_t* base, size_t str
 // staged table entry
 __device__ moe_expert gather_one(const moe_expert& src, uint8_t* dst, size_t nq, size_t ns, size_t stride) {
     const size_t n16 = (3 * nq + 3 * ns) / 16;
-    for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n16; u += (size_t)gridDim.x * 256) {
-        const size_t off = u * 16;
-        const uint8_t* sp;
-        if (off < nq) sp = src.gate_q + off;
-        else if (off < 2 * nq) sp = src.up_q + (off - nq);
-        else if (off < 3 * nq) sp = src.down_q + (off - 2 * nq);
-        else if (off < 3 * nq + ns) sp = src.gate_s + (off - 3 * nq);
-        else if (off < 3 * nq + 2 * ns) sp = src.up_s + (off - 3 * nq - ns);
-        else sp = src.down_s + (off - 3 * nq - 2 * ns);
-        *(uint4*)(dst + off) = *(const uint4*)sp;
+    auto src_of = [&](size_t off) -> const uint8_t* {
+        if (off < nq) return src.gate_q + off;
+        if (off < 2 * nq) return src.up_q + (off - nq);
+        if (off < 3 * nq) return src.down_q + (off - 2 * nq);
+        if (off < 3 * nq + ns) return src.gate_s + (off - 3 * nq);
+        if (off < 3 * nq + 2 * ns) return src.up_s + (off - 3 * nq - ns);
+        return src.down_s + (off - 3 * nq - 2 * ns);
+    };
+    // four 16-byte units per thread and round, all loaded before any is stored, so that each
+    // thread keeps four loads in flight; units past the end re-read the last one and are not stored
+    const size_t G = (size_t)gridDim.x * 256;
+    for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n16; u += 4 * G) {
+        uint4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const size_t ui = u + i * G < n16 ? u + i * G : n16 - 1;
+            v[i] = gload16(src_of(ui * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (u + i * G < n16) *(uint4*)(dst + (u + i * G) * 16) = v[i];
     }
     moe_expert m;
     m.gate_q = dst;

@@ -30,9 +30,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 template <int SS>
 __device__ __forceinline__ uint32_t load_scale_word(const uint8_t* p) {
-    if constexpr (SS == 4) return *(const uint32_t*)p;
-    else if constexpr (SS == 2) return *(const uint16_t*)p;
-    else return *p;
+    if constexpr (SS == 4) return gload4(p);
+    else if constexpr (SS == 2) return *(__attribute__((address_space(1))) const uint16_t*)p;
+    else return *(__attribute__((address_space(1))) const uint8_t*)p;
 }
 
 __device__ __forceinline__ v4f mfma_fp4_fp8(const uint4& a, const uint4& b0, const uint4& b1, v4f c,
@@ -62,19 +62,19 @@ __device__ __forceinline__ void mx_accumulate(const uint8_t* const (&aq)[NA], co
             const size_t s = (size_t)(s0 + c);
 #pragma unroll
             for (int f = 0; f < NA; ++f) {
-                const uint4* p = (const uint4*)(aq[f] + s * 64 * SS);
+                const uint8_t* p = aq[f] + s * 64 * SS;
 #pragma unroll
-                for (int h = 0; h < SS; ++h) A[c][f][h] = p[h];
+                for (int h = 0; h < SS; ++h) A[c][f][h] = gload16(p + 16 * h);
                 sa[c][f] = load_scale_word<SS>(as[f] + s * 4 * SS);
             }
 #pragma unroll
             for (int n = 0; n < NTN; ++n) {
                 if (bval[n]) {
-                    const uint4* p = (const uint4*)(bq[n] + s * 128 * SS);
+                    const uint8_t* p = bq[n] + s * 128 * SS;
 #pragma unroll
                     for (int h = 0; h < SS; ++h) {
-                        B[c][n][h][0] = p[2 * h];
-                        B[c][n][h][1] = p[2 * h + 1];
+                        B[c][n][h][0] = gload16(p + 32 * h);
+                        B[c][n][h][1] = gload16(p + 32 * h + 16);
                     }
                     sb[c][n] = load_scale_word<SS>(bs[n] + s * 4 * SS);
                 } else {

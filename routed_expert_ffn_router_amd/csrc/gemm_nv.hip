@@ -146,14 +146,14 @@ __global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
         uint32_t sc[NA];
 #pragma unroll
         for (int f = 0; f < NA; ++f) {
-            A[f] = *(const uint4*)(aq[f] + (size_t)s * 64);
-            sc[f] = *(const uint16_t*)(as[f] + (size_t)s * 8);
+            A[f] = gload16(aq[f] + (size_t)s * 64);
+            sc[f] = *(__attribute__((address_space(1))) const uint16_t*)(as[f] + (size_t)s * 8);
         }
         uint4 B[NCF][4];
 #pragma unroll
         for (int n = 0; n < NCF; ++n)
 #pragma unroll
-            for (int h = 0; h < 4; ++h) B[n][h] = *(const uint4*)(bp[n] + (size_t)s * 128 + 8 * h);
+            for (int h = 0; h < 4; ++h) B[n][h] = gload16(bp[n] + (size_t)s * 128 + 8 * h);
 #pragma unroll
         for (int f = 0; f < NA; ++f) {
             const v2f_t bs = e4m3x2_to_f32(sc[f]);
@@ -308,8 +308,8 @@ __global__ __launch_bounds__(256) void k_nv_pf(GemmArgs a, int tiles_per_xcd_cap
     auto load_step = [&](int st) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) vA[i] = gload16(srcA[i] + (size_t)st * 64);
-        vS0 = *(const uint2*)(srcS0 + (size_t)st * 8);
-        vS1 = *(const uint2*)(srcS1 + (size_t)st * 8);
+        vS0 = gload8(srcS0 + (size_t)st * 8);
+        vS1 = gload8(srcS1 + (size_t)st * 8);
 #pragma unroll
         for (int i = 0; i < NBC; ++i) vB[i] = gload16(srcB[i] + (size_t)st * 256);
     };
