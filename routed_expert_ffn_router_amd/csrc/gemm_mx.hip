@@ -114,10 +114,14 @@ __device__ __forceinline__ void sum_terms(v4f (&acc)[NA][NTN]) {
 
 template <int NT, int NTN, int KSPLIT, int SS, bool GATEUP>
 __global__ __launch_bounds__(256) void k_mx_gemm(GemmArgs a, int ss2) {
-    constexpr int NA = GATEUP ? 4 : 2;      // A fragments per MFMA step
+    // output rows per row group: 32 (gate/up: the same 32 rows of gate and of up); down with K split
+    // four ways 64, so that a workgroup streams as many weight bytes as a gate/up one (with 32, twice
+    // the workgroups each brought half the bytes, and down ran at about 70% of gate/up's rate)
+    constexpr int RB = (GATEUP || KSPLIT != 4) ? 32 : 64;
+    constexpr int NA = GATEUP ? 4 : RB / 16;  // A fragments per MFMA step
     // tokens per tile: the tile's columns, at most the tokens a few-token tile record holds
     constexpr int TT = (16 * NTN / NT) < kDescTokens ? 16 * NTN / NT : kDescTokens;
-    constexpr int CH = GATEUP ? 1 : 2;
+    constexpr int CH = NA == 4 ? 1 : 2;      // super-steps per load burst: 16 weight loads per lane either way
     const int tile = blockIdx.x;
     if (tile >= *a.ntiles) return;
     const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(256) void k_mx_gemm(GemmArgs a, int ss2) {
 
     // row group owned by this wave: one natural 32-row block of the output
     const int rg = (KSPLIT == 4) ? blockIdx.y : (blockIdx.y * 4 + wave);
-    const int T0 = 32 * rg, T1 = T0 + 16;
+    const int T0 = RB * rg, T1 = T0 + 16;
     const int kw = (KSPLIT == 4) ? wave : 0;
     const int nss = (K / KSPLIT) / (128 * SS);
     const int kss0 = kw * nss;  // first super-step of this wave
@@ -143,7 +147,8 @@ __global__ __launch_bounds__(256) void k_mx_gemm(GemmArgs a, int ss2) {
         const uint8_t* ms1 = GATEUP ? ex.up_s : ex.down_s;
 #pragma unroll
         for (int f = 0; f < NA; ++f) {
-            const int row = ((f & 1) ? T1 : T0) + li;
+            // gate/up: gate rows T0, T1 then up rows T0, T1; down: rows T0 + 16 f
+            const int row = GATEUP ? ((f & 1) ? T1 : T0) + li : T0 + 16 * f + li;
             const uint8_t* mq = (f < 2) ? mq0 : mq1;
             const uint8_t* ms = (f < 2) ? ms0 : ms1;
             aq[f] = mq + (size_t)row * (K / 2) + lg * 16 * SS + (size_t)kss0 * 64 * SS;
@@ -233,8 +238,10 @@ __global__ __launch_bounds__(256) void k_mx_gemm(GemmArgs a, int ss2) {
             const int tc = n * (16 / NT) + li / NT;
             if (tc < ntok && (li % NT) == 0) {
                 float* dst = a.o + ((size_t)i0 + tc) * a.d;
-                *(float4*)(dst + T0 + 4 * lg) = make_float4(acc[0][n][0], acc[0][n][1], acc[0][n][2], acc[0][n][3]);
-                *(float4*)(dst + T1 + 4 * lg) = make_float4(acc[1][n][0], acc[1][n][1], acc[1][n][2], acc[1][n][3]);
+#pragma unroll
+                for (int f = 0; f < NA; ++f)
+                    *(float4*)(dst + T0 + 16 * f + 4 * lg) =
+                        make_float4(acc[f][n][0], acc[f][n][1], acc[f][n][2], acc[f][n][3]);
             }
         }
     }
@@ -1162,7 +1169,8 @@ static hipError_t launch_gemm(const GemmArgs& a, int NT, int variant, int max_ti
     const int ks = ksplit_for(K, variant);
     const int SS = super_step(K, ks);
     const int ss2 = super_step(a.f, ksplit_for(a.f, variant));
-    dim3 grid(max_tiles, (rows / 32) / (ks == 4 ? 1 : 4));
+    // row groups of 32 rows (64 for down with K split four ways: k_mx_gemm's RB)
+    dim3 grid(max_tiles, ks == 4 ? rows / (GATEUP ? 32 : 64) : (rows / 32) / 4);
     if (variant == 0) {
         if (ks == 4) return NT == 1 ? launch_one<GATEUP, 1, 1, 4>(a, SS, ss2, grid, st)
                           : NT == 2 ? launch_one<GATEUP, 2, 1, 4>(a, SS, ss2, grid, st)
