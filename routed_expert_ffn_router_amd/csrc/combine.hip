@@ -16,15 +16,30 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, co
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= d) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const float wj = w[(size_t)t * k + j];
-        const int pos = pick_pos[(size_t)t * k + j];
-        if (pos < 0) continue;                  // a pick without an expert (dropped or refused)
-        const float4 v = *(const float4*)(o + (size_t)pos * d + c);
-        acc.x = fmaf(wj, v.x, acc.x);
-        acc.y = fmaf(wj, v.y, acc.y);
-        acc.z = fmaf(wj, v.z, acc.z);
-        acc.w = fmaf(wj, v.w, acc.w);
+    // eight picks at a time: their positions and weights, then all eight partial loads, then the
+    // sums in rank order (so the loads are in flight together, not one round trip per pick).  A
+    // pick without an expert (dropped or refused, position -1), or past k, reads row 0 and adds
+    // nothing.
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        int pos[8];
+        float wj[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = j0 + i;
+            pos[i] = j < k ? pick_pos[(size_t)t * k + j] : -1;
+            wj[i] = j < k ? w[(size_t)t * k + j] : 0.0f;
+        }
+        float4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = *(const float4*)(o + (size_t)(pos[i] >= 0 ? pos[i] : 0) * d + c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bool use = pos[i] >= 0;
+            acc.x = use ? fmaf(wj[i], v[i].x, acc.x) : acc.x;
+            acc.y = use ? fmaf(wj[i], v[i].y, acc.y) : acc.y;
+            acc.z = use ? fmaf(wj[i], v[i].z, acc.z) : acc.z;
+            acc.w = use ? fmaf(wj[i], v[i].w, acc.w) : acc.w;
+        }
     }
     float r[4] = {acc.x * scaling, acc.y * scaling, acc.z * scaling, acc.w * scaling};
     if (shared) {
