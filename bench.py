@@ -250,6 +250,17 @@ def expert_entry(m, synth, wl, ptr):
     return bytes(e)
 
 
+def issued_mfma(flops, terms, ms, kern):
+    """MFMA use against the instruction rate actually issued: the split activations make `terms`
+    FP8 columns per value, so the scaled FP4 x FP8 MFMAs issue terms x the algorithmic FLOPs, at the
+    FP8 rate; over the layer and over its two GEMM kernels alone."""
+    issued = terms * flops
+    gemm_us = kern.get("gemm_gate_up", 0.0) + kern.get("gemm_down", 0.0)
+    return {"activation_terms": terms,
+            "issued_fp8_mfma_frac": issued / (ms * 1e-3) / (FP8_PEAK_TFLOPS * 1e12),
+            "gemm_issued_fp8_mfma_frac": issued / (gemm_us * 1e-6) / (FP8_PEAK_TFLOPS * 1e12) if gemm_us else None}
+
+
 def time_graph(hip, S, step, reps, warm=3):
     """Capture step() on stream S as one graph; returns (ms per replay, graph)."""
     gexec, _ = hip.capture(S, step)
@@ -388,6 +399,7 @@ def rows_legs(args, m, synth, torch, np, hip, stream, S, stack, oracle, parity, 
     rec["mxfp8_activations"] = {"workload": "prefill chunk T=4096, opt-in MXFP8 activations (one E4M3 term)",
                                 "ms_per_layer": ms, "tokens_per_s": T / (ms * 1e-3),
                                 "fp4_mfma_frac": flops / (ms * 1e-3) / (FP4_PEAK_TFLOPS * 1e12),
+                                **issued_mfma(flops, 1, ms, {k: float(np.mean(v)) for k, v in per.items()}),
                                 "kernels_us": {k: float(np.mean(v)) for k, v in per.items()}}
     log(f"# MXFP8 activations, prefill T=4096: {ms:.3f} ms/layer; kernels (us): "
         + ", ".join(f"{k} {v:.1f}" for k, v in rec["mxfp8_activations"]["kernels_us"].items()))
@@ -594,6 +606,8 @@ def main():
             "hbm_frac": bytes_ / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "fp4_mfma_frac": flops / (ms * 1e-3) / (FP4_PEAK_TFLOPS * 1e12),
             "roofline_frac": floor_ms / ms, "kernels_us": kern,
+            # the MFMAs actually issued: each activation as `terms` FP8 columns, FP4 x FP8 at the FP8 rate
+            **issued_mfma(flops, 2 if wl.act_dtype == 1 else 4, ms, kern),
         }
         log(f"# prefill T={T}: {ms:.3f} ms/layer, {T / ms * 1e3:.0f} tokens/s, "
             f"{100 * out['prefill']['roofline_frac']:.1f}% of the roofline bound")
