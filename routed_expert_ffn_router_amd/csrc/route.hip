@@ -548,31 +548,53 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
         const float* row = a.wr + (size_t)(e < E ? e : 0) * d + (size_t)part * pl;
 #pragma unroll
         for (int u = 0; u < NC; ++u) w4[u] = *(const float4*)(row + at(u));
-        // 2. logits, fp64 accumulation of exact products (the parts of a row added in order)
+        // 2. logits, fp64 accumulation of exact products (the parts of a row added in order), TB
+        // tokens at a time so that their loads are in flight together (past T: the last token
+        // again, not stored); one token alone does no extra work
         __shared__ double s_part[4][kSmallT];
-        if (e < E) {
+        auto logits = [&](auto tb) {
+            constexpr int TB = decltype(tb)::value;
 #pragma unroll 1
-            for (int t = 0; t < T; ++t) {
-                const XT* xt = x + (size_t)t * d + (size_t)part * pl;
-                float4 x4[NC];
+            for (int t0 = 0; t0 < T; t0 += TB) {
+                float4 x4[TB][NC];
 #pragma unroll
-                for (int u = 0; u < NC; ++u) x4[u] = load_act4(xt, at(u));
-                double acc = 0.0;
+                for (int b = 0; b < TB; ++b) {
+                    const XT* xt = x + (size_t)min(t0 + b, T - 1) * d + (size_t)part * pl;
 #pragma unroll
-                for (int u = 0; u < NC; ++u) {
-                    double p = fma((double)x4[u].x, (double)w4[u].x, acc);
-                    p = fma((double)x4[u].y, (double)w4[u].y, p);
-                    p = fma((double)x4[u].z, (double)w4[u].z, p);
-                    p = fma((double)x4[u].w, (double)w4[u].w, p);
-                    acc = used(u) ? p : acc;
+                    for (int u = 0; u < NC; ++u) x4[b][u] = load_act4(xt, at(u));
                 }
-                acc = wave_sum_f64(acc);
-                if constexpr (WPR == 1) {
-                    if (lane == 0) put_slot(a.slots + (size_t)t * E + e, a.bias ? acc + (double)a.bias[e] : acc);
-                } else {
-                    if (lane == 0) s_part[wave][t] = acc;
+                double acc[TB];
+#pragma unroll
+                for (int b = 0; b < TB; ++b) {
+                    acc[b] = 0.0;
+#pragma unroll
+                    for (int u = 0; u < NC; ++u) {
+                        double p = fma((double)x4[b][u].x, (double)w4[u].x, acc[b]);
+                        p = fma((double)x4[b][u].y, (double)w4[u].y, p);
+                        p = fma((double)x4[b][u].z, (double)w4[u].z, p);
+                        p = fma((double)x4[b][u].w, (double)w4[u].w, p);
+                        acc[b] = used(u) ? p : acc[b];
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < TB; ++b) acc[b] = wave_sum_f64(acc[b]);
+#pragma unroll
+                for (int b = 0; b < TB; ++b) {
+                    const int t = t0 + b;
+                    if (t < T && lane == 0) {
+                        if constexpr (WPR == 1)
+                            put_slot(a.slots + (size_t)t * E + e, a.bias ? acc[b] + (double)a.bias[e] : acc[b]);
+                        else
+                            s_part[wave][t] = acc[b];
+                    }
                 }
             }
+        };
+        if (e < E) {
+            if (T == 1)
+                logits(std::integral_constant<int, 1>{});
+            else
+                logits(std::integral_constant<int, 4>{});
         }
         if constexpr (WPR > 1) {
             __syncthreads();
@@ -594,8 +616,9 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
     // the routing workgroup
     __shared__ int32_t s_idx[kMaxFusedPicks];
     __shared__ float s_w[kMaxFusedPicks];
-    __shared__ int32_t s_sorted[kMaxFusedPicks];    // sorted position -> pick
-    __shared__ uint8_t s_start[kMaxFusedPicks];     // sorted position starts a tile
+    __shared__ uint32_t s_tm[64 * S];               // per expert: the tokens that picked it
+    __shared__ uint32_t s_off[64 * S];              // per expert: picks and tiles of lower experts
+    __shared__ uint32_t s_wsum[4];
     __shared__ uint4 s_cand[4][128];                // top-k candidates, per wave
     __shared__ unsigned long long s_rk[4][8];       // keys of the picks in rank order, per wave
     const int P = T * k, tt = a.tt;
@@ -890,6 +913,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
             if (g < 4 * E) s_tab[g] = tab[r];
         }
     }
+    for (int e = tid; e < E; e += 256) s_tm[e] = 0u;   // (the barrier after the top-k orders these)
     // wave w routes tokens w, w + 4, ...; J of them per round of polls (lane l: experts l + 64 s).
     // Every poll load is issued without a condition (indices past T or E re-read the last slot
     // and are not used), so that all of them are in flight together.
@@ -928,133 +952,112 @@ __global__ __launch_bounds__(256) void k_route_small(RouteSmallArgs a) {
                 const int t = t0 + 4 * j, e = lane + 64 * s;
                 if (t < T && e < E) clear_slot(a.slots + (size_t)t * E + e);
             }
-#pragma unroll
+        // the round's tokens one after another in a rolled loop: one copy of the top-k code, warm in
+        // the instruction cache after the first token (the keys are taken out of kv by selects, so
+        // that kv stays in registers)
+#pragma unroll 1
         for (int j = 0; j < J; ++j) {
             const int t = t0 + 4 * j;
-            if (t < T) {
-                unsigned long long my_key = 0ull;
-                if (k > 8 || !topk_pass<S>(kv[j], E, k, s_idx + t * k, s_cand[wave], s_rk[wave], my_key))
-                    my_key = topk_rounds<S>(kv[j], E, k, s_idx + t * k);
-                topk_weights(my_key, nullptr, s_idx + t * k, k, s_w + t * k, nullptr, tau);
+            if (t >= T) break;
+            unsigned long long cur[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                cur[s] = kv[0][s];
+#pragma unroll
+                for (int jj = 1; jj < J; ++jj) cur[s] = j == jj ? kv[jj][s] : cur[s];
             }
+            unsigned long long my_key = 0ull;
+            if (k > 8 || !topk_pass<S>(cur, E, k, s_idx + t * k, s_cand[wave], s_rk[wave], my_key))
+                my_key = topk_rounds<S>(cur, E, k, s_idx + t * k);
+            topk_weights(my_key, nullptr, s_idx + t * k, k, s_w + t * k, nullptr, tau);
         }
     }
     if (lane == 0) s_fail[wave] = gave_up ? 1 : 0;
-    __syncthreads();
+    lds_barrier();
     if (s_fail[0] | s_fail[1] | s_fail[2] | s_fail[3]) {
         put_refused(a.desc, a.idx, a.w, a.pick_pos, a.sorted_pick, a.offsets, a.ntiles);
         return;
     }
-    // the expert offsets: the number of picks of lower experts (a dropped pick, id -1, is no
-    // expert's: as unsigned it is above every id)
-    auto put_offsets = [&]() {
-        for (int e = tid; e <= E; e += 256) {
-            int lower = 0;
-#pragma unroll 8
-            for (int q = 0; q < P; ++q) lower += (uint32_t)s_idx[q] < (uint32_t)e;
-            a.offsets[e] = lower;
-        }
-    };
-    // kept picks (P unless renorm-skip dropped some: they are no expert's and take no position)
-    int Pv = P;
-    if (tau > 0.0f) {
-        Pv = 0;
-#pragma unroll 8
-        for (int q = 0; q < P; ++q) Pv += s_idx[q] >= 0;
-        for (int i = Pv + tid; i < P; i += 256) a.sorted_pick[i] = -1;
+    // Grouping, without a pass over the picks per pick (P <= 512, T <= 16).  A token picks an
+    // expert at most once, so each expert's picks are a set of tokens: a bit mask (dropped picks, id
+    // -1, are in none).  A pick's sorted position is the number of kept picks of lower experts plus
+    // the number of earlier tokens of its own expert, and it starts a tile when that number is a
+    // multiple of tt.  One exclusive scan over the experts gives both per-expert prefixes: picks
+    // (the expert offsets) in the low 16 bits, tiles (the first record id) in the high 16 bits.
+    for (int p = tid; p < P; p += 256) {
+        const int e = s_idx[p];
+        if (e >= 0) atomicOr(&s_tm[e], 1u << (p / k));
     }
-    if (T == 1) {
-        // one token (more than kTabLds experts): each kept pick is a tile of its own, as above
-        for (int p = tid; p < k; p += 256) {
-            const int e = s_idx[p];
-            if (e < 0) {
-                a.idx[p] = -1;
-                a.w[p] = 0.0f;
-                a.pick_pos[p] = -1;
-                continue;
-            }
-            int pos = 0;
-#pragma unroll 8
-            for (int q = 0; q < k; ++q) pos += (uint32_t)s_idx[q] < (uint32_t)e;
-            TileDesc* D = a.desc + pos;
-            put_expert(D, e);
-            D->i0 = pos;
-            D->ntok = 1;
-            D->e = e;
-            D->pad0 = 0;
+    lds_barrier();
+    const int Q = (E + 255) / 256, e0 = tid * Q;        // Q <= 4 consecutive experts per thread
+    uint32_t cnt[4], own = 0u;
 #pragma unroll
-            for (int c = 0; c < kDescTokens; ++c) D->tok[c] = 0;
-            a.tiles[2 * pos] = e;
-            a.tiles[2 * pos + 1] = pos;
-            a.idx[p] = e;
-            a.w[p] = s_w[p];
-            a.pick_pos[p] = pos;
-            a.sorted_pick[pos] = p;
-        }
-        put_offsets();
-        const int nall = Pv + put_shared(a.desc, a.tiles, Pv, tid, 256);
-        for (int id = nall + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id, s_idx[0]);
-        if (tid == 0) *a.ntiles = nall;
-        return;
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t n = (i < Q && e0 + i < E) ? (uint32_t)__popc(s_tm[e0 + i]) : 0u;
+        cnt[i] = n | (((n + tt - 1) / tt) << 16);
+        own += cnt[i];
     }
-    // Grouping without atomics or scans (P <= 512, two picks per thread): a pick's sorted
-    // position is the number of picks of lower experts plus its rank among the picks of its own
-    // expert; it starts a tile when that rank is a multiple of tt.
-    int pos[2], rank[2], cnt[2];
+    uint32_t inc = own;                                  // inclusive scan over the wave
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int p = tid + 256 * u;
-        pos[u] = -1;
-        if (p < P && s_idx[p] < 0) {           // dropped: no expert, no position
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_up((int)inc, o);
+        inc += lane >= o ? v : 0u;
+    }
+    if (lane == 63) s_wsum[wave] = inc;
+    lds_barrier();
+    const uint32_t total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    uint32_t ex = inc - own;
+    for (int w = 0; w < wave; ++w) ex += s_wsum[w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i < Q && e0 + i < E) {
+            s_off[e0 + i] = ex;
+            a.offsets[e0 + i] = (int32_t)(ex & 0xffffu);
+        }
+        ex += cnt[i];
+    }
+    const int Pv = (int)(total & 0xffffu);              // kept picks
+    if (tid == 0) a.offsets[E] = Pv;
+    lds_barrier();
+    for (int p = tid; p < P; p += 256) {
+        const int e = s_idx[p];
+        if (e < 0) {                                     // dropped: no expert, no position
             a.idx[p] = -1;
             a.w[p] = 0.0f;
             a.pick_pos[p] = -1;
-        } else if (p < P) {
-            const int e = s_idx[p];
-            int lower = 0, before = 0, same = 0;
-#pragma unroll 8
-            for (int q = 0; q < P; ++q) {
-                const int eq = s_idx[q];
-                lower += (uint32_t)eq < (uint32_t)e;
-                same += eq == e;
-                before += (eq == e) & (q < p);
-            }
-            pos[u] = lower + before;
-            rank[u] = before;
-            cnt[u] = same;
-            s_sorted[pos[u]] = p;
-            s_start[pos[u]] = (before % tt) == 0;
-            a.idx[p] = e;
-            a.w[p] = s_w[p];
-            a.pick_pos[p] = pos[u];
-            a.sorted_pick[pos[u]] = p;
+            continue;
         }
-    }
-    put_offsets();
-    __syncthreads();
-    // tiles: numbered by sorted position of their first pick
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        if (pos[u] >= 0 && s_start[pos[u]]) {
-            int id = 0;
-#pragma unroll 8
-            for (int q = 0; q < pos[u]; ++q) id += s_start[q];
-            const int ntok = min(tt, cnt[u] - rank[u]);
+        const int t = p / k;
+        const uint32_t m = s_tm[e], o = s_off[e];
+        const int before = __popc(m & ((1u << t) - 1u)), pos = (int)(o & 0xffffu) + before;
+        a.idx[p] = e;
+        a.w[p] = s_w[p];
+        a.pick_pos[p] = pos;
+        a.sorted_pick[pos] = p;
+        if (before % tt == 0) {
+            // a tile: this expert's tokens from t on (t is its first), at most tt of them
+            const int id = (int)(o >> 16) + before / tt, ntok = min(tt, __popc(m) - before);
             TileDesc* D = a.desc + id;
-            put_expert(D, s_idx[tid + 256 * u]);
-            D->i0 = pos[u];
+            put_expert(D, e);
+            D->i0 = pos;
             D->ntok = ntok;
-            D->e = s_idx[s_sorted[pos[u]]];
+            D->e = e;
             D->pad0 = 0;
-            for (int c = 0; c < kDescTokens; ++c) D->tok[c] = c < ntok ? s_sorted[pos[u] + c] / k : 0;
-            a.tiles[2 * id] = D->e;
-            a.tiles[2 * id + 1] = pos[u];
+            uint32_t mm = m >> t;
+#pragma unroll
+            for (int c = 0; c < kDescTokens; ++c) {
+                D->tok[c] = c < ntok ? t + __builtin_ctz(mm | 0x80000000u) : 0;
+                mm &= mm - 1u;
+            }
+            a.tiles[2 * id] = e;
+            a.tiles[2 * id + 1] = pos;
         }
     }
-    // the tile count, and empty records up to max_tiles
-    int nt = 0;
-#pragma unroll 8
-    for (int q = 0; q < Pv; ++q) nt += s_start[q];
+    if (tau > 0.0f)
+        for (int i = Pv + tid; i < P; i += 256) a.sorted_pick[i] = -1;
+    // the tile count (the shared expert's tiles after the routed ones), and empty records up to
+    // max_tiles
+    int nt = (int)(total >> 16);
     nt += put_shared(a.desc, a.tiles, nt, tid, 256);
     for (int id = nt + tid; id < a.max_tiles; id += 256) put_empty(a.desc, id, s_idx[0]);
     if (tid == 0) *a.ntiles = nt;

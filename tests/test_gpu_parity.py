@@ -132,6 +132,10 @@ SMALL_CASES = [
     # fused router: k > 8 takes the k-round top-k; E > 320 holds 16 logits per lane
     ("tiny", dict(n_experts=64, top_k=12), 3),
     ("tiny", dict(n_experts=400, top_k=8, act_dtype=synth.BF16), 5),
+    ("tiny", dict(n_experts=400, top_k=8, act_dtype=synth.BF16), 1),
+    ("tiny", dict(n_experts=400, top_k=8, act_dtype=synth.BF16), 16),
+    # fused router, 16 tokens on four experts: an expert's tokens fill more than one tile
+    ("tiny", dict(n_experts=4, top_k=2), 16),
 ]
 
 
