@@ -546,12 +546,17 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs 
 
 // down projection + weighted combine for very few picks (P * NT <= 32, d_ff <= 2048): one
 // workgroup of 16 output rows per CU.  Round trip 1 fetches the tile records and the combine's
-// inputs; then every pick's h terms are requested (for LDS) ahead of each wave's weight loads for
-// two (tile, K slice) units, so the FP8 operand comes from LDS and costs no registers.
+// inputs.  Then waves 4-7 request the weights of their two (tile, K slice) units at once, while
+// waves 0-3 first stage every pick's h terms in LDS and only then request theirs: a wave cannot
+// get past a long run of load instructions until the CU's memory pipeline has taken them, so an
+// LDS store placed after its weight requests would wait for most of the weight stream.  Each wave
+// waits for the staged h terms (an LDS counter, not a barrier) just before its MFMAs.
 constexpr int kDownLdsCols = 32;
 constexpr int kDownMaxF = 2048;
 constexpr int kDownMaxTiles = 32;
-constexpr int kDownFillRounds = (kDownLdsCols * (kDownMaxF / 16 + kDownMaxF / 512) + 511) / 512;
+constexpr int kDownFillThreads = 256;      // waves 0-3 stage the h terms
+constexpr int kDownFillRounds =
+    (kDownLdsCols * (kDownMaxF / 16 + kDownMaxF / 512) + kDownFillThreads - 1) / kDownFillThreads;
 
 template <typename XT, int NT, bool PLAIN>
 __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineArgs c) {
@@ -563,6 +568,7 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
     __shared__ float o_part[kMaxDecSlices][MAXP][16];
     __shared__ float s_wq[MAXP];
     __shared__ int s_posq[MAXP];
+    __shared__ int s_staged;                        // filler waves done with the h terms
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
@@ -588,23 +594,48 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
         s_wq[tid] = wq;
         s_posq[tid] = posq;
     }
+    if (tid == 0) s_staged = 0;
     __syncthreads();
-    // 2. every pick's h codes and scales (first P*NT rows of the h terms) for LDS: requested
-    // before the weights, so that waiting for them does not wait for the weights; only the rounds
-    // that hold chunks (the round count is uniform)
+    // 2. every pick's h codes and scales (first P*NT rows of the h terms), by waves 0-3: all
+    // requests of a wave first, then its LDS stores (only the rounds that hold chunks; the round
+    // count is uniform)
     const int nb = ncols * (K / 16), ntot = nb + ncols * (K / 512);
-    uint4 v[kDownFillRounds];
+    const bool filler = wave < kDownFillThreads / 64;
+    auto stage_h = [&]() {
+        uint4 v[kDownFillRounds];
 #pragma unroll
-    for (int r = 0; r < kDownFillRounds; ++r) {
-        if (r * 512 < ntot) {
-            int g = r * 512 + tid;
-            g = g < ntot ? g : ntot - 1;
-            // one address by selects, one load: no branch between the loads of the round
-            const uintptr_t base = g < nb ? (uintptr_t)a.aq : (uintptr_t)a.as;
-            const int gi = g < nb ? g : g - nb;
-            v[r] = gload16((const void*)(base + (size_t)gi * 16));
+        for (int r = 0; r < kDownFillRounds; ++r) {
+            if (r * kDownFillThreads < ntot) {
+                int g = r * kDownFillThreads + tid;
+                g = g < ntot ? g : ntot - 1;
+                // one address by selects, one load: no branch between the loads of the round
+                const uintptr_t base = g < nb ? (uintptr_t)a.aq : (uintptr_t)a.as;
+                const int gi = g < nb ? g : g - nb;
+                v[r] = gload16((const void*)(base + (size_t)gi * 16));
+            }
         }
-    }
+#pragma unroll
+        for (int r = 0; r < kDownFillRounds; ++r) {
+            const int g = r * kDownFillThreads + tid;
+            if (g < nb) {
+                const int col = g / (K / 16);
+                *(uint4*)&b_lds[col][(g % (K / 16)) * 16] = v[r];
+            } else if (g < ntot) {
+                const int gg = g - nb, col = gg / (K / 512);
+                *(uint4*)&bs_lds[col][(gg % (K / 512)) * 16] = v[r];
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);            // this wave's LDS stores are done
+        asm volatile("" ::: "memory");
+        if (lane == 0) atomicAdd(&s_staged, 1);
+    };
+    // the staged h terms: wait until the four filler waves have counted themselves in (an atomic
+    // read: a volatile one would also wait for this wave's weight loads)
+    auto wait_h = [&]() {
+        while (__hip_atomic_load(&s_staged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kDownFillThreads / 64)
+            __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");
+    };
     // 3. the weights of this wave's first two units (tile, K slice): u0 = wave, u1 = wave + 8
     const int units = a.max_tiles * nsl;
     const int tc = li / NT, t = li % NT;
@@ -674,24 +705,13 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec_lds(GemmArgs a, CombineA
     uint32_t sa[2][NSS];
     bool ok0, ok1;
     int us[2];
+    if (filler) stage_h();
+    __builtin_amdgcn_sched_barrier(0);
     load_units(wave, A, sa, ok0, ok1, us);
     __builtin_amdgcn_sched_barrier(0);
-    // 4. h terms into LDS, then the MFMAs of the first units
-#pragma unroll
-    for (int r = 0; r < kDownFillRounds; ++r)
-        if (r * 512 < ntot) asm volatile("" ::"v"(v[r].x), "v"(v[r].y), "v"(v[r].z), "v"(v[r].w));
-#pragma unroll
-    for (int r = 0; r < kDownFillRounds; ++r) {
-        const int g = r * 512 + tid;
-        if (g < nb) {
-            const int col = g / (K / 16);
-            *(uint4*)&b_lds[col][(g % (K / 16)) * 16] = v[r];
-        } else if (g < ntot) {
-            const int gg = g - nb, col = gg / (K / 512);
-            *(uint4*)&bs_lds[col][(gg % (K / 512)) * 16] = v[r];
-        }
-    }
-    lds_barrier();          // not waiting for the weights: each unit's MFMAs start when its own are in
+    // 4. the MFMAs of the first units, once the h terms are staged (each unit's MFMAs start when
+    // its own weights are in)
+    wait_h();
     run_units(A, sa, ok0, ok1, us);
     for (int u0 = wave + 16; u0 < units; u0 += 16) {      // more than sixteen units: further pairs
         if (!unit_ok(u0) && !unit_ok(u0 + 8)) continue;       // (none of them holds a tile)
