@@ -818,19 +818,24 @@ hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineA
 }
 
 int gemm_variant(const moe_shape* s, int T) {
-    const long long P = (long long)T * s->top_k;
-    return (P <= 8LL * s->n_experts) ? 0 : 1;
+    const long long P = (long long)T * s->top_k, E = s->n_experts;
+    const int NT = act_terms(s);
+    // few-pick tiles up to 5/8 of a tile's picks per expert on average (measured crossover at d_model
+    // 4096, d_ff 2048, 288 experts: between 4.4 and 5.3 picks per expert), then the 64-column tile
+    // up to its picks per expert, then the 128-column tile
+    if (8 * P <= 5LL * gemm_tile_tokens(0, NT) * E) return 0;
+    return P <= (long long)(64 / NT) * E ? 2 : 1;
 }
 
 // picks per tile: the MFMA columns over the terms per value; a few-token tile also at most the
 // tokens its tile record holds
 int gemm_tile_tokens(int variant, int NT) {
     if (variant == 0) return 16 / NT < kDescTokens ? 16 / NT : kDescTokens;
-    return 128 / NT;
+    return (variant == 2 ? 64 : 128) / NT;
 }
 
 // activation layout super-step for the variant: the LDS-tiled many-picks GEMM reads chunks of 128
-int act_super_step(int K, int variant) { return variant == 1 ? 1 : super_step(K, ksplit_for(K, variant)); }
+int act_super_step(int K, int variant) { return variant >= 1 ? 1 : super_step(K, ksplit_for(K, variant)); }
 
 int super_step(int K, int ksplit) {
     const int span = K / ksplit;
@@ -875,8 +880,11 @@ static hipError_t launch_one(const GemmArgs& a, int SS, int ss2, dim3 grid, hipS
 constexpr int kPfRows = 256, kPfCols = 128;
 constexpr int kPfA = 0, kPfB = 16384, kPfStage = 32768;
 constexpr int kScA = 0, kScB = 4096, kScSlot = 6144;
-constexpr int kPfLoads = 8;                   // direct loads per wave and stage
-constexpr int kScLoads = 6;                   // direct loads per wave and group of four steps
+// NCF = MFMA column fragments per wave: 4 (128 columns per workgroup) or 2 (64 columns, the
+// narrow tile for 8-32 picks per expert: half the MFMAs and B-side LDS work per step, the same
+// weight bytes)
+template <int NCF> constexpr int pf_loads() { return 4 + NCF; }       // direct loads per wave and stage
+template <int NCF> constexpr int sc_loads() { return 4 + NCF / 2; }   // per wave and group of four steps
 
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 __device__ __forceinline__ int swz_b(int c) { return ((c >> 1) ^ ((c & 1) << 2)) & 7; }
@@ -890,7 +898,7 @@ struct PfFrags {
 };
 
 // fragments of one step: stg = its stage, sc = its scale slot, w = the step's index in its group
-template <bool GATEUP>
+template <bool GATEUP, int NCF>
 __device__ __forceinline__ void pf_read(const uint8_t* stg, const uint8_t* sc, int w, PfFrags& fr, int wm,
                                         int wn, int lane) {
     const int lg = lane >> 4, li = lane & 15;
@@ -901,8 +909,8 @@ __device__ __forceinline__ void pf_read(const uint8_t* stg, const uint8_t* sc, i
         fr.sa[j] = sc[kScA + (fa * 16 + li) * 16 + w * 4 + lg];      // scale byte of K block lg
     }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int col = (wn * 4 + n) * 16 + li;
+    for (int n = 0; n < NCF; ++n) {
+        const int col = (wn * NCF + n) * 16 + li;
         const uint8_t* cp = stg + kPfB + col * 128;
         fr.b[n][0] = *(const uint4*)(cp + (((2 * lg) ^ swz_b(li)) * 16));
         fr.b[n][1] = *(const uint4*)(cp + (((2 * lg + 1) ^ swz_b(li)) * 16));
@@ -910,17 +918,19 @@ __device__ __forceinline__ void pf_read(const uint8_t* stg, const uint8_t* sc, i
     }
 }
 
-__device__ __forceinline__ void pf_mfma(const PfFrags& fr, v4f (&acc)[8][4]) {
+template <int NCF>
+__device__ __forceinline__ void pf_mfma(const PfFrags& fr, v4f (&acc)[8][NCF]) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < NCF; ++n)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             acc[j][n] = mfma_fp4_fp8(fr.a[j], fr.b[n][0], fr.b[n][1], acc[j][n], fr.sa[j], fr.sb[n]);
 }
 
 
-// FULL: 0, or the step count K / 128 that this instance runs as straight-line code
-template <int NT, bool GATEUP, int FULL>
+// FULL: 0, or the step count K / 128 that this instance runs as straight-line code; NCF: column
+// fragments per wave (above)
+template <int NT, bool GATEUP, int FULL, int NCF>
 __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles_per_xcd_cap) {
     __shared__ __align__(16) uint8_t stg0[kPfStage];
     __shared__ __align__(16) uint8_t stg1[kPfStage];
@@ -928,7 +938,8 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
     __shared__ __align__(16) uint8_t stg3[kPfStage];
     __shared__ __align__(16) uint8_t scr0[kScSlot];
     __shared__ __align__(16) uint8_t scr1[kScSlot];
-    constexpr int TT = kPfCols / NT;
+    constexpr int TT = 32 * NCF / NT;                   // picks per tile
+    constexpr int PL = pf_loads<NCF>(), SL = sc_loads<NCF>();
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
@@ -961,7 +972,7 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
         }
         return base + (size_t)mr * (scale ? K / 32 : K / 2);
     };
-    // tile column c (0..127) = (pick c / NT, term c % NT); columns past the tile re-read column 0
+    // tile column c (0..32 NCF - 1) = (pick c / NT, term c % NT); columns past the tile re-read column 0
     auto b_col_ptr = [&](int c, bool scale) -> const uint8_t* {
         const int tc = c / NT, t = c % NT;
         const int tcc = tc < ntok ? tc : 0;
@@ -969,22 +980,25 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
         return scale ? a.as + (arow * NT + t) * (size_t)(K / 32) : a.aq + (arow * NT + t) * (size_t)K;
     };
     // this wave's direct loads: weight rows 64 w .. 64 w + 63 (4 instructions of 16 rows, a
-    // lane quad per row), activation columns 32 w .. 32 w + 31 (4 instructions of 8 columns, 8
-    // lanes per column); scale words of the same rows (4 instructions) and columns (2)
+    // lane quad per row), activation columns 8 NCF w .. 8 NCF w + 8 NCF - 1 (NCF instructions of
+    // 8 columns, 8 lanes per column); scale words of the same rows (4 instructions) and columns
+    // (NCF / 2)
     const uint8_t* srcA[4];
-    const uint8_t* srcB[4];
+    const uint8_t* srcB[NCF];
     const uint8_t* srcAs[4];
-    const uint8_t* srcBs[2];
+    const uint8_t* srcBs[NCF / 2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = (wave * 4 + j) * 16 + (lane >> 2);
         srcA[j] = a_row_ptr(r, false) + (((lane & 3) ^ swz_a(r & 15)) * 16);
-        const int c = (wave * 4 + j) * 8 + (lane >> 3);
-        srcB[j] = b_col_ptr(c, false) + (((lane & 7) ^ swz_b(c & 15)) * 16);
+        if (j < NCF) {
+            const int c = (wave * NCF + j) * 8 + (lane >> 3);
+            srcB[j] = b_col_ptr(c, false) + (((lane & 7) ^ swz_b(c & 15)) * 16);
+        }
         srcAs[j] = a_row_ptr(r, true);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) srcBs[j] = b_col_ptr((wave * 2 + j) * 16 + (lane >> 2), true);
+    for (int j = 0; j < NCF / 2; ++j) srcBs[j] = b_col_ptr((wave * (NCF / 2) + j) * 16 + (lane >> 2), true);
     const int nsteps = K / 128, last = nsteps - 1;
 
     auto issue = [&](int st, uint8_t* stg) {
@@ -992,7 +1006,7 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
 #pragma unroll
         for (int j = 0; j < 4; ++j) dma16(srcA[j] + oa, stg + kPfA + (wave * 4 + j) * 1024);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(srcB[j] + ob, stg + kPfB + (wave * 4 + j) * 1024);
+        for (int j = 0; j < NCF; ++j) dma16(srcB[j] + ob, stg + kPfB + (wave * NCF + j) * 1024);
     };
     // scale words of steps 4m .. 4m + 3 (past the last step: the last step's) into slot sc
     auto issue_scales = [&](int m, uint8_t* sc) {
@@ -1000,14 +1014,14 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
 #pragma unroll
         for (int j = 0; j < 4; ++j) dma4(srcAs[j] + ow, sc + kScA + (wave * 4 + j) * 256);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dma4(srcBs[j] + ow, sc + kScB + (wave * 2 + j) * 256);
+        for (int j = 0; j < NCF / 2; ++j) dma4(srcBs[j] + ow, sc + kScB + (wave * (NCF / 2) + j) * 256);
     };
 
-    v4f acc[8][4];
+    v4f acc[8][NCF];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < NCF; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
     PfFrags fr0, fr1;
     // Every step issues one stage, clamped to the last: past the end the ring is refilled with
     // copies of the last stage that no step reads.  The scale group of steps 4m.. rides with
@@ -1018,9 +1032,9 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
     issue(min(1, last), stg1);
     issue(min(2, last), stg2);
     issue(min(3, last), stg3);
-    wait_vm<3 * kPfLoads>();                                 // stage 0 and its scales complete
+    wait_vm<3 * PL>();                                       // stage 0 and its scales complete
     ring_barrier();
-    pf_read<GATEUP>(stg0, scr0, 0, fr0, wm, wn, lane);
+    pf_read<GATEUP, NCF>(stg0, scr0, 0, fr0, wm, wn, lane);
 
     // buffers by compile-time index (distinct arrays, so the compiler sees that a direct load
     // into one never feeds a read of another)
@@ -1043,32 +1057,52 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
         constexpr int Q = decltype(pos)::value;
         PfFrags& cur = (Q & 1) ? fr1 : fr0;
         PfFrags& nxt = (Q & 1) ? fr0 : fr1;
-        wait_vm<2 * kPfLoads + (((Q & 3) == 1 || (Q & 3) == 2) ? kScLoads : 0)>();
+        wait_vm<2 * PL + (((Q & 3) == 1 || (Q & 3) == 2) ? SL : 0)>();
         ring_barrier();                                      // also: every wave has stage s in registers
         __builtin_amdgcn_sched_barrier(0);
         issue(min(s + 4, last), stage_buf(StepPos<Q & 3>{}));
         if constexpr ((Q & 3) == 0) issue_scales((s >> 2) + 1, scale_buf(StepPos<((Q >> 2) + 1) & 1>{}));
-        pf_read<GATEUP>(stage_buf(StepPos<(Q + 1) & 3>{}), scale_buf(StepPos<((Q + 1) >> 2) & 1>{}), (Q + 1) & 3,
-                        nxt, wm, wn, lane);
-        pf_mfma(cur, acc);
+        pf_read<GATEUP, NCF>(stage_buf(StepPos<(Q + 1) & 3>{}), scale_buf(StepPos<((Q + 1) >> 2) & 1>{}),
+                             (Q + 1) & 3, nxt, wm, wn, lane);
+        pf_mfma<NCF>(cur, acc);
         // schedule: the step's direct loads (NV) and its 28 LDS reads of step s + 1 go between the
         // 32 MFMAs of step s, one MFMA, one direct load and one LDS read at a time, so that their
         // issue hides under the matrix core's work (with one wave per SIMD nothing else would);
         // the MFMAs do not wait for those reads, and no MFMA of step s + 1 is hoisted above the
         // next barrier
-        constexpr int NV = kPfLoads + ((Q & 3) == 0 ? kScLoads : 0);
+        constexpr int NV = PL + ((Q & 3) == 0 ? SL : 0);
+        if constexpr (NCF == 4) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+            for (int i = 0; i < NV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
 #pragma unroll
-        for (int i = 0; i < 28 - NV; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int i = 0; i < 28 - NV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        } else {
+            // 16 MFMAs, 22 LDS reads: the first 14 MFMAs each take one or two reads (and the
+            // direct loads, one each, from the first), the last two none
+            constexpr int NMF = 8 * NCF, NDS = 16 + 3 * NCF, SLOTS = NMF - 2, D2 = NDS - SLOTS;
+            static_assert(D2 >= 0 && D2 <= SLOTS && NV <= SLOTS, "one or two LDS reads per MFMA slot");
+#pragma unroll
+            for (int i = 0; i < D2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+#pragma unroll
+            for (int i = D2; i < SLOTS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF - SLOTS, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     // The K extents of the workload (d_model 4096 for gate/up, d_ff 2048 for down) run as straight-
@@ -1100,15 +1134,15 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
     wait_vm<0>();                                            // no direct load outlives the workgroup
     }
 
-    // columns: n * 16 + li of this wave's 64 = (pick tc, term t)
+    // columns: n * 16 + li of this wave's 16 NCF = (pick tc, term t)
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) mfma_results_here(acc[j][n]);
+        for (int n = 0; n < NCF; ++n) mfma_results_here(acc[j][n]);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
+        for (int n = 0; n < NCF; ++n)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[j][n][r] = sum_adjacent<NT>(acc[j][n][r]);
     const int t = li % NT;
@@ -1116,7 +1150,7 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
         // h = silu(g) u for the wave's 64 row indices (two natural blocks of h), each split into
         // NT terms with one exponent per term and block
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
+        for (int n = 0; n < NCF; ++n)
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 float v[8];
@@ -1129,7 +1163,7 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
                 int S[NT];
                 split_terms<NT>(v, codes, S, [](float mm) { return max_xor32(max_xor16(mm)); });
                 const int rg = (mblk * 128 + wm * 64) / 32 + b;
-                const int tc = (wn * 64 + n * 16 + li) / NT;
+                const int tc = (wn * 16 * NCF + n * 16 + li) / NT;
                 if (tc < ntok) {
                     const size_t pos = (size_t)i0 + tc;
                     uint32_t w0 = codes[0][0], w1 = codes[0][1];
@@ -1145,8 +1179,8 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
             }
     } else {
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int tc = (wn * 64 + n * 16 + li) / NT;
+        for (int n = 0; n < NCF; ++n) {
+            const int tc = (wn * 16 * NCF + n * 16 + li) / NT;
             if (tc < ntok && t == 0) {
                 float* dst = a.o + ((size_t)i0 + tc) * a.d;
 #pragma unroll
@@ -1160,7 +1194,7 @@ __global__ __launch_bounds__(256, 1) void k_mx_pf(GemmArgs a, int ss2, int tiles
     }
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int NCF>
 static hipError_t launch_pf(const GemmArgs& a, int NT, int max_tiles, hipStream_t st) {
     const int MT = GATEUP ? a.f / 128 : (a.d + kPfRows - 1) / kPfRows;
     const int cap = (max_tiles + 7) / 8;
@@ -1170,14 +1204,14 @@ static hipError_t launch_pf(const GemmArgs& a, int NT, int max_tiles, hipStream_
     const bool full = (GATEUP ? a.d : a.f) == 128 * kFull;
     if (NT == 1) {
         // (single-term down runs the looped instance: the straight-line one spills at K = 2048)
-        if (full && GATEUP) MOE_LAUNCH((k_mx_pf<1, true, 32>), grid, dim3(256), 0, st, a, 1, cap);
-        else MOE_LAUNCH((k_mx_pf<1, GATEUP, 0>), grid, dim3(256), 0, st, a, 1, cap);
+        if (full && GATEUP) MOE_LAUNCH((k_mx_pf<1, true, 32, NCF>), grid, dim3(256), 0, st, a, 1, cap);
+        else MOE_LAUNCH((k_mx_pf<1, GATEUP, 0, NCF>), grid, dim3(256), 0, st, a, 1, cap);
     } else if (NT == 2) {
-        if (full) MOE_LAUNCH((k_mx_pf<2, GATEUP, kFull>), grid, dim3(256), 0, st, a, 1, cap);
-        else MOE_LAUNCH((k_mx_pf<2, GATEUP, 0>), grid, dim3(256), 0, st, a, 1, cap);
+        if (full) MOE_LAUNCH((k_mx_pf<2, GATEUP, kFull, NCF>), grid, dim3(256), 0, st, a, 1, cap);
+        else MOE_LAUNCH((k_mx_pf<2, GATEUP, 0, NCF>), grid, dim3(256), 0, st, a, 1, cap);
     } else {
-        if (full) MOE_LAUNCH((k_mx_pf<4, GATEUP, kFull>), grid, dim3(256), 0, st, a, 1, cap);
-        else MOE_LAUNCH((k_mx_pf<4, GATEUP, 0>), grid, dim3(256), 0, st, a, 1, cap);
+        if (full) MOE_LAUNCH((k_mx_pf<4, GATEUP, kFull, NCF>), grid, dim3(256), 0, st, a, 1, cap);
+        else MOE_LAUNCH((k_mx_pf<4, GATEUP, 0, NCF>), grid, dim3(256), 0, st, a, 1, cap);
     }
     return hipGetLastError();
 }
@@ -1199,7 +1233,7 @@ static hipError_t launch_gemm(const GemmArgs& a, int NT, int variant, int max_ti
              : NT == 2 ? launch_one<GATEUP, 2, 1, 1>(a, SS, ss2, grid, st)
                        : launch_one<GATEUP, 4, 1, 1>(a, SS, ss2, grid, st);
     }
-    return launch_pf<GATEUP>(a, NT, max_tiles, st);
+    return variant == 2 ? launch_pf<GATEUP, 2>(a, NT, max_tiles, st) : launch_pf<GATEUP, 4>(a, NT, max_tiles, st);
 }
 
 hipError_t launch_gemm_gateup(const GemmArgs& a, int NT, int variant, int max_tiles, hipStream_t st) {

@@ -489,7 +489,7 @@ struct CombineArgs {
 };
 
 // variant: 0 = few tokens per expert (16 columns per tile, K split over the 4 waves when
-// possible); 1 = many tokens per expert (128 columns per tile)
+// possible); 1 = many tokens per expert (128 columns per tile); 2 = between (64 columns per tile)
 int gemm_variant(const moe_shape* s, int T);
 int gemm_tile_tokens(int variant, int NT);
 hipError_t launch_gemm_gateup(const GemmArgs& a, int NT, int variant, int max_tiles, hipStream_t st);

@@ -92,7 +92,8 @@ def small(name="tiny", **kw):
 
 
 def covering_sample(idx, E, tile_picks, n_min=64, seed=0):
-    """Tokens whose picks, between them, fill every column slot of a tile of `tile_picks` picks,
+    """Tokens whose picks, between them, fill every column slot of a tile of `tile_picks` picks
+    that some tile fills,
     land in every eighth of the tile list (the many-pick GEMM hands each of the 8 XCDs one
     contiguous eighth), and include a pick of every ragged last tile, padded with further tokens
     to at least n_min.  idx: [T, k] routing.  Pure bookkeeping of the tile plan (expert ranges in
@@ -115,7 +116,9 @@ def covering_sample(idx, E, tile_picks, n_min=64, seed=0):
     tile = tile0[e] + rel // tile_picks
     xcd = tile // tpx
     ragged = (rel // tile_picks == tiles_per[e] - 1) & (counts[e] % tile_picks != 0)
-    need = {("slot", s) for s in range(tile_picks)} | {("xcd", x) for x in range(min(8, ntiles))}
+    # (the slots some tile fills: with few picks per expert no tile reaches the last slots)
+    filled = int(min(tile_picks, counts.max())) if counts.size else 0
+    need = {("slot", s) for s in range(filled)} | {("xcd", x) for x in range(min(8, ntiles))}
     rng = np.random.default_rng(seed)
     chosen = []
     for t in rng.permutation(T):

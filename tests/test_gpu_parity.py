@@ -136,6 +136,12 @@ SMALL_CASES = [
     ("tiny", dict(n_experts=400, top_k=8, act_dtype=synth.BF16), 16),
     # fused router, 16 tokens on four experts: an expert's tokens fill more than one tile
     ("tiny", dict(n_experts=4, top_k=2), 16),
+    # 8-32 picks per expert on average: the 64-column tile (32 picks with two terms, some experts
+    # over two tiles); with fp32 activations (four terms) 16 picks per tile
+    ("tiny", dict(d_model=512, d_ff=256, n_experts=16, top_k=4, act_dtype=synth.BF16), 90),
+    ("tiny", dict(n_experts=8, top_k=2), 60),
+    # fp32 activations on the few-pick tiles of the general path (four terms: 4 picks per tile)
+    ("tiny", dict(n_experts=64, top_k=4), 24),
 ]
 
 
@@ -314,6 +320,27 @@ def test_glm_decode_zero_token(glm_layer):
     np.testing.assert_array_equal(oidx[0], np.arange(8))
     np.testing.assert_allclose(w[0].cpu().numpy(), 0.125, rtol=0, atol=0)
     assert rel_l2(y.float().cpu().numpy(), oy) <= tol(wl)
+
+
+@pytest.mark.parametrize("T", [512, 1024])
+def test_glm_mid_chunk_sampled(glm_layer, T):
+    """Chunks of 14 and 28 picks per expert on average: the 64-column (32-pick) tiles of the
+    many-picks GEMM at full width.  Routing bit-exact on every token; the output on tokens whose
+    picks fill every column slot of a 32-pick tile and every eighth of the tile list."""
+    dl = glm_layer
+    wl = dl.wl
+    print(f"glm chunk T={T}", flush=True)
+    x = _x(wl, T, tag=f"mid{T}")
+    y, idx, w = run_layer(m, dl, x)
+    _, oidx, ow = oracle.route(oracle.to_f64(x), dl.router.cpu().numpy(), None, wl.top_k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oidx)
+    sample = covering_sample(oidx, wl.n_experts, 32, n_min=48)
+    print(f"  {len(sample)} sampled tokens", flush=True)
+    xs = x[sample].contiguous()
+    oy, _, _, _ = oracle_layer(dl, xs, idx_hint=oidx[sample])
+    err = rel_l2(y[sample].float().cpu().numpy(), oy)
+    print(f"  sampled rel-L2 {err:.3e}")
+    assert err <= tol(wl)
 
 
 def test_glm_prefill_chunk_sampled(glm_layer):
