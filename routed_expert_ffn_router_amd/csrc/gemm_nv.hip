@@ -651,6 +651,7 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
     __shared__ __align__(16) uint8_t b_lds[NCOL * CST];
     __shared__ v4f_nv part[8][64];
     __shared__ __align__(16) uint8_t s_sc[8][16][128];   // per wave: its rows' scale bytes of its K quarter
+    __shared__ int s_staged;                              // filler waves done with the columns
     static_assert(NSW * 8 <= 128 && NSW % 4 == 0, "a K quarter's scale bytes: 8 per super-step and row");
     const int tile = blockIdx.x;
     int t0 = 0, t1 = *a.ntiles;
@@ -659,6 +660,10 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
         t1 = a.tile_range[1];
     }
     if (tile < t0 || tile >= t1) return;
+    if constexpr (NCOL <= 2) {
+        if (threadIdx.x == 0) s_staged = 0;
+        __syncthreads();
+    }
     const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
     const int ntok = min(min(kNvTilePicks, NCOL / NT), range_end(a, e) - i0);
     const int tid = threadIdx.x;
@@ -698,12 +703,38 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
             return a.aq + ((arow * NT + t) * (size_t)K + (size_t)(g % cpc) * 8) * 2;
         }
     };
-    // (every round's load is issued, without a branch; chunks past the columns re-read the last)
-    uint4 vx[RF];
+    // (every round's load is issued, without a branch; chunks past the columns re-read the last).
+    // With at most two columns, waves 0-3 stage them in LDS before requesting anything else and
+    // count themselves in; waves 4-7 go straight to their scales and weights.  (A wave cannot get
+    // past a long run of load instructions until the CU's memory pipeline has taken them, so
+    // columns stored after the weight requests would hold every wave's MFMAs for most of the
+    // stream.)
+    constexpr int RS = ALL_FIRST ? 2 * RF : 1;        // rounds of 256 threads
+    if constexpr (ALL_FIRST) {
+        if (wave < 4) {
+            uint4 cv[RS];
 #pragma unroll
-    for (int r = 0; r < RF; ++r) {
-        const int g = tid + 512 * r;
-        vx[r] = gload16(chunk_src(g < nchunk ? g : nchunk - 1));
+            for (int r = 0; r < RS; ++r) {
+                const int g = tid + 256 * r;
+                cv[r] = gload16(chunk_src(g < nchunk ? g : nchunk - 1));
+            }
+#pragma unroll
+            for (int r = 0; r < RS; ++r) {
+                const int g = tid + 256 * r;
+                if (g < nchunk) *(uint4*)(b_lds + (size_t)(g / cpc) * cst + (size_t)(g % cpc) * 16) = cv[r];
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);        // this wave's LDS stores are done
+            asm volatile("" ::: "memory");
+            if (lane == 0) atomicAdd(&s_staged, 1);
+        }
+    }
+    uint4 vx[ALL_FIRST ? 1 : RF];
+    if constexpr (!ALL_FIRST) {
+#pragma unroll
+        for (int r = 0; r < RF; ++r) {
+            const int g = tid + 512 * r;
+            vx[r] = gload16(chunk_src(g < nchunk ? g : nchunk - 1));
+        }
     }
     __builtin_amdgcn_sched_barrier(0);     // requested in this order: columns, scales, weights
     // 2. the scale bytes of this wave's quarter, 8 per super-step and row: lane (li, lg) loads
@@ -733,19 +764,28 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
     // 4. the columns and scale bytes into LDS (further rounds, for many columns, after the weights).
     // Their registers are taken here, in straight-line code, so that the wait for them counts the
     // weight loads issued since and leaves those in flight
+    if constexpr (!ALL_FIRST) {
 #pragma unroll
-    for (int r = 0; r < RF; ++r) asm volatile("" ::"v"(vx[r].x), "v"(vx[r].y), "v"(vx[r].z), "v"(vx[r].w));
+        for (int r = 0; r < RF; ++r) asm volatile("" ::"v"(vx[r].x), "v"(vx[r].y), "v"(vx[r].z), "v"(vx[r].w));
+    }
 #pragma unroll
     for (int i = 0; i < NSW / 4; ++i) asm volatile("" ::"v"(S2[i].x), "v"(S2[i].y));
+    if constexpr (!ALL_FIRST) {
 #pragma unroll
-    for (int r = 0; r < RF; ++r) {
-        const int g = tid + 512 * r;
-        if (g < nchunk) *(uint4*)(b_lds + (size_t)(g / cpc) * cst + (size_t)(g % cpc) * 16) = vx[r];
+        for (int r = 0; r < RF; ++r) {
+            const int g = tid + 512 * r;
+            if (g < nchunk) *(uint4*)(b_lds + (size_t)(g / cpc) * cst + (size_t)(g % cpc) * 16) = vx[r];
+        }
     }
 #pragma unroll
     for (int i = 0; i < NSW / 4; ++i) *(uint2*)&s_sc[wave][li][8 * (4 * i + lg)] = S2[i];
     if constexpr (ALL_FIRST) {
-        lds_barrier();              // not waiting for the weights in flight
+        // the staged columns (an atomic read: a volatile one would also wait for the weights); this
+        // wave's own scale bytes are read back by itself, in order
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        while (__hip_atomic_load(&s_staged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < 4)
+            __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");
     } else {
         for (int g = tid + 512; g < nchunk; g += 512)
             *(uint4*)(b_lds + (size_t)(g / cpc) * cst + (size_t)(g % cpc) * 16) = gload16(chunk_src(g));
