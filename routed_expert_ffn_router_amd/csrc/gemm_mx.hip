@@ -480,13 +480,16 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
     }
 }
 
-// down projection + weighted combine for few picks: workgroup = 16 output rows; its 16 waves
-// take (tile, K slice) units in turn (K slice = kDecKSlice of d_ff; eight waves per workgroup), park each unit's 16 outputs
-// per pick in LDS, and the workgroup sums slices and picks in a fixed order.
+// down projection + weighted combine for few picks: workgroup = 16 output rows; its sixteen
+// waves take (tile, K slice) units in turn (K slice = kDecKSlice of d_ff), park each unit's 16
+// outputs per pick in LDS, and the workgroup sums slices and picks in a fixed order.  A wave has
+// one unit in flight at a time (its loads, then its MFMAs), so sixteen waves rather than eight
+// keep twice the bytes in flight per CU (at most 128 VGPRs, four waves per SIMD).
 // PLAIN: no renorm-skip and no shared expert (known at compile time): every pick has a position,
 // so the combine carries no test for dropped picks and no shared row (about 0.5 us of its tail)
+constexpr int kDownDecWaves = 16;
 template <typename XT, int NT, bool PLAIN>
-__global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs c) {
+__global__ __launch_bounds__(64 * kDownDecWaves) void k_mx_down_dec(GemmArgs a, CombineArgs c) {
     constexpr int SS = 4;
     __shared__ float o_part[kMaxDecSlices][kMaxFusedPicks][16];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -496,7 +499,7 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs 
     const int nsl = K / kDecKSlice;
     const int nss = kDecKSlice / (128 * SS);
     const int units = a.max_tiles * nsl;
-    for (int unit = wave; unit < units; unit += 8) {
+    for (int unit = wave; unit < units; unit += kDownDecWaves) {
         const int tile = unit / nsl, ks = unit % nsl;
         const TileDesc& D = a.desc[tile];
         const int ntok = D.ntok;
@@ -521,7 +524,7 @@ __global__ __launch_bounds__(512, 2) void k_mx_down_dec(GemmArgs a, CombineArgs 
     }
     __syncthreads();
     const int k = a.k;
-    for (int q = threadIdx.x; q < c.T * 16; q += 512) {
+    for (int q = threadIdx.x; q < c.T * 16; q += 64 * kDownDecWaves) {
         const int tok = q >> 4, r = q & 15;
         float accv = 0.f;
         for (int j = 0; j < k; ++j) {
@@ -807,6 +810,8 @@ hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineA
         if (bf) MOE_DD_PL(k_mx_down_dec_lds, uint16_t);
         else MOE_DD_PL(k_mx_down_dec_lds, float);
     } else {
+#undef MOE_DD
+#define MOE_DD(K, XT, N, PL) MOE_LAUNCH((K<XT, N, PL>), grid, dim3(64 * kDownDecWaves), 0, st, a, c)
         if (bf) MOE_DD_PL(k_mx_down_dec, uint16_t);
         else MOE_DD_PL(k_mx_down_dec, float);
     }
