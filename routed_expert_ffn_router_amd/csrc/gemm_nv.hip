@@ -93,23 +93,26 @@ hipError_t launch_bf16_terms(const float* x, int rows, int K, uint16_t* terms, h
 // (MFMA columns = TTP * NT, in NCF 16-column fragments).  GATEUP: the gate and up rows of one
 // 32-row block, SwiGLU, and h as NT bf16 terms; else the down rows, o in fp32.
 template <int NT, bool GATEUP, int TTP>
-__global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a) {
+__global__ __launch_bounds__(256) void k_nv_gemm(GemmArgs a, int nrg) {
     constexpr int NA = GATEUP ? 4 : 2;      // 16-row fragments: gate lo/hi, up lo/hi (or down lo/hi)
     constexpr int NCF = (TTP * NT + 15) / 16;
-    const int tile = blockIdx.x;
+    // workgroup -> (tile, 32-row block rg of nrg): XCD x = id % 8 takes blocks x, x + 8, .. and,
+    // within each, the tiles in order, so that the tiles of one expert read the same weight rows on
+    // one XCD at about the same time, from its L2
+    const int g = blockIdx.x, j = g >> 3;
+    const int rg = (g & 7) + 8 * (j / a.max_tiles), tile = j % a.max_tiles;
     int t0 = 0, t1 = *a.ntiles;
     if (a.tile_range) {
         t0 = a.tile_range[0];
         t1 = a.tile_range[1];
     }
-    if (tile < t0 || tile >= t1) return;
+    if (rg >= nrg || tile < t0 || tile >= t1) return;
     const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
     const int ntok = min(TTP, range_end(a, e) - i0);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int K = GATEUP ? a.d : a.f;
     const moe_expert ex = a.table[e];
-    const int rg = blockIdx.y;
     const int T0 = 32 * rg;
     const int NS = K / 128;                  // super-steps of the row, shared out over the 4 waves
     const int s0 = (wave * NS) / 4, nss = ((wave + 1) * NS) / 4 - s0;
@@ -854,8 +857,14 @@ hipError_t launch_nv_gemm(const GemmArgs& a, bool gateup, int NT, int tile_picks
     const char* name = gateup ? "gemm_gate_up" : "gemm_down";
     trace(name, 0, st);
     const int rows = gateup ? a.f : a.d;
-    dim3 grid(max_tiles, rows / 32);
-#define MOE_NV(N, G, P) MOE_LAUNCH((k_nv_gemm<N, G, P>), grid, dim3(256), 0, st, a)
+    // few-pick tiles: eight XCD lanes of (32-row blocks / 8, rounded up) x max_tiles workgroups
+    const int nrg = rows / 32;
+    const dim3 grid((unsigned)(8LL * max_tiles * ((nrg + 7) / 8)));
+#define MOE_NV(N, G, P)                                                                     \
+    do {                                                                                    \
+        if (a.max_tiles != max_tiles) return hipErrorInvalidValue;                          \
+        MOE_LAUNCH((k_nv_gemm<N, G, P>), grid, dim3(256), 0, st, a, nrg);                   \
+    } while (0)
     if (tile_picks == kNvTilePicksMany) {
         const int MT = gateup ? a.f / 64 : a.d / 128;
         const int cap = (max_tiles + 7) / 8;

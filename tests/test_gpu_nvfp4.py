@@ -42,6 +42,10 @@ def _layer(m, dl, x, staging=None, residual=None):
     (dict(d_model=512, d_ff=384, n_experts=24, top_k=3), 9),        # K not a multiple of 512
     (dict(act_dtype=synth.BF16, n_experts=8, top_k=8), 53),        # every expert, tiles of 8 picks
     (dict(d_model=384, d_ff=256, n_experts=40, top_k=4, act_dtype=synth.BF16), 300),
+    # K past the LDS-decoded few-pick kernel's 8192: gate/up (K = d_model) on the tile GEMM, 12
+    # blocks of 32 rows (not a multiple of the 8 XCD lanes); then down (K = d_ff, 65 steps of 128)
+    (dict(d_model=9216, d_ff=384, n_experts=8, top_k=2, act_dtype=synth.BF16), 13),
+    (dict(d_model=384, d_ff=8320, n_experts=8, top_k=2), 7),
 ])
 def test_nvfp4_layer_small(kw, T):
     wl = small("tiny", wformat=synth.NVFP4, **kw)

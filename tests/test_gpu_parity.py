@@ -120,6 +120,10 @@ SMALL_CASES = [
     ("tiny", dict(d_model=512, d_ff=256, n_experts=32, top_k=4, act_dtype=synth.BF16), 37),
     ("tiny", dict(d_model=1024, d_ff=512, n_experts=64, top_k=8, act_dtype=synth.BF16), 300),
     ("tiny", dict(d_model=1024, d_ff=2048, n_experts=8, top_k=2), 11),
+    # d_model past the staged-column decode kernels (4096) and d_ff past the LDS down (2048):
+    # the tile GEMMs with long K at few picks
+    ("tiny", dict(d_model=5120, d_ff=384, n_experts=8, top_k=2, act_dtype=synth.BF16), 5),
+    ("tiny", dict(d_model=1024, d_ff=4224, n_experts=8, top_k=2), 6),
     # many picks per expert (LDS-tiled GEMM): fp32 activations in four terms
     ("tiny", dict(n_experts=4, top_k=2), 200),
     # 3 K steps of gate/up, 5 of down; the second block of 256 down rows runs past d_model
