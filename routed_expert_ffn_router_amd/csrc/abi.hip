@@ -182,6 +182,8 @@ static moe_status run_ffn_nv(const moe_shape* s, const moe_expert* table, const 
     const int NT = bf ? 1 : 2;      // bf16 terms of x and of h: one with bf16 activations, two with fp32
     if (!bf) MOE_HIP(launch_bf16_terms((const float*)x, T, s->d_model, (uint16_t*)(ws + L.xq), st));
     GemmArgs a = gemm_args(s, table, T, sorted_pick, offsets, ws, L, o);
+    // the few-token router's tile records name the table's experts: used in place only
+    if (!planned || staging) a.desc = nullptr;
     const uint8_t* xin = bf ? (const uint8_t*)x : ws + L.xq;
     if (!staging) {
         a.aq = xin;

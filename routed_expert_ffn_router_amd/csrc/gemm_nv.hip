@@ -656,26 +656,76 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
     __shared__ __align__(16) uint8_t s_sc[8][16][128];   // per wave: its rows' scale bytes of its K quarter
     __shared__ int s_staged;                              // filler waves done with the columns
     static_assert(NSW * 8 <= 128 && NSW % 4 == 0, "a K quarter's scale bytes: 8 per super-step and row");
+    static_assert(kNvTilePicks <= 4 && kDescTokens >= 4, "a tile's tokens: the first four of its record");
     const int tile = blockIdx.x;
-    int t0 = 0, t1 = *a.ntiles;
-    if (a.tile_range) {
-        t0 = a.tile_range[0];
-        t1 = a.tile_range[1];
-    }
-    if (tile < t0 || tile >= t1) return;
     if constexpr (NCOL <= 2) {
         if (threadIdx.x == 0) s_staged = 0;
         __syncthreads();
     }
-    const int e = a.tiles[2 * tile], i0 = a.tiles[2 * tile + 1];
-    const int ntok = min(min(kNvTilePicks, NCOL / NT), range_end(a, e) - i0);
+    // the tile: with the few-token router's records (a.desc set), the tile count and the record
+    // (the expert's pointers and tensor scales, first position, pick count and tokens) in one
+    // round trip on the scalar path; else the tile count or range, then the tile list, then the
+    // expert table and the end of the expert's range
+    moe_expert ex;
+    int i0, ntok, tk[4] = {0, 0, 0, 0};
+    if (a.desc) {
+        const TileDesc* D = a.desc + tile;         // tile < max_tiles: always a written record
+        const int32_t* ntp = a.ntiles;
+        asm volatile("" : "+s"(ntp));     // read with the record in one round trip
+        const int ntile_count = sload(ntp);
+        if (GATEUP) {
+            ex.gate_q = sload(&D->ex.gate_q);
+            ex.up_q = sload(&D->ex.up_q);
+            ex.gate_s = sload(&D->ex.gate_s);
+            ex.up_s = sload(&D->ex.up_s);
+            ex.gate_ts = sload(&D->ex.gate_ts);
+            ex.up_ts = sload(&D->ex.up_ts);
+            ex.down_q = ex.down_s = nullptr;
+            ex.down_ts = 0.0f;
+        } else {
+            ex.down_q = sload(&D->ex.down_q);
+            ex.down_s = sload(&D->ex.down_s);
+            ex.down_ts = sload(&D->ex.down_ts);
+            ex.gate_q = ex.up_q = ex.gate_s = ex.up_s = nullptr;
+            ex.gate_ts = ex.up_ts = 0.0f;
+        }
+        i0 = sload(&D->i0);
+        const int dn = sload(&D->ntok);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tk[j] = sload(&D->tok[j]);
+        // all of them requested before the first wait
+        asm volatile("" ::"s"(ntile_count), "s"(ex.gate_q), "s"(ex.up_q), "s"(ex.down_q), "s"(ex.gate_s),
+                     "s"(ex.up_s), "s"(ex.down_s), "s"(ex.gate_ts), "s"(ex.up_ts), "s"(ex.down_ts), "s"(i0),
+                     "s"(dn), "s"(tk[0]), "s"(tk[1]), "s"(tk[2]), "s"(tk[3]));
+        if (tile >= ntile_count) return;
+        ntok = min(min(kNvTilePicks, NCOL / NT), dn);
+    } else {
+        // (the list entry is read with the count: tile < max_tiles keeps it in bounds, and it is
+        // used only for a tile in range)
+        const int ntile_count = sload(a.ntiles);
+        const int e = sload(&a.tiles[2 * tile]);
+        i0 = sload(&a.tiles[2 * tile + 1]);
+        int t0 = 0, t1 = ntile_count;
+        if (a.tile_range) {
+            t0 = sload(a.tile_range);
+            t1 = sload(a.tile_range + 1);
+        }
+        if (tile < t0 || tile >= t1) return;
+        ex = a.table[e];
+        const int end = e < a.E ? sload(a.offsets + e + 1) : a.Pall;
+        ntok = min(min(kNvTilePicks, NCOL / NT), end - i0);
+    }
+    // token of the tile's pick tc (gate/up columns): the record's, else through sorted_pick
+    auto tile_token = [&](int tc) -> int {
+        if (a.desc) return tc == 0 ? tk[0] : tc == 1 ? tk[1] : tc == 2 ? tk[2] : tk[3];
+        return pos_token(a, i0 + tc);
+    };
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int f = wave >> 2, kq = wave & 3;
     const int K = GATEUP ? a.d : a.f;
     const int cst = K * 2 + 16;
-    const moe_expert ex = a.table[e];
     const int T0 = (GATEUP ? 16 : 32) * blockIdx.y;
     const int NS = K / 128, s0 = (kq * NS) / 4, nss = ((kq + 1) * NS) / 4 - s0;
     // 1. activation columns c = (pick c / NT, term c % NT), K bf16 each, as 16-byte chunks.  With
@@ -693,7 +743,7 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int cc = c < ncol ? c : ncol - 1, tc = cc / NT, t = cc % NT;
-            const size_t arow = GATEUP ? (size_t)pos_token(a, i0 + tc) : (size_t)(i0 + tc);
+            const size_t arow = GATEUP ? (size_t)tile_token(tc) : (size_t)(i0 + tc);
             colb[c] = a.aq + (arow * NT + t) * (size_t)K * 2;
         }
     }
@@ -702,7 +752,7 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
             return colb[g >= cpc ? 1 : 0] + (size_t)(g % cpc) * 16;
         } else {
             const int c = g / cpc, tc = c / NT, t = c % NT;
-            const size_t arow = GATEUP ? (size_t)pos_token(a, i0 + tc) : (size_t)(i0 + tc);
+            const size_t arow = GATEUP ? (size_t)tile_token(tc) : (size_t)(i0 + tc);
             return a.aq + ((arow * NT + t) * (size_t)K + (size_t)(g % cpc) * 8) * 2;
         }
     };
