@@ -138,6 +138,31 @@ def test_staging_rejected_for_mxfp4():
 # the NVFP4 configuration at full size (d_model 6144, d_ff 2048, 256 experts, top-8)
 # ---------------------------------------------------------------------------------------------
 
+def test_nvfp4_few_token_calls_repeat_on_one_workspace():
+    """Few-token calls (the fused router, in place) of different token counts in turn on one
+    workspace, with the shared expert and a residual, give exactly what the staged path (the
+    general router and a separate gather) gives, every time: nothing a call leaves in the
+    workspace changes the next one."""
+    wl = small("tiny", wformat=synth.NVFP4, d_model=512, d_ff=256, n_experts=24, top_k=4,
+               act_dtype=synth.BF16, n_shared=1, routed_scaling=2.5)
+    dl = DeviceLayer(m, wl)
+    Ts = (5, 1, 16, 3)
+    xs = {T: _x(wl, T, tag=f"rep{T}") for T in Ts}
+    rs = {T: _x(wl, T, tag=f"rres{T}") for T in Ts}
+    staging = torch.empty(wl.n_experts, dl.stride, dtype=torch.uint8, device="cuda")
+    ref = {T: _layer(m, dl, xs[T], staging=staging, residual=rs[T])[0] for T in Ts}
+    ws = m.workspace(dl.shape, 16)
+    for rnd in range(5):
+        for T in Ts:
+            y = torch.empty_like(xs[T])
+            idx = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
+            m.moe_layer(dl.shape, xs[T], T, dl.router, dl.bias, dl.table, None, rs[T], y, idx, None, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), ref[T].view(torch.int16)), (rnd, T)
+    oy, oidx, _, _ = oracle_layer(dl, xs[5], residual=rs[5])
+    assert rel_l2(ref[5].float().cpu().numpy(), oy) <= tol(wl)
+
+
 @pytest.fixture(scope="module")
 def nv_layer():
     wl = synth.WORKLOADS["nvfp4_decode"]
