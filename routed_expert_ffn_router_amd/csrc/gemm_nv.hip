@@ -664,8 +664,8 @@ __global__ __launch_bounds__(512) void k_nv_dec(GemmArgs a) {
     }
     // the tile: with the few-token router's records (a.desc set), the tile count and the record
     // (the expert's pointers and tensor scales, first position, pick count and tokens) in one
-    // round trip on the scalar path; else the tile count or range, then the tile list, then the
-    // expert table and the end of the expert's range
+    // round trip on the scalar path; else the tile count, the tile's list entry and the tile range
+    // together, then the expert table and the end of the expert's range
     moe_expert ex;
     int i0, ntok, tk[4] = {0, 0, 0, 0};
     if (a.desc) {
