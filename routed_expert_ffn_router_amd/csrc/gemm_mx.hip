@@ -494,26 +494,41 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
 // PLAIN: no renorm-skip and no shared expert (known at compile time): every pick has a position,
 // so the combine carries no test for dropped picks and no shared row (about 0.5 us of its tail)
 constexpr int kDownDecWaves = 16;
+// tile records the kernel keeps in LDS: the most a few-token layer plans (picks of at most
+// kMaxFusedPicks, tiles of at least 4 picks, one ragged tile per expert and the shared expert's)
+constexpr int kDownDecMaxTiles = 648;
 template <typename XT, int NT, bool PLAIN>
 __global__ __launch_bounds__(64 * kDownDecWaves) void k_mx_down_dec(GemmArgs a, CombineArgs c) {
     constexpr int SS = 4;
     __shared__ float o_part[kMaxDecSlices][kMaxFusedPicks][16];
+    // the fields of the tile records that the units read, staged once (one round trip for the
+    // workgroup), instead of two dependent loads of the record per unit
+    __shared__ const uint8_t* s_dq[kDownDecMaxTiles];
+    __shared__ const uint8_t* s_ds[kDownDecMaxTiles];
+    __shared__ int s_i0[kDownDecMaxTiles], s_nt[kDownDecMaxTiles];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int r0 = blockIdx.x * 16;
     const int K = a.f;
     const int nsl = K / kDecKSlice;
     const int nss = kDecKSlice / (128 * SS);
-    const int units = a.max_tiles * nsl;
+    const int units = a.max_tiles * nsl;          // (max_tiles <= kDownDecMaxTiles: checked at launch)
+    for (int t = threadIdx.x; t < a.max_tiles; t += 64 * kDownDecWaves) {
+        const TileDesc* D = a.desc + t;
+        s_dq[t] = D->ex.down_q;
+        s_ds[t] = D->ex.down_s;
+        s_i0[t] = D->i0;
+        s_nt[t] = D->ntok;
+    }
+    __syncthreads();
     for (int unit = wave; unit < units; unit += kDownDecWaves) {
         const int tile = unit / nsl, ks = unit % nsl;
-        const TileDesc& D = a.desc[tile];
-        const int ntok = D.ntok;
+        const int ntok = s_nt[tile];
         if (ntok == 0) continue;
-        const int i0 = D.i0;
+        const int i0 = s_i0[tile];
         const int kss0 = ks * nss;
-        const uint8_t* const aq[1] = {D.ex.down_q + (size_t)(r0 + li) * (K / 2) + lg * 16 * SS + (size_t)kss0 * 64 * SS};
-        const uint8_t* const as[1] = {D.ex.down_s + (size_t)(r0 + li) * (K / 32) + lg * SS + (size_t)kss0 * 4 * SS};
+        const uint8_t* const aq[1] = {s_dq[tile] + (size_t)(r0 + li) * (K / 2) + lg * 16 * SS + (size_t)kss0 * 64 * SS};
+        const uint8_t* const as[1] = {s_ds[tile] + (size_t)(r0 + li) * (K / 32) + lg * SS + (size_t)kss0 * 4 * SS};
         const int tc = li / NT, t = li % NT;
         const bool bval[1] = {tc < ntok};
         const size_t arow = bval[0] ? (size_t)(i0 + tc) : 0;
@@ -816,6 +831,7 @@ hipError_t launch_down_dec(const moe_shape* s, const GemmArgs& a, const CombineA
         if (bf) MOE_DD_PL(k_mx_down_dec_lds, uint16_t);
         else MOE_DD_PL(k_mx_down_dec_lds, float);
     } else {
+        if (a.max_tiles > kDownDecMaxTiles) return hipErrorInvalidValue;     // (its records are kept in LDS)
 #undef MOE_DD
 #define MOE_DD(K, XT, N, PL) MOE_LAUNCH((K<XT, N, PL>), grid, dim3(64 * kDownDecWaves), 0, st, a, c)
         if (bf) MOE_DD_PL(k_mx_down_dec, uint16_t);
