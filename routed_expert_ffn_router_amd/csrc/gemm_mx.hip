@@ -341,27 +341,52 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
     // (tile, 32-row block) pairs p = tile * nrg + rg, taken by the workgroups in turn; the grid
     // never exceeds the pairs of max_tiles tiles, so the first record read is always in bounds
     const int nrg = a.f / 32;
-    for (int pair = blockIdx.x;; pair += nwg) {          // nwg = grid size, passed as an argument
-    const int tile = __builtin_amdgcn_readfirstlane(pair / nrg), rg = __builtin_amdgcn_readfirstlane(pair % nrg);
-    // one round trip on the scalar path: the tile count and the tile record's fields (the vector
-    // path would queue them behind the weight loads of the other workgroup on this CU)
-    const TileDesc* D = a.desc + tile;
+    // a tile record's fields, read on the scalar path (the vector path would queue them behind the
+    // weight loads of the other workgroup on this CU)
+    struct Rec {
+        const uint8_t *gq, *uq, *gs, *us;
+        int i0, ntok, tk[kDescTokens];
+    };
+    static_assert(kDescTokens == 8, "token fields of a tile record");
+    auto load_rec = [&](int tile) {
+        const TileDesc* D = a.desc + tile;
+        Rec r;
+        r.gq = sload(&D->ex.gate_q);
+        r.uq = sload(&D->ex.up_q);
+        r.gs = sload(&D->ex.gate_s);
+        r.us = sload(&D->ex.up_s);
+        r.i0 = sload(&D->i0);
+        r.ntok = sload(&D->ntok);
+#pragma unroll
+        for (int j = 0; j < kDescTokens; ++j) r.tk[j] = sload(&D->tok[j]);
+        return r;
+    };
+    // the first pair's record and the tile count in one round trip (all requested before the
+    // first wait); each later pair's record is requested at the start of the pair before it
+    int pair = blockIdx.x;                                // nwg = grid size, passed as an argument
     const int32_t* ntp = a.ntiles;
     asm volatile("" : "+s"(ntp));     // read with the record in one round trip, not hoisted ahead of it
     const int ntile_count = sload(ntp);
-    const uint8_t* const gq = sload(&D->ex.gate_q);
-    const uint8_t* const uq = sload(&D->ex.up_q);
-    const uint8_t* const gs = sload(&D->ex.gate_s);
-    const uint8_t* const us = sload(&D->ex.up_s);
-    const int i0 = sload(&D->i0);
-    const int ntok = sload(&D->ntok);
-    static_assert(kDescTokens == 8, "token fields of a tile record");
-    const int tk0 = sload(&D->tok[0]), tk1 = sload(&D->tok[1]), tk2 = sload(&D->tok[2]), tk3 = sload(&D->tok[3]);
-    const int tk4 = sload(&D->tok[4]), tk5 = sload(&D->tok[5]), tk6 = sload(&D->tok[6]), tk7 = sload(&D->tok[7]);
-    // all of them requested before the first wait
-    asm volatile("" ::"s"(ntile_count), "s"(gq), "s"(uq), "s"(gs), "s"(us), "s"(i0), "s"(ntok), "s"(tk0), "s"(tk1),
-                 "s"(tk2), "s"(tk3), "s"(tk4), "s"(tk5), "s"(tk6), "s"(tk7));
+    Rec rec = load_rec(__builtin_amdgcn_readfirstlane(pair / nrg));
+    asm volatile("" ::"s"(ntile_count), "s"(rec.gq), "s"(rec.uq), "s"(rec.gs), "s"(rec.us), "s"(rec.i0),
+                 "s"(rec.ntok), "s"(rec.tk[0]), "s"(rec.tk[1]), "s"(rec.tk[2]), "s"(rec.tk[3]), "s"(rec.tk[4]),
+                 "s"(rec.tk[5]), "s"(rec.tk[6]), "s"(rec.tk[7]));
+    for (;;) {
+    const int tile = __builtin_amdgcn_readfirstlane(pair / nrg), rg = __builtin_amdgcn_readfirstlane(pair % nrg);
     if (tile >= ntile_count) break;
+    // the next pair's record, requested now and used by the next pass (none when this pair is the
+    // workgroup's last: one pair per workgroup with one token)
+    const bool more = pair + nwg < ntile_count * nrg;
+    Rec nrec = rec;
+    if (more) nrec = load_rec(__builtin_amdgcn_readfirstlane((pair + nwg) / nrg));
+    const uint8_t* const gq = rec.gq;
+    const uint8_t* const uq = rec.uq;
+    const uint8_t* const gs = rec.gs;
+    const uint8_t* const us = rec.us;
+    const int i0 = rec.i0;
+    const int ntok = rec.ntok;
+    const int tk0 = rec.tk[0], tk1 = rec.tk[1], tk2 = rec.tk[2], tk3 = rec.tk[3];
+    const int tk4 = rec.tk[4], tk5 = rec.tk[5], tk6 = rec.tk[6], tk7 = rec.tk[7];
     const int row = 32 * rg + 16 * (f & 1) + li;
     const int kss0 = ks * nss;
     // 1. the tile's x terms (ncol columns of K code bytes and K/32 scale bytes) are staged in LDS,
@@ -482,7 +507,9 @@ __global__ __launch_bounds__(512, 4) void k_mx_gateup_dec(GemmArgs a, int ss2, i
         if (lg == 0) a.hs[(pos * NT + t) * (size_t)(a.f / 32) + rg] = (uint8_t)(Sme + 127);
     }
     }
-    if (pair + nwg >= ntile_count * nrg) break;
+    if (!more) break;
+    pair += nwg;
+    rec = nrec;
     }
 }
 
